@@ -1,0 +1,30 @@
+"""Plain, slow CPU reference for paged GQA decode -- TEST INFRASTRUCTURE ONLY.
+
+What it computes, in float64 with numpy:
+
+* ``page_table``  -- the CSR page table for a list of KV lengths and the
+  length identity l = P (n - 1) + r, 1 <= r <= P;
+* ``attention``   -- softmax(q K^T / sqrt(d)) V and its log-sum-exp for each
+  request and query head, gathering K and V through the page table;
+* ``merge``       -- the exact combination of attention states over
+  disjoint key sets;
+* ``plan_ref``    -- the split-KV work schedule (chunking, longest-first
+  assignment to a fixed number of workgroups, reduction map) that the
+  library's host planner must reproduce bit for bit.
+
+Sources: the three FlashInfer pages (aicassindra "FlashInfer, in depth";
+pyshine "FlashInfer" source tour; pinghaoyang "FlashInfer 完全拆解").  Each
+function cites the passage it follows.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The HIP library never calls it, and it
+shares no code with the library: the two meet only on the seeded inputs from
+``workloads``.
+
+Parity status: every function here is pinned by ``tests/test_oracle_*.py``
+against the pages' worked example, closed forms, a library routine (torch's
+scaled_dot_product_attention in float64) or brute force.  No function is
+"parity unpinned".
+"""
+
+from . import attention, merge, page_table, plan_ref  # noqa: F401

@@ -1,0 +1,153 @@
+"""Split-KV work schedule (oracle).
+
+The shape of the algorithm is the pinghaoyang page's, section
+"先切长 KV，再做最长任务优先分配" (split long KV first, then longest-first
+assignment):
+
+* the chunk bound is the total work divided by the fixed CTA count,
+  L_kv = sum_i ceil(l_q(i) / T_q) l_kv(i) / N_CTA; with one query row per
+  request (decode) that is T / S for T = sum of KV lengths and S slots;
+* KV ranges longer than the bound are cut along the sequence into chunks;
+* a work item costs C = alpha l_q + beta l_kv;
+* items are sorted by cost, longest first, and each goes to the slot with the
+  least accumulated cost (LPT);
+* partial states are combined through a fixed reduction map, in a fixed
+  order, with no atomics (same section, the Stream-K paragraph).
+
+Requests that are not split write their output directly ("writethrough",
+pinghaoyang section "Split-KV 解决的是并行度，不是减少计算量"; aicassindra
+"Load balancing with split-KV": short sequences are not split).
+
+Readings where the pages leave a step open (also in the design notes):
+* chunks are whole pages;
+* cp = fixed_chunk_pages when given, else
+  max(ceil(min_chunk_tokens / P), ceil(ceil(T / S) / P)), min_chunk_tokens = 128;
+* alpha = beta = 1 with l_q = 1, so cost = 1 + chunk length;
+* ties: items are ordered by (-cost, request, chunk); an item goes to the
+  least-loaded slot, the lowest slot id among equals;
+* split request i gets partial ids base_i .. base_i + k_i - 1, with base_i
+  the number of chunks of the split requests before it.
+
+Two independent implementations are given (a heap and a plain scan over the
+slots); the tests require them to agree.
+"""
+
+from __future__ import annotations
+
+import heapq
+
+import numpy as np
+
+DEFAULT_MIN_CHUNK_TOKENS = 128
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def chunk_pages(total_tokens: int, page_size: int, num_slots: int,
+                fixed_chunk_pages: int = 0,
+                min_chunk_tokens: int = DEFAULT_MIN_CHUNK_TOKENS) -> int:
+    if fixed_chunk_pages > 0:
+        return int(fixed_chunk_pages)
+    bound = _ceil_div(int(total_tokens), int(num_slots))
+    return max(1, _ceil_div(int(min_chunk_tokens), page_size), _ceil_div(bound, page_size))
+
+
+def work_items(kv_indptr, kv_last_page_len, page_size: int, cp: int, alpha: int, beta: int):
+    """Chunks of every request, in request/chunk order, and the split map.
+
+    Each item is a dict with request, chunk, page_begin, num_pages, last_len,
+    length, out (partial id, -1 for writethrough) and cost."""
+    indptr = [int(x) for x in kv_indptr]
+    last = [int(x) for x in kv_last_page_len]
+    items, merges = [], []
+    next_partial = 0
+    for i in range(len(last)):
+        n = indptr[i + 1] - indptr[i]
+        k = _ceil_div(n, cp)
+        split = k > 1
+        base = next_partial
+        if split:
+            merges.append((i, base, k))
+            next_partial += k
+        for j in range(k):
+            pages = min(cp, n - j * cp)
+            last_len = last[i] if j == k - 1 else page_size
+            length = (pages - 1) * page_size + last_len
+            items.append(dict(request=i, chunk=j, page_begin=indptr[i] + j * cp,
+                              num_pages=pages, last_len=last_len, length=length,
+                              out=base + j if split else -1,
+                              cost=alpha + beta * length))
+    return items, merges, next_partial
+
+
+def _assemble(assignments, num_slots, items_in_order, merges, n_partials, header):
+    per_slot = [[] for _ in range(num_slots)]
+    for slot, item in assignments:
+        per_slot[slot].append(item)
+    slot_indptr = np.zeros(num_slots + 1, dtype=np.int32)
+    rows = []
+    for s in range(num_slots):
+        slot_indptr[s + 1] = slot_indptr[s] + len(per_slot[s])
+        for it in per_slot[s]:
+            rows.append((it["request"], it["page_begin"], it["num_pages"], it["last_len"],
+                         it["out"]))
+    items_arr = np.array(rows, dtype=np.int32).reshape(-1, 5)
+    merge_arr = np.array(merges, dtype=np.int32).reshape(-1, 3)
+    loads = np.zeros(num_slots, dtype=np.int64)
+    for slot, it in assignments:
+        loads[slot] += it["cost"]
+    return dict(header, slot_indptr=slot_indptr, items=items_arr, merges=merge_arr,
+                num_items=len(items_in_order), n_partials=n_partials, n_split=len(merges),
+                slot_loads=loads)
+
+
+def _prepare(kv_indptr, kv_last_page_len, page_size, num_slots, fixed_chunk_pages,
+             min_chunk_tokens, alpha, beta):
+    indptr = np.asarray(kv_indptr, dtype=np.int64)
+    last = np.asarray(kv_last_page_len, dtype=np.int64)
+    n = indptr[1:] - indptr[:-1]
+    lengths = page_size * (n - 1) + last
+    total = int(lengths.sum())
+    cp = chunk_pages(total, page_size, num_slots, fixed_chunk_pages, min_chunk_tokens)
+    items, merges, n_partials = work_items(indptr, last, page_size, cp, alpha, beta)
+    order = sorted(items, key=lambda it: (-it["cost"], it["request"], it["chunk"]))
+    header = dict(batch=int(last.shape[0]), page_size=int(page_size), num_slots=int(num_slots),
+                  chunk_pages=cp, total_tokens=total, alpha=alpha, beta=beta)
+    return items, order, merges, n_partials, header
+
+
+def plan(kv_indptr, kv_last_page_len, page_size: int, num_slots: int,
+         fixed_chunk_pages: int = 0, min_chunk_tokens: int = DEFAULT_MIN_CHUNK_TOKENS,
+         alpha: int = 1, beta: int = 1):
+    """The schedule, with a binary heap keyed (load, slot)."""
+    items, order, merges, n_partials, header = _prepare(
+        kv_indptr, kv_last_page_len, page_size, num_slots, fixed_chunk_pages,
+        min_chunk_tokens, alpha, beta)
+    heap = [(0, s) for s in range(num_slots)]
+    assignments = []
+    for it in order:
+        load, slot = heapq.heappop(heap)
+        assignments.append((slot, it))
+        heapq.heappush(heap, (load + it["cost"], slot))
+    return _assemble(assignments, num_slots, items, merges, n_partials, header)
+
+
+def plan_naive(kv_indptr, kv_last_page_len, page_size: int, num_slots: int,
+               fixed_chunk_pages: int = 0, min_chunk_tokens: int = DEFAULT_MIN_CHUNK_TOKENS,
+               alpha: int = 1, beta: int = 1):
+    """The same schedule with a linear scan for the least-loaded slot."""
+    items, order, merges, n_partials, header = _prepare(
+        kv_indptr, kv_last_page_len, page_size, num_slots, fixed_chunk_pages,
+        min_chunk_tokens, alpha, beta)
+    loads = [0] * num_slots
+    assignments = []
+    for it in order:
+        best = 0
+        for s in range(1, num_slots):
+            if loads[s] < loads[best]:
+                best = s
+        assignments.append((best, it))
+        loads[best] += it["cost"]
+    return _assemble(assignments, num_slots, items, merges, n_partials, header)
