@@ -1,0 +1,242 @@
+/*
+ * pkd.h -- paged GQA decode attention for AMD gfx950 (MI355X), C ABI.
+ *
+ * The operation: batched decode attention (one query token per request)
+ * over a paged KV cache described by a CSR page table, with split-KV load
+ * balancing.  It follows the inspector/executor contract of the FlashInfer
+ * pages:
+ *   - pkd_plan  ("plan"): once per decode step, on the host, from the page
+ *     table and head configuration; writes a chunked work schedule into
+ *     caller-owned workspaces at fixed addresses (aicassindra "FlashInfer,
+ *     in depth", section "Plan and run: the inspector-executor split";
+ *     pinghaoyang page, sections on the CUDA-graph conflict and on fixed
+ *     pointers);
+ *   - pkd_run   ("run"): once per layer, launches the decode kernel and the
+ *     merge kernel with fixed grids that read everything else from the
+ *     workspace, so a run can be captured in a HIP graph and replayed after
+ *     later plans (same sections);
+ *   - pkd_merge_state / pkd_merge_states: the exact combine of attention
+ *     states (pinghaoyang page, section on why online softmax allows any
+ *     split; aicassindra, section "Load balancing with split-KV").
+ *
+ * Data layouts (all row-major, contiguous):
+ *   q         bf16 [batch, num_qo_heads, head_dim]
+ *   kv_cache  bf16 [num_pages, 2, page_size, num_kv_heads, head_dim]
+ *             (NHD; index 0 of the second axis is K, 1 is V)
+ *   o         bf16 [batch, num_qo_heads, head_dim]
+ *   lse       fp32 [batch, num_qo_heads], natural-log log-sum-exp of the
+ *             scaled logits
+ *   page table: kv_indptr int32 [batch+1], kv_indices int32 [kv_indptr[batch]],
+ *             kv_last_page_len int32 [batch], 1 <= last <= page_size
+ *             (aicassindra, section "The block-sparse page table").
+ * Query head h attends with KV head h / (num_qo_heads / num_kv_heads).
+ *
+ * Ownership: the caller owns every buffer (inputs, outputs, the three
+ * workspaces).  The library never allocates device memory in pkd_plan,
+ * pkd_run or the merge calls.  A workspace must outlive every graph that
+ * captured a pkd_run using it.
+ *
+ * Errors: every call returns a pkd_status; nothing throws across the ABI.
+ * pkd_last_error() returns a thread-local message for the last failure.
+ *
+ * Streams: pkd_stream_t is a hipStream_t (NULL = the null stream).  A plan
+ * and the runs that use it must be ordered on the device (same stream, or
+ * synchronised by the caller).
+ */
+#ifndef PKD_H_
+#define PKD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct pkd_handle pkd_handle;
+typedef void* pkd_stream_t; /* hipStream_t */
+
+typedef enum pkd_status {
+  PKD_OK = 0,
+  PKD_ERR_INVALID_ARG = 1,         /* malformed page table or argument */
+  PKD_ERR_UNSUPPORTED = 2,         /* head_dim, dtype, layout or page size not built */
+  PKD_ERR_DTYPE_MISMATCH = 3,      /* run dtypes differ from the plan's */
+  PKD_ERR_WORKSPACE_TOO_SMALL = 4, /* a workspace cannot hold this plan */
+  PKD_ERR_STALE_PLAN = 5,          /* run before any plan, or batch differs from the plan */
+  PKD_ERR_HIP = 6                  /* a HIP runtime call failed */
+} pkd_status;
+
+enum { PKD_DTYPE_BF16 = 1, PKD_DTYPE_FP16 = 2, PKD_DTYPE_FP8_E4M3 = 3 };
+enum { PKD_LAYOUT_NHD = 0, PKD_LAYOUT_HND = 1 };
+
+/* Device error flags, read with pkd_read_device_error. */
+enum { PKD_DEVERR_PAGE_ID = 1 }; /* a kv_indices entry was < 0 or >= num_pages */
+
+/* Scheduling knobs.  A NULL pointer means all defaults. */
+typedef struct pkd_plan_opts {
+  int32_t fixed_chunk_pages; /* > 0: chunk size in pages (forces splits); 0: derived */
+  int32_t min_chunk_tokens;  /* smallest derived chunk, in tokens; <= 0: 128 */
+  int32_t alpha;             /* cost = alpha * l_q + beta * chunk_len, l_q = 1; */
+  int32_t beta;              /*   alpha < 0 or beta <= 0: 1 */
+} pkd_plan_opts;
+
+/* ---------------------------------------------------------------------
+ * Plan image.  The int workspace (and the output of pkd_plan_host) is an
+ * array of int32:
+ *   [0, 32)                       device-only words (error flag at 0)
+ *   [32, 64)                      header, PKD_H_* below at 32 + index
+ *   [off_slots, +S+1)             slot_indptr: items of slot s are
+ *                                 items[slot_indptr[s] .. slot_indptr[s+1])
+ *   [off_items, +8*I)             items, 8 ints each: request, page_begin
+ *                                 (index into kv_indices), num_pages,
+ *                                 last_len, out (partial id, -1 = write the
+ *                                 final output directly), length, 0, 0
+ *   [off_merge, +4*n_split)       split requests in ascending order: request,
+ *                                 first partial id, number of partials, 0
+ *   [off_indices, +nnz)           copy of kv_indices taken by pkd_plan
+ * The float workspace holds the partial states: o_part fp32
+ * [n_partials, num_qo_heads, head_dim] followed by lse_part fp32
+ * [n_partials, num_qo_heads].
+ * ------------------------------------------------------------------- */
+enum {
+  PKD_H_MAGIC = 0, /* 0x31444B50 */
+  PKD_H_VERSION,
+  PKD_H_BATCH,
+  PKD_H_QO_HEADS,
+  PKD_H_KV_HEADS,
+  PKD_H_HEAD_DIM,
+  PKD_H_PAGE_SIZE,
+  PKD_H_SLOTS,
+  PKD_H_CHUNK_PAGES,
+  PKD_H_ITEMS,
+  PKD_H_PARTIALS,
+  PKD_H_SPLIT,
+  PKD_H_ALPHA,
+  PKD_H_BETA,
+  PKD_H_NNZ,
+  PKD_H_PLAN_ID,
+  PKD_H_OFF_SLOTS,
+  PKD_H_OFF_ITEMS,
+  PKD_H_OFF_MERGE,
+  PKD_H_OFF_INDICES,
+  PKD_H_TOTAL_TOKENS_LO,
+  PKD_H_TOTAL_TOKENS_HI,
+  PKD_H_COUNT
+};
+#define PKD_HEADER_BASE 32
+#define PKD_PLAN_MAGIC 0x31444B50
+#define PKD_PLAN_VERSION 1
+
+/* ------------------------------- handle ------------------------------- */
+
+/* Create a handle bound to HIP device `device`.  `num_slots` is the number
+ * of persistent decode workgroups S (the fixed CTA count N_CTA of the
+ * pinghaoyang page's chunk bound); 0 picks 2 per compute unit.  No device
+ * memory is allocated. */
+int pkd_create(pkd_handle** out, int32_t device, int32_t num_slots);
+int pkd_destroy(pkd_handle* h);
+int32_t pkd_num_slots(const pkd_handle* h);
+/* Id of the last successful plan on this handle (0 before any); lets an
+ * engine assert that the plan matches its batch (aicassindra, "What to do
+ * next", item 3). */
+int64_t pkd_plan_id(const pkd_handle* h);
+const char* pkd_last_error(void);
+
+/* ----------------------------- workspaces ----------------------------- */
+
+/* Bytes each workspace needs for any plan with batch <= max_batch and
+ * kv_indptr[batch] <= max_nnz on S = num_slots slots and derived chunk sizes
+ * (a plan with fixed_chunk_pages may need more, and is refused with
+ * PKD_ERR_WORKSPACE_TOO_SMALL when it does not fit).  Sizing for the worst
+ * case is the caller's job (aicassindra, "Failure modes in production",
+ * workspace too small).  Returns 0 for invalid arguments. */
+size_t pkd_int_workspace_bytes(int32_t max_batch, int32_t max_nnz, int32_t num_slots);
+size_t pkd_float_workspace_bytes(int32_t max_batch, int32_t num_slots, int32_t num_qo_heads,
+                                 int32_t head_dim);
+/* Pinned host staging (allocate with hipHostMalloc or torch pin_memory);
+ * it holds two plan images so a new plan never overwrites one whose copy to
+ * the device is still in flight. */
+size_t pkd_host_workspace_bytes(int32_t max_batch, int32_t num_slots);
+
+/* -------------------------------- plan -------------------------------- */
+
+/* Validate the page table, cut each request's pages into chunks, assign the
+ * chunks longest-first to the handle's S slots, and write the schedule
+ * (pinghaoyang page, section on splitting long KV then longest-first
+ * assignment) into host_workspace; then queue on `stream` an asynchronous
+ * copy of it into int_workspace and a device-to-device copy of kv_indices
+ * behind it.  kv_indptr and kv_last_page_len are host arrays read during the
+ * call; kv_indices is a device array the caller may reuse once `stream` has
+ * passed this call.  Only PKD_DTYPE_BF16, PKD_LAYOUT_NHD, head_dim 128,
+ * num_qo_heads / num_kv_heads in {1, 2, 4, 8} and page_size in
+ * {1, 2, 4, 8, 16, 32, 64} are built.  Rejects (PKD_ERR_INVALID_ARG)
+ * kv_indptr[0] != 0, a request with no page, last_page_len outside
+ * [1, page_size], batch < 1, num_qo_heads not a multiple of num_kv_heads.
+ * The workspaces passed here are the ones later runs use. */
+int pkd_plan(pkd_handle* h, const int32_t* kv_indptr, const int32_t* kv_indices,
+             const int32_t* kv_last_page_len, int32_t batch, int32_t num_qo_heads,
+             int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t q_dtype,
+             int32_t kv_dtype, int32_t kv_layout, void* int_workspace,
+             size_t int_workspace_bytes, void* float_workspace, size_t float_workspace_bytes,
+             void* host_workspace, size_t host_workspace_bytes, const pkd_plan_opts* opts,
+             pkd_stream_t stream);
+
+/* The same schedule computed on the host only (no HIP call): writes the plan
+ * image ints [0, off_indices) described above into `out` (out_bytes long)
+ * and stores the number of ints written in *out_ints.  For inspection and
+ * tests; kv_indices are not needed. */
+int pkd_plan_host(const int32_t* kv_indptr, const int32_t* kv_last_page_len, int32_t batch,
+                  int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t page_size, int32_t num_slots, const pkd_plan_opts* opts,
+                  int32_t* out, size_t out_bytes, int64_t* out_ints);
+
+/* --------------------------------- run -------------------------------- */
+
+/* Decode attention for the planned batch on one layer's cache: o (and lse
+ * when non-NULL) for every request and query head.  Launches exactly two
+ * kernels on `stream` with grids fixed by the handle: the decode kernel (S
+ * workgroups) and the merge kernel.  `batch` must equal the planned batch
+ * and the dtypes the planned ones (else PKD_ERR_STALE_PLAN /
+ * PKD_ERR_DTYPE_MISMATCH).  sm_scale <= 0 means 1/sqrt(head_dim).  A page id
+ * outside [0, num_pages) is not read: the kernel uses page 0 instead and
+ * raises PKD_DEVERR_PAGE_ID (see pkd_read_device_error). */
+int pkd_run(pkd_handle* h, const void* q, int32_t batch, const void* kv_cache,
+            int64_t num_pages, int32_t q_dtype, int32_t kv_dtype, void* o, float* lse,
+            float sm_scale, pkd_stream_t stream);
+
+/* Waits for `stream`, returns the device error flags raised by runs since
+ * the last read (PKD_DEVERR_*, 0 if none) and clears them. */
+int pkd_read_device_error(pkd_handle* h, int32_t* flags, pkd_stream_t stream);
+
+/* -------------------------------- merge ------------------------------- */
+
+/* Merge two attention states row by row: for each of n*H rows,
+ * M = max(lse_a, lse_b), w = exp(lse - M), o = (w_a o_a + w_b o_b) / (w_a + w_b),
+ * lse = M + log(w_a + w_b) (pinghaoyang page, section on why online softmax
+ * allows any split; aicassindra, "Load balancing with split-KV").
+ * o_a, o_b, o_out: bf16 [n, H, D]; lse_a, lse_b, lse_out: fp32 [n, H],
+ * natural log.  Two empty states (lse = -inf) give o = 0, lse = -inf.
+ * o_out / lse_out may alias o_a / lse_a (in-place merge).  Only D = 128. */
+int pkd_merge_state(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                    int32_t n, int32_t H, int32_t D, void* o_out, float* lse_out,
+                    pkd_stream_t stream);
+
+/* Merge k states per row in index order: o bf16 [n, k, H, D], lse fp32
+ * [n, k, H] -> o_out bf16 [n, H, D], lse_out fp32 [n, H].  Only D = 128. */
+int pkd_merge_states(const void* o, const float* lse, int32_t n, int32_t k, int32_t H,
+                     int32_t D, void* o_out, float* lse_out, pkd_stream_t stream);
+
+/* ------------------------------ profiling ----------------------------- */
+
+/* When enabled, each pkd_run outside graph capture brackets its decode and
+ * merge launches with HIP events on its stream; pkd_profile_read waits for
+ * them and returns the summed kernel times in milliseconds and the number
+ * of runs, then resets the sums.  Off by default. */
+int pkd_profile_enable(pkd_handle* h, int32_t enable);
+int pkd_profile_read(pkd_handle* h, double* decode_ms, double* merge_ms, int64_t* runs);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKD_H_ */

@@ -1,0 +1,233 @@
+"""Python binding of libpkd (same names as the C ABI, marshalling only).
+
+torch is used for device memory, pinned host memory and streams; every step
+of the decode path runs in the library's HIP kernels or its host scheduler.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import _lib
+from ._lib import PkdError, check, pkd_plan_opts  # noqa: F401
+
+_DTYPES = None
+
+
+def _dtype_code(dtype) -> int:
+    import torch
+
+    global _DTYPES
+    if _DTYPES is None:
+        _DTYPES = {torch.bfloat16: _lib.PKD_DTYPE_BF16, torch.float16: _lib.PKD_DTYPE_FP16}
+        fp8 = getattr(torch, "float8_e4m3fn", None)
+        if fp8 is not None:
+            _DTYPES[fp8] = _lib.PKD_DTYPE_FP8_E4M3
+    if dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dtype}")
+    return _DTYPES[dtype]
+
+
+def _opts(fixed_chunk_pages=0, min_chunk_tokens=0, alpha=-1, beta=0):
+    return pkd_plan_opts(int(fixed_chunk_pages), int(min_chunk_tokens), int(alpha), int(beta))
+
+
+def _host_i32(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _stream_ptr(stream) -> int:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def plan_host(kv_indptr, kv_last_page_len, num_qo_heads, num_kv_heads, head_dim, page_size,
+              num_slots, **opts) -> dict:
+    """The schedule pkd_plan would upload, computed on the host (pkd_plan_host),
+    decoded into numpy arrays."""
+    L = _lib.load()
+    indptr = _host_i32(kv_indptr)
+    last = _host_i32(kv_last_page_len)
+    batch = last.shape[0]
+    cap = 64 + num_slots + 1 + 8 * (indptr[-1] + num_slots + 2 * batch) + 4 * batch + 64
+    out = np.zeros(int(cap), dtype=np.int32)
+    n = ctypes.c_int64(0)
+    o = _opts(**opts)
+    check(L.pkd_plan_host(indptr.ctypes.data, last.ctypes.data, batch, num_qo_heads, num_kv_heads,
+                          head_dim, page_size, num_slots, ctypes.byref(o), out.ctypes.data,
+                          out.nbytes, ctypes.byref(n)))
+    img = out[: n.value]
+    hdr = img[_lib.HEADER_BASE: _lib.HEADER_BASE + len(_lib.H_FIELDS)]
+    f = {name: int(hdr[i]) for name, i in _lib.H.items()}
+    S, I, ns = f["SLOTS"], f["ITEMS"], f["SPLIT"]
+    items8 = img[f["OFF_ITEMS"]: f["OFF_ITEMS"] + 8 * I].reshape(I, 8)
+    merges4 = img[f["OFF_MERGE"]: f["OFF_MERGE"] + 4 * ns].reshape(ns, 4)
+    return dict(header=f, image=img,
+                slot_indptr=img[f["OFF_SLOTS"]: f["OFF_SLOTS"] + S + 1].copy(),
+                items=items8[:, :5].copy(), item_lengths=items8[:, 5].copy(),
+                item_pad=items8[:, 6:].copy(), merges=merges4[:, :3].copy(),
+                chunk_pages=f["CHUNK_PAGES"], num_items=I, n_partials=f["PARTIALS"],
+                n_split=ns)
+
+
+def int_workspace_bytes(max_batch, max_nnz, num_slots) -> int:
+    return int(_lib.load().pkd_int_workspace_bytes(max_batch, max_nnz, num_slots))
+
+
+def float_workspace_bytes(max_batch, num_slots, num_qo_heads, head_dim) -> int:
+    return int(_lib.load().pkd_float_workspace_bytes(max_batch, num_slots, num_qo_heads, head_dim))
+
+
+def host_workspace_bytes(max_batch, num_slots) -> int:
+    return int(_lib.load().pkd_host_workspace_bytes(max_batch, num_slots))
+
+
+class DecodePlanRun:
+    """One plan slot: a pkd handle plus its three workspaces.
+
+    ``plan`` once per step (host page table, device kv_indices), ``run`` once
+    per layer.  Workspaces are sized at construction for ``max_batch``,
+    ``max_nnz`` and ``max_qo_heads`` and keep their addresses for the
+    object's life, so a run captured in a graph replays correctly after
+    later plans."""
+
+    def __init__(self, max_batch: int, max_nnz: int, max_qo_heads: int = 64, head_dim: int = 128,
+                 num_slots: int = 0, device=None):
+        import torch
+
+        self._L = _lib.load()
+        dev = torch.device("cuda", torch.cuda.current_device() if device is None else device) \
+            if not isinstance(device, torch.device) else device
+        self.device = dev
+        h = ctypes.c_void_p()
+        check(self._L.pkd_create(ctypes.byref(h), dev.index or 0, int(num_slots)))
+        self._h = h
+        S = self.num_slots
+        self.max_batch, self.max_nnz = int(max_batch), int(max_nnz)
+        ib = int_workspace_bytes(max_batch, max_nnz, S)
+        fb = float_workspace_bytes(max_batch, S, max_qo_heads, head_dim)
+        hb = host_workspace_bytes(max_batch, S)
+        self.int_workspace = torch.empty(ib, dtype=torch.uint8, device=dev)
+        self.float_workspace = torch.empty(fb, dtype=torch.uint8, device=dev)
+        self._host_raw = torch.empty(hb + 256, dtype=torch.uint8, pin_memory=True)
+        off = (-self._host_raw.data_ptr()) % 256
+        self.host_workspace = self._host_raw[off: off + hb]
+        self._planned = None
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._L.pkd_destroy(h)
+            self._h = None
+
+    @property
+    def num_slots(self) -> int:
+        return int(self._L.pkd_num_slots(self._h))
+
+    @property
+    def plan_id(self) -> int:
+        return int(self._L.pkd_plan_id(self._h))
+
+    def plan(self, kv_indptr, kv_indices, kv_last_page_len, num_qo_heads: int, num_kv_heads: int,
+             head_dim: int, page_size: int, q_data_type=None, kv_data_type=None,
+             kv_layout: str = "NHD", stream=None, **opts):
+        import torch
+
+        q_data_type = torch.bfloat16 if q_data_type is None else q_data_type
+        kv_data_type = torch.bfloat16 if kv_data_type is None else kv_data_type
+        indptr = _host_i32(kv_indptr)
+        last = _host_i32(kv_last_page_len)
+        if not (isinstance(kv_indices, torch.Tensor) and kv_indices.is_cuda
+                and kv_indices.dtype == torch.int32 and kv_indices.is_contiguous()):
+            raise ValueError("kv_indices must be a contiguous int32 tensor on the GPU")
+        layout = {"NHD": _lib.PKD_LAYOUT_NHD, "HND": _lib.PKD_LAYOUT_HND}[kv_layout]
+        o = _opts(**opts)
+        check(self._L.pkd_plan(
+            self._h, indptr.ctypes.data, kv_indices.data_ptr(), last.ctypes.data, last.shape[0],
+            num_qo_heads, num_kv_heads, head_dim, page_size, _dtype_code(q_data_type),
+            _dtype_code(kv_data_type), layout,
+            self.int_workspace.data_ptr(), self.int_workspace.numel(),
+            self.float_workspace.data_ptr(), self.float_workspace.numel(),
+            self.host_workspace.data_ptr(), self.host_workspace.numel(), ctypes.byref(o),
+            _stream_ptr(stream)))
+        self._planned = (last.shape[0], num_qo_heads, head_dim)
+        self._keep = kv_indices  # the copy is queued on the stream; keep the source alive
+
+    def run(self, q, kv_cache, out=None, lse=None, return_lse: bool = False, sm_scale=None,
+            stream=None):
+        import torch
+
+        if self._planned is None:
+            B, Hq, D = q.shape
+        else:
+            B, Hq, D = self._planned
+        if not (q.is_cuda and q.is_contiguous() and kv_cache.is_cuda and kv_cache.is_contiguous()):
+            raise ValueError("q and kv_cache must be contiguous GPU tensors")
+        if q.dim() != 3 or kv_cache.dim() != 5:
+            raise ValueError("q is [batch, Hq, D] and kv_cache [pages, 2, P, Hkv, D]")
+        if out is None:
+            out = torch.empty((q.shape[0], q.shape[1], q.shape[2]), dtype=torch.bfloat16,
+                              device=q.device)
+        if return_lse and lse is None:
+            lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=q.device)
+        check(self._L.pkd_run(self._h, q.data_ptr(), q.shape[0], kv_cache.data_ptr(),
+                              kv_cache.shape[0], _dtype_code(q.dtype), _dtype_code(kv_cache.dtype),
+                              out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                              float(sm_scale) if sm_scale is not None else 0.0,
+                              _stream_ptr(stream)))
+        return (out, lse) if (return_lse or lse is not None) else out
+
+    def read_device_error(self, stream=None) -> int:
+        v = ctypes.c_int32(0)
+        check(self._L.pkd_read_device_error(self._h, ctypes.byref(v), _stream_ptr(stream)))
+        return int(v.value)
+
+    def profile_enable(self, on: bool = True) -> None:
+        check(self._L.pkd_profile_enable(self._h, 1 if on else 0))
+
+    def profile_read(self):
+        d, m, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
+        check(self._L.pkd_profile_read(self._h, ctypes.byref(d), ctypes.byref(m), ctypes.byref(n)))
+        return d.value, m.value, n.value
+
+
+def merge_state(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, stream=None):
+    """Row-wise merge of two states (bf16 o [n, H, 128], fp32 lse [n, H])."""
+    import torch
+
+    n, Hh, D = o_a.shape
+    if out is None:
+        out = torch.empty_like(o_a)
+    if lse_out is None:
+        lse_out = torch.empty_like(lse_a)
+    for t in (o_a, lse_a, o_b, lse_b, out, lse_out):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("merge_state needs contiguous GPU tensors")
+    check(_lib.load().pkd_merge_state(o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(),
+                                      lse_b.data_ptr(), n, Hh, D, out.data_ptr(),
+                                      lse_out.data_ptr(), _stream_ptr(stream)))
+    return out, lse_out
+
+
+def merge_states(o, lse, out=None, lse_out=None, stream=None):
+    """Merge k states per row: bf16 o [n, k, H, 128], fp32 lse [n, k, H]."""
+    import torch
+
+    n, k, Hh, D = o.shape
+    if out is None:
+        out = torch.empty((n, Hh, D), dtype=o.dtype, device=o.device)
+    if lse_out is None:
+        lse_out = torch.empty((n, Hh), dtype=torch.float32, device=o.device)
+    for t in (o, lse, out, lse_out):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("merge_states needs contiguous GPU tensors")
+    check(_lib.load().pkd_merge_states(o.data_ptr(), lse.data_ptr(), n, k, Hh, D, out.data_ptr(),
+                                       lse_out.data_ptr(), _stream_ptr(stream)))
+    return out, lse_out

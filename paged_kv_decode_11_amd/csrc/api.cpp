@@ -1,0 +1,476 @@
+// C ABI of the paged GQA decode library (declared in include/pkd.h).
+//
+// pkd_plan runs the host scheduler into a pinned staging buffer and queues
+// its copy into the caller's int workspace, then a device-to-device copy of
+// kv_indices behind it (pinghaoyang FlashInfer page, "固定指针比固定内容更重要":
+// the plan is built in page-locked host memory and copied asynchronously into
+// a workspace at fixed offsets, so the run sees the same addresses with new
+// contents).  pkd_run launches the decode kernel on the handle's S slots and
+// the merge kernel on a fixed grid; neither launch depends on the plan's
+// contents, only on its head configuration, so a captured run stays valid
+// across plans with the same configuration and workspaces.
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "pkd.h"
+#include "plan.h"
+
+struct pkd_handle {
+  int device = 0;
+  int num_slots = 0;
+  int cu_count = 0;
+  int merge_grid = 0;
+  int waves_per_block = 0;
+  int64_t plan_counter = 0;
+
+  // current plan
+  bool planned = false;
+  int32_t batch = 0, Hq = 0, Hkv = 0, D = 0, P = 0, q_dtype = 0, kv_dtype = 0;
+  pkd::PlanLayout layout;
+  void* int_ws = nullptr;
+  size_t int_bytes = 0;
+  void* float_ws = nullptr;
+  size_t float_bytes = 0;
+  void* host_ws = nullptr;
+  size_t host_bytes = 0;
+  void* err_cleared_for = nullptr;
+
+  // staging halves
+  int staging_next = 0;
+  hipEvent_t staging_done[2] = {nullptr, nullptr};
+  bool staging_pending[2] = {false, false};
+
+  pkd::PlanScratch scratch;
+
+  // profiling
+  bool profile = false;
+  std::vector<hipEvent_t> prof_events;  // 3 per run: start, after decode, after merge
+  size_t prof_used = 0;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PKD_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Sets the handle's device for the duration of a call.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  hipError_t err = hipSuccess;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) {
+      err = hipSetDevice(dev);
+      ok = err == hipSuccess;
+    }
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+size_t ints_to_bytes(int64_t n) { return size_t(n) * sizeof(int32_t); }
+
+constexpr int64_t kStagingAlignInts = 64;  // 256-byte aligned halves
+
+int64_t staging_half_ints(int64_t max_batch, int64_t num_slots) {
+  const int64_t I = pkd::max_items(max_batch, num_slots);
+  const int64_t ints = pkd::plan_image_ints(num_slots, I, max_batch);
+  return (ints + kStagingAlignInts - 1) / kStagingAlignInts * kStagingAlignInts;
+}
+
+pkd::PlanInput make_input(const int32_t* indptr, const int32_t* last, int32_t batch, int32_t Hq,
+                          int32_t Hkv, int32_t D, int32_t P, int32_t S,
+                          const pkd_plan_opts* opts) {
+  pkd::PlanInput in;
+  in.indptr = indptr;
+  in.last = last;
+  in.batch = batch;
+  in.num_qo_heads = Hq;
+  in.num_kv_heads = Hkv;
+  in.head_dim = D;
+  in.page_size = P;
+  in.num_slots = S;
+  if (opts) {
+    in.fixed_chunk_pages = opts->fixed_chunk_pages;
+    in.min_chunk_tokens = opts->min_chunk_tokens;
+    in.alpha = opts->alpha;
+    in.beta = opts->beta;
+  }
+  return in;
+}
+
+int check_shapes(int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t q_dtype, int32_t kv_dtype,
+                 int32_t layout) {
+  if (q_dtype != PKD_DTYPE_BF16 || kv_dtype != PKD_DTYPE_BF16)
+    return fail(PKD_ERR_UNSUPPORTED, "only bf16 q and bf16 KV are built (pass PKD_DTYPE_BF16)");
+  if (layout != PKD_LAYOUT_NHD) return fail(PKD_ERR_UNSUPPORTED, "only the NHD cache layout is built");
+  if (D != pkd::kHeadDim) return fail(PKD_ERR_UNSUPPORTED, "only head_dim 128 is built");
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+    return fail(PKD_ERR_INVALID_ARG, "num_qo_heads must be a positive multiple of num_kv_heads");
+  if (!pkd::decode_variant_built(Hq / Hkv, P))
+    return fail(PKD_ERR_UNSUPPORTED,
+                "group size must be 1, 2, 4 or 8 and page_size 1, 2, 4, 8, 16, 32 or 64");
+  return PKD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkd_last_error(void) { return g_last_error.c_str(); }
+
+int pkd_create(pkd_handle** out, int32_t device, int32_t num_slots) {
+  if (!out) return fail(PKD_ERR_INVALID_ARG, "out must be non-null");
+  *out = nullptr;
+  if (num_slots < 0) return fail(PKD_ERR_INVALID_ARG, "num_slots must be >= 0");
+  int count = 0;
+  hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+  if (device < 0 || device >= count) return fail(PKD_ERR_INVALID_ARG, "no such HIP device");
+  DeviceGuard guard(device);
+  if (!guard.ok) return hip_fail(guard.err, "hipSetDevice");
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, device);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  pkd_handle* h = new pkd_handle();
+  h->device = device;
+  h->cu_count = prop.multiProcessorCount;
+  h->waves_per_block = pkd::kMaxWavesPerBlock;
+  h->num_slots = num_slots > 0 ? num_slots
+                               : h->cu_count * pkd::decode_blocks_per_cu(h->waves_per_block);
+  if (num_slots == 0 && h->num_slots > 2 * h->cu_count) h->num_slots = 2 * h->cu_count;
+  h->merge_grid = 4 * h->cu_count;
+  for (int i = 0; i < 2; ++i) {
+    e = hipEventCreateWithFlags(&h->staging_done[i], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      pkd_destroy(h);
+      return hip_fail(e, "hipEventCreate");
+    }
+  }
+  *out = h;
+  return PKD_OK;
+}
+
+int pkd_destroy(pkd_handle* h) {
+  if (!h) return PKD_OK;
+  DeviceGuard guard(h->device);
+  for (int i = 0; i < 2; ++i) {
+    if (h->staging_done[i]) {
+      (void)hipEventSynchronize(h->staging_done[i]);
+      (void)hipEventDestroy(h->staging_done[i]);
+    }
+  }
+  for (hipEvent_t ev : h->prof_events) (void)hipEventDestroy(ev);
+  delete h;
+  return PKD_OK;
+}
+
+int32_t pkd_num_slots(const pkd_handle* h) { return h ? h->num_slots : 0; }
+
+int64_t pkd_plan_id(const pkd_handle* h) { return h && h->planned ? h->plan_counter : 0; }
+
+size_t pkd_int_workspace_bytes(int32_t max_batch, int32_t max_nnz, int32_t num_slots) {
+  if (max_batch < 1 || max_nnz < 1 || num_slots < 1) return 0;
+  const int64_t I = pkd::max_items(max_batch, num_slots);
+  return ints_to_bytes(pkd::plan_image_ints(num_slots, I, max_batch) + max_nnz);
+}
+
+size_t pkd_float_workspace_bytes(int32_t max_batch, int32_t num_slots, int32_t num_qo_heads,
+                                 int32_t head_dim) {
+  if (max_batch < 1 || num_slots < 1 || num_qo_heads < 1 || head_dim < 1) return 0;
+  const int64_t I = pkd::max_items(max_batch, num_slots);
+  return size_t(I) * size_t(num_qo_heads) * size_t(head_dim + 1) * sizeof(float);
+}
+
+size_t pkd_host_workspace_bytes(int32_t max_batch, int32_t num_slots) {
+  if (max_batch < 1 || num_slots < 1) return 0;
+  return 2 * ints_to_bytes(staging_half_ints(max_batch, num_slots));
+}
+
+int pkd_plan_host(const int32_t* kv_indptr, const int32_t* kv_last_page_len, int32_t batch,
+                  int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t page_size, int32_t num_slots, const pkd_plan_opts* opts, int32_t* out,
+                  size_t out_bytes, int64_t* out_ints) {
+  pkd::PlanInput in = make_input(kv_indptr, kv_last_page_len, batch, num_qo_heads, num_kv_heads,
+                                 head_dim, page_size, num_slots, opts);
+  pkd::PlanScratch scratch;
+  pkd::PlanLayout layout;
+  std::string err;
+  int rc = pkd::plan_build(in, scratch, out, int64_t(out_bytes / sizeof(int32_t)), &layout, &err);
+  if (rc != PKD_OK) return fail(rc, err);
+  if (out_ints) *out_ints = layout.off_indices;
+  return PKD_OK;
+}
+
+int pkd_plan(pkd_handle* h, const int32_t* kv_indptr, const int32_t* kv_indices,
+             const int32_t* kv_last_page_len, int32_t batch, int32_t num_qo_heads,
+             int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t q_dtype,
+             int32_t kv_dtype, int32_t kv_layout, void* int_workspace,
+             size_t int_workspace_bytes, void* float_workspace, size_t float_workspace_bytes,
+             void* host_workspace, size_t host_workspace_bytes, const pkd_plan_opts* opts,
+             pkd_stream_t stream) {
+  if (!h) return fail(PKD_ERR_INVALID_ARG, "null handle");
+  int rc = check_shapes(num_qo_heads, num_kv_heads, head_dim, page_size, q_dtype, kv_dtype,
+                        kv_layout);
+  if (rc != PKD_OK) return rc;
+  if (!kv_indices || !int_workspace || !float_workspace || !host_workspace)
+    return fail(PKD_ERR_INVALID_ARG, "kv_indices and the three workspaces must be non-null");
+  if ((reinterpret_cast<uintptr_t>(int_workspace) & 255) ||
+      (reinterpret_cast<uintptr_t>(float_workspace) & 255) ||
+      (reinterpret_cast<uintptr_t>(host_workspace) & 255))
+    return fail(PKD_ERR_INVALID_ARG, "workspaces must be 256-byte aligned");
+
+  DeviceGuard guard(h->device);
+  if (!guard.ok) return hip_fail(guard.err, "hipSetDevice");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  // Build into the staging half that is not the latest in-flight copy.
+  const int half = h->staging_next;
+  if (h->staging_pending[half]) {
+    hipError_t e = hipEventSynchronize(h->staging_done[half]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    h->staging_pending[half] = false;
+  }
+  const int64_t half_ints = int64_t(host_workspace_bytes / sizeof(int32_t) / 2) /
+                            kStagingAlignInts * kStagingAlignInts;
+  int32_t* image = static_cast<int32_t*>(host_workspace) + half * half_ints;
+
+  pkd::PlanInput in = make_input(kv_indptr, kv_last_page_len, batch, num_qo_heads, num_kv_heads,
+                                 head_dim, page_size, h->num_slots, opts);
+  in.plan_id = h->plan_counter + 1;
+  pkd::PlanLayout layout;
+  std::string err;
+  rc = pkd::plan_build(in, h->scratch, image, half_ints, &layout, &err);
+  if (rc == PKD_ERR_WORKSPACE_TOO_SMALL)
+    return fail(rc, "host workspace too small for this plan (size it with pkd_host_workspace_bytes)");
+  if (rc != PKD_OK) return fail(rc, err);
+
+  const size_t need_int = ints_to_bytes(layout.off_indices + layout.nnz);
+  const size_t need_float =
+      size_t(layout.n_partials) * size_t(num_qo_heads) * size_t(head_dim + 1) * sizeof(float);
+  if (int_workspace_bytes < need_int)
+    return fail(PKD_ERR_WORKSPACE_TOO_SMALL, "int workspace too small for this plan (needs " +
+                                                 std::to_string(need_int) + " bytes)");
+  if (float_workspace_bytes < need_float)
+    return fail(PKD_ERR_WORKSPACE_TOO_SMALL, "float workspace too small for this plan (needs " +
+                                                 std::to_string(need_float) + " bytes)");
+
+  hipError_t e;
+  if (h->err_cleared_for != int_workspace) {
+    // fresh workspace: clear the device-only words (error flag) once
+    e = hipMemsetAsync(int_workspace, 0, ints_to_bytes(PKD_HEADER_BASE), s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync");
+    h->err_cleared_for = int_workspace;
+  }
+  int32_t* dev = static_cast<int32_t*>(int_workspace);
+  e = hipMemcpyAsync(dev + PKD_HEADER_BASE, image + PKD_HEADER_BASE,
+                     ints_to_bytes(layout.off_indices - PKD_HEADER_BASE), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan)");
+  e = hipEventRecord(h->staging_done[half], s);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  h->staging_pending[half] = true;
+  h->staging_next = half ^ 1;
+  e = hipMemcpyAsync(dev + layout.off_indices, kv_indices, ints_to_bytes(layout.nnz),
+                     hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (kv_indices)");
+
+  h->planned = true;
+  h->plan_counter += 1;
+  h->batch = batch;
+  h->Hq = num_qo_heads;
+  h->Hkv = num_kv_heads;
+  h->D = head_dim;
+  h->P = page_size;
+  h->q_dtype = q_dtype;
+  h->kv_dtype = kv_dtype;
+  h->layout = layout;
+  h->int_ws = int_workspace;
+  h->int_bytes = int_workspace_bytes;
+  h->float_ws = float_workspace;
+  h->float_bytes = float_workspace_bytes;
+  h->host_ws = host_workspace;
+  h->host_bytes = host_workspace_bytes;
+  return PKD_OK;
+}
+
+int pkd_run(pkd_handle* h, const void* q, int32_t batch, const void* kv_cache, int64_t num_pages,
+            int32_t q_dtype, int32_t kv_dtype, void* o, float* lse, float sm_scale,
+            pkd_stream_t stream) {
+  if (!h) return fail(PKD_ERR_INVALID_ARG, "null handle");
+  if (!h->planned) return fail(PKD_ERR_STALE_PLAN, "pkd_run before any pkd_plan on this handle");
+  if (batch != h->batch)
+    return fail(PKD_ERR_STALE_PLAN, "batch " + std::to_string(batch) + " differs from the planned batch " +
+                                        std::to_string(h->batch) + " (call pkd_plan for this batch)");
+  if (q_dtype != h->q_dtype || kv_dtype != h->kv_dtype)
+    return fail(PKD_ERR_DTYPE_MISMATCH, "run dtypes differ from the dtypes the plan was made for");
+  if (!q || !kv_cache || !o) return fail(PKD_ERR_INVALID_ARG, "q, kv_cache and o must be non-null");
+  if (num_pages < 1) return fail(PKD_ERR_INVALID_ARG, "num_pages must be >= 1");
+  if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(kv_cache) & 15) ||
+      (reinterpret_cast<uintptr_t>(o) & 15))
+    return fail(PKD_ERR_INVALID_ARG, "q, kv_cache and o must be 16-byte aligned");
+  if (!(std::isfinite(sm_scale))) return fail(PKD_ERR_INVALID_ARG, "sm_scale must be finite");
+
+  DeviceGuard guard(h->device);
+  if (!guard.ok) return hip_fail(guard.err, "hipSetDevice");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  const float scale = sm_scale > 0.f ? sm_scale : 1.f / std::sqrt(float(h->D));
+  pkd::DecodeParams dp;
+  dp.q = static_cast<const uint16_t*>(q);
+  dp.kv = static_cast<const uint16_t*>(kv_cache);
+  dp.o = static_cast<uint16_t*>(o);
+  dp.lse = lse;
+  dp.ws = static_cast<const int32_t*>(h->int_ws);
+  dp.fws = static_cast<float*>(h->float_ws);
+  dp.err = static_cast<int32_t*>(h->int_ws);
+  dp.num_pages = num_pages;
+  dp.scale_log2 = scale * 1.44269504088896341f;
+  dp.num_qo_heads = h->Hq;
+  dp.num_kv_heads = h->Hkv;
+
+  pkd::MergeParams mp;
+  std::memset(&mp, 0, sizeof(mp));
+  mp.o_in = h->float_ws;
+  mp.lse_in = nullptr;  // located from the plan header on the device
+  mp.o_stride_c = int64_t(h->Hq) * pkd::kHeadDim;
+  mp.lse_stride_c = h->Hq;
+  mp.ws = static_cast<const int32_t*>(h->int_ws);
+  mp.H = h->Hq;
+  mp.o_out = static_cast<uint16_t*>(o);
+  mp.lse_out = lse;
+
+  bool prof = false;
+  hipEvent_t* ev = nullptr;
+  if (h->profile) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone) {
+      if (h->prof_used + 3 > h->prof_events.size()) {
+        for (int i = 0; i < 3; ++i) {
+          hipEvent_t x;
+          hipError_t e = hipEventCreate(&x);
+          if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+          h->prof_events.push_back(x);
+        }
+      }
+      ev = &h->prof_events[h->prof_used];
+      h->prof_used += 3;
+      prof = true;
+    }
+  }
+
+  hipError_t e;
+  if (prof && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = pkd::launch_decode(dp, h->Hq / h->Hkv, h->P, h->num_slots, s);
+  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+  if (prof && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = pkd::launch_merge_partials(mp, h->merge_grid, s);
+  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  if (prof && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return PKD_OK;
+}
+
+int pkd_read_device_error(pkd_handle* h, int32_t* flags, pkd_stream_t stream) {
+  if (!h || !flags) return fail(PKD_ERR_INVALID_ARG, "null argument");
+  *flags = 0;
+  if (!h->int_ws) return PKD_OK;
+  DeviceGuard guard(h->device);
+  if (!guard.ok) return hip_fail(guard.err, "hipSetDevice");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t value = 0;
+  hipError_t e = hipMemcpyAsync(&value, h->int_ws, sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "reading the device error word");
+  if (value != 0) {
+    static const int32_t zero = 0;
+    e = hipMemcpyAsync(h->int_ws, &zero, sizeof(int32_t), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "clearing the device error word");
+  }
+  *flags = value;
+  return PKD_OK;
+}
+
+int pkd_merge_state(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                    int32_t n, int32_t H, int32_t D, void* o_out, float* lse_out,
+                    pkd_stream_t stream) {
+  if (D != pkd::kHeadDim) return fail(PKD_ERR_UNSUPPORTED, "only head_dim 128 is built");
+  if (n < 0 || H < 1) return fail(PKD_ERR_INVALID_ARG, "n must be >= 0 and H >= 1");
+  if (n == 0) return PKD_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !o_out || !lse_out)
+    return fail(PKD_ERR_INVALID_ARG, "null pointer");
+  hipError_t e = pkd::launch_merge_two_bf16(
+      static_cast<const uint16_t*>(o_a), lse_a, static_cast<const uint16_t*>(o_b), lse_b,
+      int64_t(n) * H, static_cast<uint16_t*>(o_out), lse_out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge_state launch");
+  return PKD_OK;
+}
+
+int pkd_merge_states(const void* o, const float* lse, int32_t n, int32_t k, int32_t H, int32_t D,
+                     void* o_out, float* lse_out, pkd_stream_t stream) {
+  if (D != pkd::kHeadDim) return fail(PKD_ERR_UNSUPPORTED, "only head_dim 128 is built");
+  if (n < 0 || k < 1 || H < 1) return fail(PKD_ERR_INVALID_ARG, "n >= 0, k >= 1 and H >= 1 required");
+  if (n == 0) return PKD_OK;
+  if (!o || !lse || !o_out) return fail(PKD_ERR_INVALID_ARG, "null pointer");
+  pkd::MergeParams mp;
+  std::memset(&mp, 0, sizeof(mp));
+  mp.o_in = o;
+  mp.lse_in = lse;
+  mp.o_stride_c = int64_t(H) * pkd::kHeadDim;
+  mp.lse_stride_c = H;
+  mp.rows = n;
+  mp.k = k;
+  mp.H = H;
+  mp.o_out = static_cast<uint16_t*>(o_out);
+  mp.lse_out = lse_out;
+  hipError_t e = pkd::launch_merge_states_bf16(mp, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge_states launch");
+  return PKD_OK;
+}
+
+int pkd_profile_enable(pkd_handle* h, int32_t enable) {
+  if (!h) return fail(PKD_ERR_INVALID_ARG, "null handle");
+  h->profile = enable != 0;
+  return PKD_OK;
+}
+
+int pkd_profile_read(pkd_handle* h, double* decode_ms, double* merge_ms, int64_t* runs) {
+  if (!h || !decode_ms || !merge_ms || !runs) return fail(PKD_ERR_INVALID_ARG, "null argument");
+  DeviceGuard guard(h->device);
+  double dsum = 0, msum = 0;
+  int64_t n = 0;
+  for (size_t i = 0; i + 3 <= h->prof_used; i += 3) {
+    hipError_t e = hipEventSynchronize(h->prof_events[i + 2]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float a = 0, b = 0;
+    e = hipEventElapsedTime(&a, h->prof_events[i], h->prof_events[i + 1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&b, h->prof_events[i + 1], h->prof_events[i + 2]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    dsum += a;
+    msum += b;
+    ++n;
+  }
+  h->prof_used = 0;
+  *decode_ms = dsum;
+  *merge_ms = msum;
+  *runs = n;
+  return PKD_OK;
+}
+
+}  // extern "C"

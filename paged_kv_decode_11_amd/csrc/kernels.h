@@ -1,0 +1,60 @@
+// Kernel parameter blocks and launchers shared by the C ABI (api.cpp) and
+// the HIP kernels (decode.hip, merge.hip).  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+namespace pkd {
+
+constexpr int kHeadDim = 128;
+constexpr int kMaxWavesPerBlock = 8;
+
+struct DecodeParams {
+  const uint16_t* q;   // bf16 [B, Hq, 128]
+  const uint16_t* kv;  // bf16 [num_pages, 2, P, Hkv, 128]
+  uint16_t* o;         // bf16 [B, Hq, 128]
+  float* lse;          // fp32 [B, Hq] or null
+  const int32_t* ws;   // int workspace (plan image + kv_indices copy)
+  float* fws;          // float workspace (partial states)
+  int32_t* err;        // device error word
+  int64_t num_pages;
+  float scale_log2;    // sm_scale * log2(e)
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+};
+
+struct MergeParams {
+  // task t = (row r = t / H, head h = t % H); state c of a task:
+  //   o at  o_in + (row_base(r) + c) * o_stride_c + h * 128   (fp32 or bf16)
+  //   lse at lse_in + (row_base(r) + c) * lse_stride_c + h
+  const void* o_in;
+  const float* lse_in;
+  int64_t o_stride_c;
+  int64_t lse_stride_c;
+  const int32_t* ws;   // plan image (partials mode) or null (uniform mode)
+  int32_t rows;        // uniform mode: number of rows
+  int32_t k;           // uniform mode: states per row
+  int32_t H;
+  uint16_t* o_out;     // bf16 [.., H, 128]
+  float* lse_out;      // fp32 [.., H] or null
+};
+
+// Decode kernel for group size g and page size P (both must be built).
+hipError_t launch_decode(const DecodeParams& p, int g, int page_size, int num_slots,
+                         hipStream_t stream);
+bool decode_variant_built(int g, int page_size);
+// Occupancy (workgroups per CU) of the decode kernel at g=4, P=16.
+int decode_blocks_per_cu(int waves_per_block);
+
+// Merge of the split requests of the current plan (reads the plan image).
+hipError_t launch_merge_partials(const MergeParams& p, int grid, hipStream_t stream);
+// Merge of `k` bf16 states per row, rows laid out uniformly.
+hipError_t launch_merge_states_bf16(const MergeParams& p, hipStream_t stream);
+// Row-wise merge of two bf16 states.
+hipError_t launch_merge_two_bf16(const uint16_t* o_a, const float* lse_a, const uint16_t* o_b,
+                                 const float* lse_b, int64_t rows, uint16_t* o_out,
+                                 float* lse_out, hipStream_t stream);
+
+}  // namespace pkd

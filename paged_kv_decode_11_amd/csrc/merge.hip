@@ -1,0 +1,218 @@
+// Merge of attention states for gfx950.
+//
+// The combine is the one on the pinghaoyang FlashInfer page, section
+// "在线 Softmax 为什么允许任意切块" (why online softmax allows any split), and
+// in aicassindra "Load balancing with split-KV": with M = max_c lse_c and
+// w_c = exp(lse_c - M), the merged state is o = sum_c w_c o_c / sum_c w_c and
+// lse = M + log sum_c w_c.  States are merged in a fixed order with no
+// atomics, so results are reproducible (pinghaoyang, Stream-K paragraph).
+//
+// One workgroup (256 lanes) per (row, query head) task, tasks taken in a
+// grid-stride loop so the grid is fixed.  Pass 1 finds M over the task's lse
+// values; pass 2 splits the states over 8 groups of 32 lanes (4 elements of
+// head_dim per lane, state c to group c mod 8), and the 8 group sums are
+// added in group order.  Empty states (lse = -inf) get weight 0; a task with
+// only empty states yields o = 0, lse = -inf.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.h"
+#include "pkd.h"
+
+namespace pkd {
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr int kMergeThreads = 256;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v;
+  v.x = (__bf16)lo;
+  v.y = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+__device__ __forceinline__ float4 load4(const uint16_t* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+}
+
+// Where a task's states are and where its result goes.
+struct Task {
+  int64_t first;    // index of state 0 (times the strides below)
+  int k;            // number of states
+  int64_t out_row;  // output row (request)
+};
+
+template <typename OT>
+__device__ void merge_task(const MergeParams& p, const Task& t, int h, float* red,
+                           float* grp_s, float4* grp_acc) {
+  const int tid = threadIdx.x;
+  const int grp = tid >> 5;
+  const int gl = tid & 31;
+  const OT* o_in = static_cast<const OT*>(p.o_in);
+
+  // pass 1: M = max lse
+  float mx = kNegInf;
+  for (int c = tid; c < t.k; c += kMergeThreads)
+    mx = fmaxf(mx, p.lse_in[(t.first + c) * p.lse_stride_c + h]);
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
+  // pass 2: weighted sums per group
+  float s = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (mx != kNegInf) {
+#pragma unroll 4
+    for (int c = grp; c < t.k; c += 8) {
+      const int64_t st = t.first + c;
+      const float L = p.lse_in[st * p.lse_stride_c + h];
+      const float4 v = load4(o_in + st * p.o_stride_c + int64_t(h) * kHeadDim + gl * 4);
+      const float w = __builtin_amdgcn_exp2f((L - mx) * kLog2e);
+      s += w;
+      acc.x = fmaf(w, v.x, acc.x);
+      acc.y = fmaf(w, v.y, acc.y);
+      acc.z = fmaf(w, v.z, acc.z);
+      acc.w = fmaf(w, v.w, acc.w);
+    }
+  }
+  if (gl == 0) grp_s[grp] = s;
+  grp_acc[grp * 32 + gl] = acc;
+  __syncthreads();
+
+  if (grp == 0) {
+    float S = 0.f;
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      S += grp_s[g];
+      const float4 a = grp_acc[g * 32 + gl];
+      A.x += a.x;
+      A.y += a.y;
+      A.z += a.z;
+      A.w += a.w;
+    }
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lse = kNegInf;
+    if (mx != kNegInf) {
+      const float inv = 1.f / S;
+      o = make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
+      lse = mx + __log2f(S) * kLn2;
+    }
+    uint2 w;
+    w.x = pack_bf16x2(o.x, o.y);
+    w.y = pack_bf16x2(o.z, o.w);
+    *reinterpret_cast<uint2*>(p.o_out + (t.out_row * p.H + h) * kHeadDim + gl * 4) = w;
+    if (p.lse_out && gl == 0) p.lse_out[t.out_row * p.H + h] = lse;
+  }
+  __syncthreads();
+}
+
+// Split requests of the current plan: fp32 partials in the float workspace.
+__global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(MergeParams p) {
+  __shared__ float red[4];
+  __shared__ float grp_s[8];
+  __shared__ float4 grp_acc[8 * 32];
+  const int32_t* hdr = p.ws + PKD_HEADER_BASE;
+  const int n_split = hdr[PKD_H_SPLIT];
+  const int H = p.H;
+  const int64_t n_partials = hdr[PKD_H_PARTIALS];
+  const int32_t* merges = p.ws + hdr[PKD_H_OFF_MERGE];
+  MergeParams q = p;
+  q.lse_in = static_cast<const float*>(p.o_in) + n_partials * H * kHeadDim;
+  const int tasks = n_split * H;
+  for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+    const int e = task / H;
+    const int h = task - e * H;
+    Task t;
+    t.out_row = merges[4 * e + 0];
+    t.first = merges[4 * e + 1];
+    t.k = merges[4 * e + 2];
+    merge_task<float>(q, t, h, red, grp_s, grp_acc);
+  }
+}
+
+// k bf16 states per row, rows laid out uniformly.
+__global__ __launch_bounds__(kMergeThreads) void merge_states_kernel(MergeParams p) {
+  __shared__ float red[4];
+  __shared__ float grp_s[8];
+  __shared__ float4 grp_acc[8 * 32];
+  const int64_t tasks = int64_t(p.rows) * p.H;
+  for (int64_t task = blockIdx.x; task < tasks; task += gridDim.x) {
+    const int64_t row = task / p.H;
+    const int h = int(task - row * p.H);
+    Task t;
+    t.out_row = row;
+    t.first = row * p.k;
+    t.k = p.k;
+    merge_task<uint16_t>(p, t, h, red, grp_s, grp_acc);
+  }
+}
+
+// Two bf16 states per row; 32 lanes per row, 4 elements per lane.
+__global__ __launch_bounds__(256) void merge_two_kernel(const uint16_t* o_a, const float* lse_a,
+                                                        const uint16_t* o_b, const float* lse_b,
+                                                        int64_t rows, uint16_t* o_out,
+                                                        float* lse_out) {
+  const int64_t row = int64_t(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  const int gl = threadIdx.x & 31;
+  if (row >= rows) return;
+  const float la = lse_a[row];
+  const float lb = lse_b[row];
+  const float4 a = load4(o_a + row * kHeadDim + gl * 4);
+  const float4 b = load4(o_b + row * kHeadDim + gl * 4);
+  const float M = fmaxf(la, lb);
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float lse = kNegInf;
+  if (M != kNegInf) {
+    const float wa = __builtin_amdgcn_exp2f((la - M) * kLog2e);
+    const float wb = __builtin_amdgcn_exp2f((lb - M) * kLog2e);
+    const float inv = 1.f / (wa + wb);
+    o = make_float4((wa * a.x + wb * b.x) * inv, (wa * a.y + wb * b.y) * inv,
+                    (wa * a.z + wb * b.z) * inv, (wa * a.w + wb * b.w) * inv);
+    lse = M + __log2f(wa + wb) * kLn2;
+  }
+  uint2 w;
+  w.x = pack_bf16x2(o.x, o.y);
+  w.y = pack_bf16x2(o.z, o.w);
+  *reinterpret_cast<uint2*>(o_out + row * kHeadDim + gl * 4) = w;
+  if (gl == 0) lse_out[row] = lse;
+}
+
+}  // namespace
+
+hipError_t launch_merge_partials(const MergeParams& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(merge_partials_kernel, dim3(grid), dim3(kMergeThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_states_bf16(const MergeParams& p, hipStream_t stream) {
+  const int64_t tasks = int64_t(p.rows) * p.H;
+  const int grid = int(tasks < 65536 ? tasks : 65536);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(merge_states_kernel, dim3(grid), dim3(kMergeThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_two_bf16(const uint16_t* o_a, const float* lse_a, const uint16_t* o_b,
+                                 const float* lse_b, int64_t rows, uint16_t* o_out,
+                                 float* lse_out, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const int64_t grid = (rows + 7) / 8;
+  hipLaunchKernelGGL(merge_two_kernel, dim3(unsigned(grid)), dim3(256), 0, stream, o_a, lse_a,
+                     o_b, lse_b, rows, o_out, lse_out);
+  return hipGetLastError();
+}
+
+}  // namespace pkd

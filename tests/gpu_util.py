@@ -1,0 +1,96 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device, run
+the library through its binding, and compare with the oracle."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+TOL_O = 1e-2    # max abs error on the bf16 output
+TOL_LSE = 1e-3  # max abs error on lse
+
+
+def say(*args):
+    print("[gpu-case]", *args, file=sys.stderr, flush=True)
+
+
+def bits_to_dev(bits: np.ndarray):
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).cuda()
+
+
+def dev_to_f64(t) -> np.ndarray:
+    import torch
+
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def dev_bits(t) -> np.ndarray:
+    import torch
+
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+_RUNNERS = {}
+
+
+def runner(max_batch=512, max_nnz=1 << 17, max_qo_heads=64, num_slots=0):
+    import paged_kv_decode_11_amd as pkd
+
+    key = (max_batch, max_nnz, max_qo_heads, num_slots)
+    if key not in _RUNNERS:
+        _RUNNERS[key] = pkd.DecodePlanRun(max_batch, max_nnz, max_qo_heads, 128, num_slots)
+    return _RUNNERS[key]
+
+
+def decode(batch, q_dev, cache_dev, r=None, sm_scale=None, return_lse=True, **opts):
+    """Plan + run; returns (o [B,Hq,D] bf16 tensor, lse tensor or None)."""
+    import torch
+
+    r = r or runner()
+    idx = torch.from_numpy(batch.kv_indices.astype(np.int32)).cuda()
+    r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, batch.num_qo_heads, batch.num_kv_heads,
+           batch.head_dim, batch.page_size, **opts)
+    res = r.run(q_dev, cache_dev, return_lse=return_lse, sm_scale=sm_scale)
+    torch.cuda.synchronize()
+    return res if return_lse else (res, None)
+
+
+def assert_close(o_dev, lse_dev, o_ref, lse_ref, requests=None, label=""):
+    o = dev_to_f64(o_dev)
+    rows = slice(None) if requests is None else list(requests)
+    err_o = np.max(np.abs(o[rows] - o_ref[rows]))
+    assert np.all(np.isfinite(o[rows])), f"{label}: non-finite output"
+    max_ref = np.max(np.abs(o_ref[rows]))
+    # bf16 half-ulp reaches the tolerance only for |o| >= 4; report if it happens
+    assert max_ref < 4.0, f"{label}: |o| = {max_ref} is outside the tolerance's range"
+    assert err_o <= TOL_O, f"{label}: max |o - o_ref| = {err_o}"
+    if lse_dev is not None:
+        lse = lse_dev.detach().cpu().numpy().astype(np.float64)
+        err_l = np.max(np.abs(lse[rows] - lse_ref[rows]))
+        assert err_l <= TOL_LSE, f"{label}: max |lse - lse_ref| = {err_l}"
+        return err_o, err_l
+    return err_o, None
+
+
+def compact_pages(batch, cache_dev, requests):
+    """Copy the pages of `requests` from a device cache to the host; return a
+    compact host cache and the remapped page table for those requests (as a
+    smaller batch, in the given order)."""
+    import torch
+
+    rows, lens = [], []
+    for i in requests:
+        rows.append(batch.kv_indices[batch.kv_indptr[i]:batch.kv_indptr[i + 1]])
+        lens.append(int(batch.kv_lens[i]))
+    pages = np.unique(np.concatenate(rows))
+    sel = torch.from_numpy(pages.astype(np.int64)).cuda()
+    host = dev_bits(cache_dev.index_select(0, sel))
+    remap = {int(p): j for j, p in enumerate(pages)}
+    indptr = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+    indices = np.array([remap[int(p)] for r in rows for p in r], dtype=np.int32)
+    last = np.array([batch.kv_last_page_len[i] for i in requests], dtype=np.int32)
+    return host, indptr, indices, last

@@ -1,0 +1,116 @@
+"""Decode parity on the GPU: the HIP path (through the C ABI) against the
+fp64 oracle, element by element, on seeded inputs.  Bar: max abs error
+<= 1e-2 on the bf16 output and <= 1e-3 on lse."""
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import attention as att
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _small(seed, lens, P, Hq, Hkv, poison=True, spare=9):
+    rng = np.random.default_rng(seed)
+    need = int(sum(-(-l // P) for l in lens))
+    batch = workloads.make_batch(lens, P, need + spare, Hq, Hkv, 128, rng)
+    q = workloads.host_query(batch, rng)
+    cache = workloads.host_cache(batch, rng, poison=poison)
+    return batch, q, cache
+
+
+def _check(batch, q, cache, label, sm_scale=None, return_lse=True, r=None, **opts):
+    gu.say(label, "B", batch.batch, "P", batch.page_size, "Hq", batch.num_qo_heads,
+           "Hkv", batch.num_kv_heads, "T", batch.total_tokens, opts)
+    o_ref, lse_ref = att.decode(q, cache, batch.kv_indptr, batch.kv_indices,
+                                batch.kv_last_page_len, batch.num_kv_heads, sm_scale=sm_scale)
+    o, lse = gu.decode(batch, gu.bits_to_dev(q), gu.bits_to_dev(cache), r=r, sm_scale=sm_scale,
+                       return_lse=return_lse, **opts)
+    return gu.assert_close(o, lse, o_ref, lse_ref, label=label)
+
+
+def test_tiny_workload_writethrough():
+    spec, rng, b = workloads.workload("tiny")
+    batch = b["main"]
+    q = workloads.host_query(batch, rng)
+    cache = workloads.host_cache(batch, rng, poison=True)
+    _check(batch, q, cache, "tiny")
+
+
+def test_tiny_worked_example_pages():
+    rng = np.random.default_rng(0)
+    batch = workloads.make_batch([37, 16, 5], 16, 64, 32, 8, 128, rng, scatter=False)
+    assert batch.kv_indptr.tolist() == [0, 3, 4, 5]
+    q = workloads.host_query(batch, rng)
+    cache = workloads.host_cache(batch, rng, poison=True)
+    _check(batch, q, cache, "worked-example")
+
+
+@pytest.mark.parametrize("fixed", [1, 2])
+def test_tiny_forced_splits(fixed):
+    spec, rng, b = workloads.workload("tiny")
+    batch = b["main"]
+    q = workloads.host_query(batch, rng)
+    cache = workloads.host_cache(batch, rng, poison=True)
+    _check(batch, q, cache, f"tiny-split{fixed}", fixed_chunk_pages=fixed)
+
+
+@pytest.mark.parametrize("P", [1, 2, 4, 8, 16, 32, 64])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_page_sizes_and_groups(P, G):
+    Hkv = 8 if G <= 4 else 4
+    lens = sorted(set(workloads.edge_lengths(P) + [3 * P + 5, 77, 300]))
+    batch, q, cache = _small(10 * P + G, lens, P, Hkv * G, Hkv)
+    _check(batch, q, cache, f"P{P}-G{G}")
+    _check(batch, q, cache, f"P{P}-G{G}-split", fixed_chunk_pages=1 if P >= 16 else max(1, 48 // P))
+
+
+@pytest.mark.parametrize("Hkv", [1, 2, 3, 8, 12, 16])
+def test_kv_head_counts(Hkv):
+    """Fewer waves than 8 per workgroup (Hkv < 8) and heads looped over
+    waves (Hkv > 8)."""
+    batch, q, cache = _small(50 + Hkv, [1, 40, 129, 500], 16, 4 * Hkv, Hkv)
+    _check(batch, q, cache, f"Hkv{Hkv}")
+    _check(batch, q, cache, f"Hkv{Hkv}-split", min_chunk_tokens=16)
+
+
+def test_no_lse_and_custom_scale():
+    batch, q, cache = _small(7, [100, 33, 1], 16, 32, 8)
+    _check(batch, q, cache, "no-lse", return_lse=False)
+    _check(batch, q, cache, "scale0.3", sm_scale=0.3)
+    _check(batch, q, cache, "scale0.3-split", sm_scale=0.3, fixed_chunk_pages=2)
+
+
+def test_single_token_requests():
+    batch, q, cache = _small(8, [1] * 37, 16, 32, 8)
+    _check(batch, q, cache, "ones")
+
+
+def test_random_batches_many_splits():
+    rng = np.random.default_rng(99)
+    for trial in range(4):
+        lens = rng.integers(1, 2000, size=int(rng.integers(1, 40)))
+        batch, q, cache = _small(200 + trial, lens.tolist(), 16, 32, 8)
+        _check(batch, q, cache, f"random{trial}")
+        _check(batch, q, cache, f"random{trial}-mct16", min_chunk_tokens=16)
+
+
+def test_few_slots_long_queues():
+    """A handle with 3 slots: each workgroup walks many items."""
+    r = gu.runner(max_batch=64, max_nnz=1 << 14, num_slots=3)
+    assert r.num_slots == 3
+    batch, q, cache = _small(31, [700, 20, 1, 999, 64, 65], 16, 32, 8)
+    _check(batch, q, cache, "3slots", r=r)
+    _check(batch, q, cache, "3slots-split", r=r, fixed_chunk_pages=4)
+
+
+def test_outputs_are_deterministic():
+    import torch
+
+    batch, q, cache = _small(12, [3000, 17, 900], 16, 32, 8)
+    qd, cd = gu.bits_to_dev(q), gu.bits_to_dev(cache)
+    o1, l1 = gu.decode(batch, qd, cd, min_chunk_tokens=16)
+    o2, l2 = gu.decode(batch, qd, cd, min_chunk_tokens=16)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

@@ -137,22 +137,35 @@ def host_cache(batch: PagedBatch, rng: np.random.Generator, poison: bool = False
     return cache
 
 
-def device_cache(batch: PagedBatch, seed: int, device, chunk_pages: int = 4096):
+def device_cache(batch: PagedBatch, seed: int, device, chunk_pages: int = 4096,
+                 used_only: bool = False):
     """One layer's cache on ``device`` as a torch bfloat16 tensor.
 
-    The whole pool is filled with N(0, 1) float32 draws from torch's
-    generator seeded with ``seed`` and rounded to bf16 (torch rounds to
-    nearest even).  Used for pools too large to fill with numpy."""
+    The pool is filled with N(0, 1) float32 draws from torch's generator
+    seeded with ``seed`` and rounded to bf16 (torch rounds to nearest even):
+    every page, or with ``used_only`` only the pages the batch uses, in
+    ascending page order (the others hold zeros).  Used for pools too large
+    to fill with numpy."""
     import torch
 
     gen = torch.Generator(device=device)
     gen.manual_seed(int(seed))
-    cache = torch.empty(batch.cache_shape(), dtype=torch.bfloat16, device=device)
+    if used_only:
+        cache = torch.zeros(batch.cache_shape(), dtype=torch.bfloat16, device=device)
+        pages = torch.from_numpy(np.unique(batch.kv_indices).astype(np.int64)).to(device)
+    else:
+        cache = torch.empty(batch.cache_shape(), dtype=torch.bfloat16, device=device)
+        pages = None
     flat = cache.view(batch.num_pages, -1)
-    for p0 in range(0, batch.num_pages, chunk_pages):
-        p1 = min(batch.num_pages, p0 + chunk_pages)
-        flat[p0:p1].copy_(torch.randn((p1 - p0, flat.shape[1]), generator=gen,
-                                      dtype=torch.float32, device=device))
+    total = batch.num_pages if pages is None else int(pages.shape[0])
+    for p0 in range(0, total, chunk_pages):
+        p1 = min(total, p0 + chunk_pages)
+        vals = torch.randn((p1 - p0, flat.shape[1]), generator=gen, dtype=torch.float32,
+                           device=device).to(torch.bfloat16)
+        if pages is None:
+            flat[p0:p1].copy_(vals)
+        else:
+            flat.index_copy_(0, pages[p0:p1], vals)
     return cache
 
 
