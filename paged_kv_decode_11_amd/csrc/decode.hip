@@ -20,8 +20,8 @@
 // v_dot2_f32_bf16 on the packed pairs and are reduced over the 16 lanes of a
 // row with DPP; the online softmax runs in base 2 (v_exp_f32) with the tile
 // maximum taken across rows with permlane swaps; V accumulates in fp32.
-// K of the next tile is requested as soon as the current tile's logits are
-// formed, V of the next tile as soon as the current V is consumed.
+// The next tile's K is requested as soon as the current logits are formed,
+// its V as soon as the current V is consumed.
 //
 // The data path is HBM-bound (aicassindra "Why serving attention is a
 // different problem": decode streams every cached key and value once), so no
@@ -64,25 +64,41 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
-// Combine the 4 rows of a wave: exchange with the row 32 lanes away, then
-// with the neighbouring row.  Each swap returns both halves, so lane L sees
-// its own value and the one at L ^ 32 (then L ^ 16).
+// Exchange with the lane 32 (permlane32) or 16 (permlane16) positions away:
+// each swap instruction returns both registers, so with v in both, lane L
+// ends up holding v[L] in one and v[L ^ 32] (or v[L ^ 16]) in the other.  The
+// pair is read through a 64-bit cast: element access on the builtin's vector
+// result loses the second element with this compiler.
+__device__ __forceinline__ void xswap32(float v, float& a, float& b) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
+                                                  __builtin_bit_cast(uint32_t, v), false, false);
+  const uint64_t u = __builtin_bit_cast(uint64_t, s);
+  a = __uint_as_float(uint32_t(u));
+  b = __uint_as_float(uint32_t(u >> 32));
+}
+
+__device__ __forceinline__ void xswap16(float v, float& a, float& b) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
+                                                  __builtin_bit_cast(uint32_t, v), false, false);
+  const uint64_t u = __builtin_bit_cast(uint64_t, s);
+  a = __uint_as_float(uint32_t(u));
+  b = __uint_as_float(uint32_t(u >> 32));
+}
+
+// Combine the 4 rows of 16 lanes: every lane gets the max (sum) of its
+// column over the rows.
 __device__ __forceinline__ float rows_max(float v) {
-  auto a = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
-                                            __builtin_bit_cast(uint32_t, v), false, false);
-  v = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
-  auto b = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
-                                            __builtin_bit_cast(uint32_t, v), false, false);
-  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
+  float a, b;
+  xswap32(v, a, b);
+  xswap16(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
 }
 
 __device__ __forceinline__ float rows_sum(float v) {
-  auto a = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
-                                            __builtin_bit_cast(uint32_t, v), false, false);
-  v = __builtin_bit_cast(float, a[0]) + __builtin_bit_cast(float, a[1]);
-  auto b = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
-                                            __builtin_bit_cast(uint32_t, v), false, false);
-  return __builtin_bit_cast(float, b[0]) + __builtin_bit_cast(float, b[1]);
+  float a, b;
+  xswap32(v, a, b);
+  xswap16(a + b, a, b);
+  return a + b;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -95,249 +111,340 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Page ids of one 16-token tile.  Page sizes that are multiples of 16 keep a
-// tile inside one page (one id for the wave); smaller ones spread a tile over
-// 16/P pages, so each lane looks up the page of each of its 4 rows.
-template <int P, bool kWholeTile = (P % 16 == 0)>
+struct Ctx {
+  const uint16_t* __restrict__ q;
+  const char* __restrict__ kv;  // cache base, bytes
+  uint16_t* __restrict__ o;
+  float* __restrict__ lse;
+  float* __restrict__ o_part;
+  float* __restrict__ lse_part;
+  int64_t num_pages;
+  float scale_log2;
+  int Hq;
+  int Hkv;
+  uint32_t row_bytes;   // one token's K (or V) rows of all KV heads
+  uint64_t v_bytes;     // K half of a page; V starts this far in
+  uint64_t page_bytes;
+};
+
+// Running attention state of one (item, KV head) for the G query rows.
+template <int G>
+struct State {
+  uint4 q[G];       // packed bf16, elements 8c..8c+7 of each query row
+  float m[G];       // running max of the base-2 logits
+  float l[G];       // running sum of exp2(logit - m), this lane's token rows only
+  float acc[G][8];  // running sum of exp2(logit - m) * v, this lane's token rows only
+};
+
+// Where the 4 rows of one tile are.  Page sizes that are multiples of 16 keep
+// a tile inside one page: one wave-uniform base address plus a 32-bit lane
+// offset per row.  Smaller page sizes spread a tile over 16 / P pages: each
+// lane carries the full address of each of its rows.
+template <int P, bool kWhole = (P % 16 == 0)>
+struct TileRef;
+
+template <int P>
+struct TileRef<P, true> {
+  const char* kbase;  // K rows of the tile (wave-uniform)
+  const char* vbase;  // V rows of the tile (wave-uniform)
+  uint32_t off[4];    // this lane's byte offset of row i from either base
+  __device__ __forceinline__ const uint4* k(int i) const {
+    return reinterpret_cast<const uint4*>(kbase + off[i]);
+  }
+  __device__ __forceinline__ const uint4* v(int i) const {
+    return reinterpret_cast<const uint4*>(vbase + off[i]);
+  }
+};
+
+template <int P>
+struct TileRef<P, false> {
+  const char* row[4];
+  uint64_t v_bytes;
+  __device__ __forceinline__ const uint4* k(int i) const {
+    return reinterpret_cast<const uint4*>(row[i]);
+  }
+  __device__ __forceinline__ const uint4* v(int i) const {
+    return reinterpret_cast<const uint4*>(row[i] + v_bytes);
+  }
+};
+
+// Page ids the next tiles need, read ahead of their use.  For whole-tile
+// pages one wave-uniform id; otherwise one per row of this lane.
+template <int P, bool kWhole = (P % 16 == 0)>
 struct TileIds;
 
 template <int P>
 struct TileIds<P, true> {
-  int64_t page;
+  int32_t id;
 };
 
 template <int P>
 struct TileIds<P, false> {
-  int32_t page[4];
+  int32_t id[4];
 };
 
-struct Chunk {
-  const int32_t* idx;  // kv_indices of the chunk (first page)
-  int len;             // tokens in the chunk
-  int ntiles;
-};
+// Rows past the end of a chunk re-read its last token: their logits are
+// masked, so the values never matter, and no slot past last_page_len (or past
+// the request's pages) is read.
+__device__ __forceinline__ int clamp_row(int i, int R, int valid) { return min(4 * i + R, valid - 1); }
 
-__device__ __forceinline__ int tile_row(const Chunk& ch, int n, int i, int R) {
-  // Rows past the end of the chunk re-read its last token; their logits are
-  // masked, so the values never matter, and no slot past last_page_len (or
-  // past the request's pages) is touched.
-  const int valid = min(16, ch.len - 16 * n);
-  return min(4 * i + R, valid - 1);
+template <int P>
+__device__ __forceinline__ TileIds<P> read_ids(const int32_t* idx, int len, int t, int R) {
+  TileIds<P> ids;
+  const int valid = min(16, len - 16 * t);
+  if constexpr (P % 16 == 0) {
+    ids.id = idx[(16 * t) / P];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ids.id[i] = idx[(16 * t + clamp_row(i, R, valid)) / P];
+  }
+  return ids;
 }
 
-__device__ __forceinline__ int64_t checked_page(int32_t pg, int64_t num_pages, int32_t* err,
-                                                int lane) {
-  if (pg < 0 || pg >= num_pages) {
-    if (lane == 0) err[0] = PKD_DEVERR_PAGE_ID;
-    return 0;
-  }
-  return pg;
+// A page id outside [0, num_pages) is replaced by page 0 and remembered.
+__device__ __forceinline__ int64_t safe_page(int32_t id, int64_t num_pages, int& bad) {
+  const bool ok = id >= 0 && id < num_pages;
+  bad |= ok ? 0 : 1;
+  return ok ? id : 0;
 }
 
 template <int P>
-__device__ __forceinline__ TileIds<P> tile_ids(const Chunk& ch, int n, int R, int lane,
-                                               const DecodeParams& p) {
-  TileIds<P> t;
+__device__ __forceinline__ TileRef<P> tile_ref(const Ctx& p, const TileIds<P>& ids, int len, int t,
+                                               int R, uint32_t col, int& bad) {
+  TileRef<P> ref;
+  const int valid = min(16, len - 16 * t);
   if constexpr (P % 16 == 0) {
-    t.page = checked_page(ch.idx[(16 * n) / P], p.num_pages, p.err, lane);
+    const int64_t pg = safe_page(ids.id, p.num_pages, bad);
+    ref.kbase = p.kv + pg * p.page_bytes + uint64_t((16 * t) % P) * p.row_bytes;
+    ref.vbase = ref.kbase + p.v_bytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ref.off[i] = uint32_t(clamp_row(i, R, valid)) * p.row_bytes + col;
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tok = 16 * n + tile_row(ch, n, i, R);
-      int32_t pg = ch.idx[tok / P];
-      if (pg < 0 || pg >= p.num_pages) {
-        p.err[0] = PKD_DEVERR_PAGE_ID;
-        pg = 0;
-      }
-      t.page[i] = pg;
+      const int64_t pg = safe_page(ids.id[i], p.num_pages, bad);
+      const int slot = clamp_row(i, R, valid) % P;
+      ref.row[i] = p.kv + pg * p.page_bytes + uint64_t(slot) * p.row_bytes + col;
+    }
+    ref.v_bytes = p.v_bytes;
+  }
+  return ref;
+}
+
+template <int P>
+__device__ __forceinline__ void load_k(uint4 (&dst)[4], const TileRef<P>& ref) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i] = *ref.k(i);
+}
+
+template <int P>
+__device__ __forceinline__ void load_v(uint4 (&dst)[4], const TileRef<P>& ref) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i] = *ref.v(i);
+}
+
+// K and V rows of one 16-token tile held by this lane.
+struct TileRegs {
+  uint4 k[4];
+  uint4 v[4];
+};
+
+// One 16-token tile: logits from t.k, online-softmax update, V from t.v.
+// With kNext, the next tile's K is requested into t.k as soon as the logits
+// are formed and its V into t.v as soon as this tile's V is consumed, so
+// loads stream while the rest of the tile is computed; the last tile masks
+// rows >= valid.
+template <int G, int P, bool kNext>
+__device__ __forceinline__ void tile_step(State<G>& st, TileRegs& t, const TileRef<P>& next,
+                                          int valid, int R, float scale_log2, uint64_t v_bytes) {
+  const TileRegs& cur = t;
+  float s[4][G];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      float a = dot2_bf16(st.q[r].x, cur.k[i].x, 0.f);
+      a = dot2_bf16(st.q[r].y, cur.k[i].y, a);
+      a = dot2_bf16(st.q[r].z, cur.k[i].z, a);
+      a = dot2_bf16(st.q[r].w, cur.k[i].w, a);
+      s[i][r] = row_sum16(a) * scale_log2;
     }
   }
-  return t;
-}
-
-// Element offset of row i of tile n (K half; V is v_off further).
-template <int P>
-__device__ __forceinline__ int64_t row_offset(const TileIds<P>& t, const Chunk& ch, int n, int i,
-                                              int R, int64_t page_stride, int64_t row_stride) {
-  const int row = tile_row(ch, n, i, R);
-  if constexpr (P % 16 == 0) {
-    return t.page * page_stride + int64_t((16 * n) % P + row) * row_stride;
+  // The scheduling barriers keep each prefetch where it is written: left
+  // alone, the scheduler sinks the loads to the end of the iteration to
+  // shorten register live ranges, and the next tile is then waited on as
+  // soon as it is requested.
+  if constexpr (kNext) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_k<P>(t.k, next);
+    __builtin_amdgcn_sched_barrier(0);
   } else {
-    return int64_t(t.page[i]) * page_stride + int64_t(row % P) * row_stride;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * i + R >= valid) {
+#pragma unroll
+        for (int r = 0; r < G; ++r) s[i][r] = kNegInf;
+      }
+  }
+
+  float mt[G];
+  bool grow = false;
+#pragma unroll
+  for (int r = 0; r < G; ++r) {
+    mt[r] = rows_max(fmaxf(fmaxf(s[0][r], s[1][r]), fmaxf(s[2][r], s[3][r])));
+    grow |= mt[r] > st.m[r];
+  }
+  // m and mt hold the same value in every lane, so the branch is uniform
+  if (__builtin_amdgcn_readfirstlane(int(grow))) {
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      const float mn = fmaxf(st.m[r], mt[r]);
+      const float scale = __builtin_amdgcn_exp2f(st.m[r] - mn);
+      st.m[r] = mn;
+      st.l[r] *= scale;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st.acc[r][e] *= scale;
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float vf[8];
+    vf[0] = bf16_lo(cur.v[i].x);
+    vf[1] = bf16_hi(cur.v[i].x);
+    vf[2] = bf16_lo(cur.v[i].y);
+    vf[3] = bf16_hi(cur.v[i].y);
+    vf[4] = bf16_lo(cur.v[i].z);
+    vf[5] = bf16_hi(cur.v[i].z);
+    vf[6] = bf16_lo(cur.v[i].w);
+    vf[7] = bf16_hi(cur.v[i].w);
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      const float pr = __builtin_amdgcn_exp2f(s[i][r] - st.m[r]);
+      st.l[r] += pr;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st.acc[r][e] = fmaf(pr, vf[e], st.acc[r][e]);
+    }
+  }
+  if constexpr (kNext) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_v<P>(t.v, next);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
+// Pointers are separate __restrict__ arguments so the compiler knows the
+// plan and kv_indices are not written by this kernel and reads them through
+// the scalar cache.
 template <int G, int P>
-__global__ __launch_bounds__(512) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2, 8)))
+void decode_kernel(
+    const uint16_t* __restrict__ q_ptr, const uint16_t* __restrict__ kv_ptr,
+    uint16_t* __restrict__ o_ptr, float* __restrict__ lse_ptr, const int32_t* __restrict__ ws,
+    float* __restrict__ fws, int32_t* __restrict__ err, int64_t num_pages, float scale_log2,
+    int num_qo_heads, int num_kv_heads) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform by construction; saying so keeps the item and page reads
+  // in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
   const int R = lane >> 4;
   const int c = lane & 15;
-  const int Hq = p.num_qo_heads;
-  const int Hkv = p.num_kv_heads;
 
-  const int32_t* hdr = p.ws + PKD_HEADER_BASE;
-  const int32_t* slot_indptr = p.ws + hdr[PKD_H_OFF_SLOTS];
-  const int32_t* items = p.ws + hdr[PKD_H_OFF_ITEMS];
-  const int32_t* kv_idx = p.ws + hdr[PKD_H_OFF_INDICES];
+  const int32_t* hdr = ws + PKD_HEADER_BASE;
+  const int32_t* slot_indptr = ws + hdr[PKD_H_OFF_SLOTS];
+  const int32_t* items = ws + hdr[PKD_H_OFF_ITEMS];
+  const int32_t* kv_idx = ws + hdr[PKD_H_OFF_INDICES];
   const int64_t n_partials = hdr[PKD_H_PARTIALS];
-  float* o_part = p.fws;
-  float* lse_part = p.fws + n_partials * Hq * kHeadDim;
 
-  const int64_t row_stride = int64_t(Hkv) * kHeadDim;
-  const int64_t v_off = int64_t(P) * row_stride;
-  const int64_t page_stride = 2 * v_off;
+  Ctx p;
+  p.q = q_ptr;
+  p.kv = reinterpret_cast<const char*>(kv_ptr);
+  p.o = o_ptr;
+  p.lse = lse_ptr;
+  p.o_part = fws;
+  p.lse_part = fws + n_partials * num_qo_heads * kHeadDim;
+  p.num_pages = num_pages;
+  p.scale_log2 = scale_log2;
+  p.Hq = num_qo_heads;
+  p.Hkv = num_kv_heads;
+  p.row_bytes = uint32_t(num_kv_heads) * kHeadDim * 2;
+  p.v_bytes = uint64_t(P) * p.row_bytes;
+  p.page_bytes = 2 * p.v_bytes;
 
   const int it_end = slot_indptr[blockIdx.x + 1];
   for (int it = slot_indptr[blockIdx.x]; it < it_end; ++it) {
     const int32_t* item = items + 8 * it;
     const int req = item[0];
     const int out = item[4];
-    Chunk ch;
-    ch.idx = kv_idx + item[1];
-    ch.len = item[5];
-    ch.ntiles = (ch.len + 15) >> 4;
+    const int len = item[5];
+    const int32_t* idx = kv_idx + item[1];
+    const int ntiles = (len + 15) >> 4;
 
-    for (int kh = wave; kh < Hkv; kh += nwaves) {
-      const uint16_t* head = p.kv + int64_t(kh) * kHeadDim + c * 8;
-
-      uint4 qv[G];
-      const uint16_t* qrow = p.q + (int64_t(req) * Hq + kh * G) * kHeadDim + c * 8;
-#pragma unroll
-      for (int r = 0; r < G; ++r) qv[r] = *reinterpret_cast<const uint4*>(qrow + r * kHeadDim);
-
-      float m[G], l[G], acc[G][8];
+    for (int kh = wave; kh < p.Hkv; kh += nwaves) {
+      const uint32_t col = uint32_t(kh * kHeadDim + c * 8) * 2;
+      State<G> st;
+      const uint16_t* qrow = p.q + (int64_t(req) * p.Hq + kh * G) * kHeadDim + c * 8;
 #pragma unroll
       for (int r = 0; r < G; ++r) {
-        m[r] = kNegInf;
-        l[r] = 0.f;
+        st.q[r] = *reinterpret_cast<const uint4*>(qrow + r * kHeadDim);
+        st.m[r] = kNegInf;
+        st.l[r] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
+        for (int e = 0; e < 8; ++e) st.acc[r][e] = 0.f;
       }
 
-      uint4 kr[4], vr[4];
+      int bad = 0;
+      TileRegs t;
       {
-        const TileIds<P> t0 = tile_ids<P>(ch, 0, R, lane, p);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t off = row_offset<P>(t0, ch, 0, i, R, page_stride, row_stride);
-          kr[i] = *reinterpret_cast<const uint4*>(head + off);
-          vr[i] = *reinterpret_cast<const uint4*>(head + off + v_off);
-        }
+        const TileRef<P> t0 = tile_ref<P>(p, read_ids<P>(idx, len, 0, R), len, 0, R, col, bad);
+        load_k<P>(t.k, t0);
+        load_v<P>(t.v, t0);
       }
-      TileIds<P> next = tile_ids<P>(ch, min(1, ch.ntiles - 1), R, lane, p);
-
-      for (int n = 0; n < ch.ntiles; ++n) {
-        const bool more = n + 1 < ch.ntiles;
-        const TileIds<P> after = tile_ids<P>(ch, min(n + 2, ch.ntiles - 1), R, lane, p);
-
-        // logits of the 4 rows of this lane's token row, scaled to base 2
-        float s[4][G];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-          for (int r = 0; r < G; ++r) {
-            float a = dot2_bf16(qv[r].x, kr[i].x, 0.f);
-            a = dot2_bf16(qv[r].y, kr[i].y, a);
-            a = dot2_bf16(qv[r].z, kr[i].z, a);
-            a = dot2_bf16(qv[r].w, kr[i].w, a);
-            s[i][r] = row_sum16(a) * p.scale_log2;
-          }
-        }
-        if (n == ch.ntiles - 1) {
-          const int valid = ch.len - 16 * n;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (4 * i + R >= valid) {
-#pragma unroll
-              for (int r = 0; r < G; ++r) s[i][r] = kNegInf;
-            }
-        }
-        if (more) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            kr[i] = *reinterpret_cast<const uint4*>(
-                head + row_offset<P>(next, ch, n + 1, i, R, page_stride, row_stride));
-        }
-
-        // online softmax: rescale the running state when the maximum grows
-        float mt[G];
-        bool grow = false;
-#pragma unroll
-        for (int r = 0; r < G; ++r) {
-          mt[r] = rows_max(fmaxf(fmaxf(s[0][r], s[1][r]), fmaxf(s[2][r], s[3][r])));
-          grow |= mt[r] > m[r];
-        }
-        if (grow) {
-#pragma unroll
-          for (int r = 0; r < G; ++r) {
-            const float mn = fmaxf(m[r], mt[r]);
-            const float scale = __builtin_amdgcn_exp2f(m[r] - mn);
-            m[r] = mn;
-            l[r] *= scale;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[r][e] *= scale;
-          }
-        }
-
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float vf[8];
-          vf[0] = bf16_lo(vr[i].x);
-          vf[1] = bf16_hi(vr[i].x);
-          vf[2] = bf16_lo(vr[i].y);
-          vf[3] = bf16_hi(vr[i].y);
-          vf[4] = bf16_lo(vr[i].z);
-          vf[5] = bf16_hi(vr[i].z);
-          vf[6] = bf16_lo(vr[i].w);
-          vf[7] = bf16_hi(vr[i].w);
-#pragma unroll
-          for (int r = 0; r < G; ++r) {
-            const float pr = __builtin_amdgcn_exp2f(s[i][r] - m[r]);
-            l[r] += pr;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(pr, vf[e], acc[r][e]);
-          }
-        }
-        if (more) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            vr[i] = *reinterpret_cast<const uint4*>(
-                head + row_offset<P>(next, ch, n + 1, i, R, page_stride, row_stride) + v_off);
-        }
-        next = after;
+      // page ids run one tile ahead of the loads that use them
+      TileIds<P> ids_next = read_ids<P>(idx, len, ntiles > 1 ? 1 : 0, R);
+      for (int n = 0; n + 1 < ntiles; ++n) {
+        const TileRef<P> ref = tile_ref<P>(p, ids_next, len, n + 1, R, col, bad);
+        ids_next = read_ids<P>(idx, len, min(n + 2, ntiles - 1), R);
+        tile_step<G, P, true>(st, t, ref, 16, R, p.scale_log2, p.v_bytes);
       }
+      {
+        const TileRef<P> none = {};
+        tile_step<G, P, false>(st, t, none, len - 16 * (ntiles - 1), R, p.scale_log2, p.v_bytes);
+      }
+      if (bad && lane == 0) err[0] = PKD_DEVERR_PAGE_ID;
 
       // totals over the 4 token rows; every lane then holds the full state
 #pragma unroll
       for (int r = 0; r < G; ++r) {
-        l[r] = rows_sum(l[r]);
+        st.l[r] = rows_sum(st.l[r]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[r][e] = rows_sum(acc[r][e]);
+        for (int e = 0; e < 8; ++e) st.acc[r][e] = rows_sum(st.acc[r][e]);
       }
 
 #pragma unroll
       for (int r = 0; r < G; ++r) {
         if ((r & 3) != R) continue;
-        const float inv = 1.f / l[r];
-        const float lse_nat = (m[r] + __log2f(l[r])) * kLn2;
+        const float inv = 1.f / st.l[r];
+        const float lse_nat = (st.m[r] + __log2f(st.l[r])) * kLn2;
         const int64_t qh = kh * G + r;
         if (out < 0) {
           uint4 w;
-          w.x = pack_bf16x2(acc[r][0] * inv, acc[r][1] * inv);
-          w.y = pack_bf16x2(acc[r][2] * inv, acc[r][3] * inv);
-          w.z = pack_bf16x2(acc[r][4] * inv, acc[r][5] * inv);
-          w.w = pack_bf16x2(acc[r][6] * inv, acc[r][7] * inv);
-          *reinterpret_cast<uint4*>(p.o + (int64_t(req) * Hq + qh) * kHeadDim + c * 8) = w;
-          if (p.lse && c == 0) p.lse[int64_t(req) * Hq + qh] = lse_nat;
+          w.x = pack_bf16x2(st.acc[r][0] * inv, st.acc[r][1] * inv);
+          w.y = pack_bf16x2(st.acc[r][2] * inv, st.acc[r][3] * inv);
+          w.z = pack_bf16x2(st.acc[r][4] * inv, st.acc[r][5] * inv);
+          w.w = pack_bf16x2(st.acc[r][6] * inv, st.acc[r][7] * inv);
+          *reinterpret_cast<uint4*>(p.o + (int64_t(req) * p.Hq + qh) * kHeadDim + c * 8) = w;
+          if (p.lse && c == 0) p.lse[int64_t(req) * p.Hq + qh] = lse_nat;
         } else {
-          float* dst = o_part + (int64_t(out) * Hq + qh) * kHeadDim + c * 8;
+          float* dst = p.o_part + (int64_t(out) * p.Hq + qh) * kHeadDim + c * 8;
           *reinterpret_cast<float4*>(dst) =
-              make_float4(acc[r][0] * inv, acc[r][1] * inv, acc[r][2] * inv, acc[r][3] * inv);
+              make_float4(st.acc[r][0] * inv, st.acc[r][1] * inv, st.acc[r][2] * inv,
+                          st.acc[r][3] * inv);
           *reinterpret_cast<float4*>(dst + 4) =
-              make_float4(acc[r][4] * inv, acc[r][5] * inv, acc[r][6] * inv, acc[r][7] * inv);
-          if (c == 0) lse_part[int64_t(out) * Hq + qh] = lse_nat;
+              make_float4(st.acc[r][4] * inv, st.acc[r][5] * inv, st.acc[r][6] * inv,
+                          st.acc[r][7] * inv);
+          if (c == 0) p.lse_part[int64_t(out) * p.Hq + qh] = lse_nat;
         }
       }
     }
@@ -347,7 +454,9 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeParams p) {
 template <int G, int P>
 hipError_t launch_one(const DecodeParams& p, int num_slots, hipStream_t stream) {
   const int waves = p.num_kv_heads < kMaxWavesPerBlock ? p.num_kv_heads : kMaxWavesPerBlock;
-  hipLaunchKernelGGL((decode_kernel<G, P>), dim3(num_slots), dim3(64 * waves), 0, stream, p);
+  hipLaunchKernelGGL((decode_kernel<G, P>), dim3(num_slots), dim3(64 * waves), 0, stream, p.q,
+                     p.kv, p.o, p.lse, p.ws, p.fws, p.err, p.num_pages, p.scale_log2,
+                     p.num_qo_heads, p.num_kv_heads);
   return hipGetLastError();
 }
 

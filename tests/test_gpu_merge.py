@@ -39,9 +39,8 @@ def test_merge_state_matches_oracle():
                                  lb.astype(np.float64))
     got_l = lse.cpu().numpy().astype(np.float64)
     assert got_l[1, 0] == -math.inf and np.all(gu.dev_to_f64(o)[1, 0] == 0)
-    fin = np.isfinite(ref_l)
-    assert np.max(np.abs(got_l[fin] - ref_l[fin])) <= gu.TOL_LSE
-    assert np.max(np.abs(gu.dev_to_f64(o) - ref_o)) <= gu.TOL_O
+    gu.check_lse(got_l, ref_l, "merge_state")
+    gu.check_o(gu.dev_to_f64(o), ref_o, "merge_state")
 
 
 def test_merge_state_in_place():
@@ -56,8 +55,8 @@ def test_merge_state_in_place():
     torch.cuda.synchronize()
     ref_o, ref_l = mg.merge_rows(att.bf16_to_f64(oa), la.astype(np.float64), att.bf16_to_f64(ob),
                                  lb.astype(np.float64))
-    assert np.max(np.abs(gu.dev_to_f64(da) - ref_o)) <= gu.TOL_O
-    assert np.max(np.abs(dla.cpu().numpy() - ref_l)) <= gu.TOL_LSE
+    gu.check_o(gu.dev_to_f64(da), ref_o, "in-place")
+    gu.check_lse(dla.cpu().numpy().astype(np.float64), ref_l, "in-place")
 
 
 @pytest.mark.parametrize("k", [1, 2, 7, 64, 300])
@@ -81,8 +80,8 @@ def test_merge_states_matches_oracle(k):
         for h in range(H):
             ref_o[i, h], ref_l[i, h] = mg.merge_many(
                 [(of[i, c, h], float(lse[i, c, h])) for c in range(k)])
-    assert np.max(np.abs(gu.dev_to_f64(out) - ref_o)) <= gu.TOL_O
-    assert np.max(np.abs(lse_out.cpu().numpy() - ref_l)) <= gu.TOL_LSE
+    gu.check_o(gu.dev_to_f64(out), ref_o, f"merge_states k={k}")
+    gu.check_lse(lse_out.cpu().numpy().astype(np.float64), ref_l, f"merge_states k={k}")
 
 
 def test_split_partials_merge_like_unsplit():
@@ -95,8 +94,9 @@ def test_split_partials_merge_like_unsplit():
     qd, cd = gu.bits_to_dev(q), gu.bits_to_dev(cache)
     o1, l1 = gu.decode(batch, qd, cd, min_chunk_tokens=100000)  # no split
     o2, l2 = gu.decode(batch, qd, cd, fixed_chunk_pages=3)      # 84 + 53 chunks
-    assert np.max(np.abs(gu.dev_to_f64(o1) - gu.dev_to_f64(o2))) <= gu.TOL_O
-    assert np.max(np.abs(l1.cpu().numpy() - l2.cpu().numpy())) <= gu.TOL_LSE
+    gu.check_o(gu.dev_to_f64(o2), gu.dev_to_f64(o1), "split-vs-unsplit")
+    gu.check_lse(l2.cpu().numpy().astype(np.float64), l1.cpu().numpy().astype(np.float64),
+                 "split-vs-unsplit")
 
 
 def test_composable_shared_prefix_small():
