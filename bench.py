@@ -48,6 +48,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="oracle time budget for cpu_baseline (0 disables)")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--variant", default="auto", choices=["auto", "dot2", "mfma"],
+                    help="decode kernel (auto = the matrix-core kernel)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of this many MiB (5 times), "
+                         "to calibrate HBM byte counters against a known size")
     return ap.parse_args()
 
 
@@ -120,8 +125,29 @@ def cpu_baseline(batch, q_bits, cache_dev, o_dev, lse_dev, budget_s: float):
     }, {"max_abs_err_o": err_o, "max_abs_err_lse": err_l, "requests_checked": len(done)}
 
 
+def calibrate_copy(mib: int) -> None:
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give
+    the scale between counter units and bytes moved."""
+    import torch
+
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 5
+    print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n,
+                      "copies": 5, "gbs_read_plus_write": round(2 * n / dt / 1e9, 1)}), flush=True)
+
+
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU sharding is a design "
                                    "note only (see the design document)", "n_gpus": args.gpus}))
@@ -175,7 +201,7 @@ def main():
 
     def plan():
         r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, batch.num_qo_heads,
-               batch.num_kv_heads, batch.head_dim, batch.page_size)
+               batch.num_kv_heads, batch.head_dim, batch.page_size, variant=args.variant)
 
     def step():
         plan()
@@ -270,6 +296,7 @@ def main():
             "head_dim": batch.head_dim, "page_size": batch.page_size,
             "kv_tokens_per_layer": batch.total_tokens, "pages_per_layer": batch.nnz,
             "pool_pages": batch.num_pages, "slots": r.num_slots,
+            "decode_kernel": "mfma" if args.variant in ("auto", "mfma") else "dot2",
             "parallelism": "single GPU",
         },
         "us_per_layer_step": round(ms_per_step * 1e3 / n_layers, 2),
@@ -279,7 +306,8 @@ def main():
             "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": "decode_kernel", "avg_launch_us": round(decode_us, 2),
+            "kernel": "decode_mfma_kernel" if args.variant in ("auto", "mfma") else "decode_kernel",
+            "avg_launch_us": round(decode_us, 2),
             "algorithmic_bytes_per_launch": layer_bytes,
             "merge_avg_launch_us": round(merge_us, 2),
         },

@@ -78,7 +78,16 @@ typedef struct pkd_plan_opts {
   int32_t min_chunk_tokens;  /* smallest derived chunk, in tokens; <= 0: 128 */
   int32_t alpha;             /* cost = alpha * l_q + beta * chunk_len, l_q = 1; */
   int32_t beta;              /*   alpha < 0 or beta <= 0: 1 */
+  int32_t variant;           /* decode kernel for runs of this plan: PKD_VARIANT_* */
 } pkd_plan_opts;
+
+/* Decode kernels.  Both compute the same result (to rounding); they differ
+ * in where q.k is evaluated. */
+enum {
+  PKD_VARIANT_AUTO = 0, /* the matrix-core kernel */
+  PKD_VARIANT_DOT2 = 1, /* q.k with packed bf16 dot products on the vector ALUs */
+  PKD_VARIANT_MFMA = 2  /* q.k as a 16 x 16 tile on the matrix cores (GQA group as rows) */
+};
 
 /* ---------------------------------------------------------------------
  * Plan image.  The int workspace (and the output of pkd_plan_host) is an

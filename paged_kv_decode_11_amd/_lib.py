@@ -24,6 +24,10 @@ PKD_DTYPE_FP8_E4M3 = 3
 PKD_LAYOUT_NHD = 0
 PKD_LAYOUT_HND = 1
 PKD_DEVERR_PAGE_ID = 1
+PKD_VARIANT_AUTO = 0
+PKD_VARIANT_DOT2 = 1
+PKD_VARIANT_MFMA = 2
+VARIANTS = {"auto": PKD_VARIANT_AUTO, "dot2": PKD_VARIANT_DOT2, "mfma": PKD_VARIANT_MFMA}
 
 HEADER_BASE = 32
 H_FIELDS = ["MAGIC", "VERSION", "BATCH", "QO_HEADS", "KV_HEADS", "HEAD_DIM", "PAGE_SIZE",
@@ -45,7 +49,7 @@ class PkdError(RuntimeError):
 
 class pkd_plan_opts(ctypes.Structure):
     _fields_ = [("fixed_chunk_pages", ctypes.c_int32), ("min_chunk_tokens", ctypes.c_int32),
-                ("alpha", ctypes.c_int32), ("beta", ctypes.c_int32)]
+                ("alpha", ctypes.c_int32), ("beta", ctypes.c_int32), ("variant", ctypes.c_int32)]
 
 
 _i32, _i64, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p

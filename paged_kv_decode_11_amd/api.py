@@ -30,8 +30,9 @@ def _dtype_code(dtype) -> int:
     return _DTYPES[dtype]
 
 
-def _opts(fixed_chunk_pages=0, min_chunk_tokens=0, alpha=-1, beta=0):
-    return pkd_plan_opts(int(fixed_chunk_pages), int(min_chunk_tokens), int(alpha), int(beta))
+def _opts(fixed_chunk_pages=0, min_chunk_tokens=0, alpha=-1, beta=0, variant="auto"):
+    v = _lib.VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    return pkd_plan_opts(int(fixed_chunk_pages), int(min_chunk_tokens), int(alpha), int(beta), v)
 
 
 def _host_i32(x) -> np.ndarray:

@@ -33,6 +33,7 @@ struct pkd_handle {
   // current plan
   bool planned = false;
   int32_t batch = 0, Hq = 0, Hkv = 0, D = 0, P = 0, q_dtype = 0, kv_dtype = 0;
+  int32_t variant = PKD_VARIANT_MFMA;
   pkd::PlanLayout layout;
   void* int_ws = nullptr;
   size_t int_bytes = 0;
@@ -237,6 +238,10 @@ int pkd_plan(pkd_handle* h, const int32_t* kv_indptr, const int32_t* kv_indices,
       (reinterpret_cast<uintptr_t>(host_workspace) & 255))
     return fail(PKD_ERR_INVALID_ARG, "workspaces must be 256-byte aligned");
 
+  const int32_t variant = opts ? opts->variant : PKD_VARIANT_AUTO;
+  if (variant != PKD_VARIANT_AUTO && variant != PKD_VARIANT_DOT2 && variant != PKD_VARIANT_MFMA)
+    return fail(PKD_ERR_INVALID_ARG, "unknown decode kernel variant");
+
   DeviceGuard guard(h->device);
   if (!guard.ok) return hip_fail(guard.err, "hipSetDevice");
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -300,6 +305,7 @@ int pkd_plan(pkd_handle* h, const int32_t* kv_indptr, const int32_t* kv_indices,
   h->P = page_size;
   h->q_dtype = q_dtype;
   h->kv_dtype = kv_dtype;
+  h->variant = variant == PKD_VARIANT_DOT2 ? PKD_VARIANT_DOT2 : PKD_VARIANT_MFMA;
   h->layout = layout;
   h->int_ws = int_workspace;
   h->int_bytes = int_workspace_bytes;
@@ -364,7 +370,9 @@ int pkd_run(pkd_handle* h, const void* q, int32_t batch, const void* kv_cache, i
       if (h->prof_used + 3 > h->prof_events.size()) {
         for (int i = 0; i < 3; ++i) {
           hipEvent_t x;
-          hipError_t e = hipEventCreate(&x);
+          // device-scope release only: a system-scope fence per record
+          // would stretch the gaps between the timed kernels
+          hipError_t e = hipEventCreateWithFlags(&x, hipEventDisableSystemFence);
           if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
           h->prof_events.push_back(x);
         }
@@ -377,7 +385,9 @@ int pkd_run(pkd_handle* h, const void* q, int32_t batch, const void* kv_cache, i
 
   hipError_t e;
   if (prof && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  e = pkd::launch_decode(dp, h->Hq / h->Hkv, h->P, h->num_slots, s);
+  e = h->variant == PKD_VARIANT_DOT2
+          ? pkd::launch_decode(dp, h->Hq / h->Hkv, h->P, h->num_slots, s)
+          : pkd::launch_decode_mfma(dp, h->Hq / h->Hkv, h->P, h->num_slots, s);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
   if (prof && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   e = pkd::launch_merge_partials(mp, h->merge_grid, s);

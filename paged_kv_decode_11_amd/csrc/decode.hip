@@ -32,83 +32,16 @@
 
 #include <cstdint>
 
+#include "device_common.h"
 #include "kernels.h"
 #include "pkd.h"
 
 namespace pkd {
 namespace {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-constexpr float kNegInf = -__builtin_inff();
-constexpr float kLn2 = 0.69314718055994531f;
-
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over the 16 lanes of a row: swap neighbours, swap pairs, mirror
-// halves, mirror the row.  Every lane of the row ends with the same bits.
-__device__ __forceinline__ float row_sum16(float v) {
-  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp<0x141>(v);  // row_half_mirror
-  v += dpp<0x140>(v);  // row_mirror
-  return v;
-}
-
-// Exchange with the lane 32 (permlane32) or 16 (permlane16) positions away:
-// each swap instruction returns both registers, so with v in both, lane L
-// ends up holding v[L] in one and v[L ^ 32] (or v[L ^ 16]) in the other.  The
-// pair is read through a 64-bit cast: element access on the builtin's vector
-// result loses the second element with this compiler.
-__device__ __forceinline__ void xswap32(float v, float& a, float& b) {
-  const auto s = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
-                                                  __builtin_bit_cast(uint32_t, v), false, false);
-  const uint64_t u = __builtin_bit_cast(uint64_t, s);
-  a = __uint_as_float(uint32_t(u));
-  b = __uint_as_float(uint32_t(u >> 32));
-}
-
-__device__ __forceinline__ void xswap16(float v, float& a, float& b) {
-  const auto s = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
-                                                  __builtin_bit_cast(uint32_t, v), false, false);
-  const uint64_t u = __builtin_bit_cast(uint64_t, s);
-  a = __uint_as_float(uint32_t(u));
-  b = __uint_as_float(uint32_t(u >> 32));
-}
-
-// Combine the 4 rows of 16 lanes: every lane gets the max (sum) of its
-// column over the rows.
-__device__ __forceinline__ float rows_max(float v) {
-  float a, b;
-  xswap32(v, a, b);
-  xswap16(fmaxf(a, b), a, b);
-  return fmaxf(a, b);
-}
-
-__device__ __forceinline__ float rows_sum(float v) {
-  float a, b;
-  xswap32(v, a, b);
-  xswap16(a + b, a, b);
-  return a + b;
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  bf16x2_t v;
-  v.x = (__bf16)lo;
-  v.y = (__bf16)hi;
-  return __builtin_bit_cast(uint32_t, v);
 }
 
 struct Ctx {
@@ -201,13 +134,6 @@ __device__ __forceinline__ TileIds<P> read_ids(const int32_t* idx, int len, int 
   return ids;
 }
 
-// A page id outside [0, num_pages) is replaced by page 0 and remembered.
-__device__ __forceinline__ int64_t safe_page(int32_t id, int64_t num_pages, int& bad) {
-  const bool ok = id >= 0 && id < num_pages;
-  bad |= ok ? 0 : 1;
-  return ok ? id : 0;
-}
-
 template <int P>
 __device__ __forceinline__ TileRef<P> tile_ref(const Ctx& p, const TileIds<P>& ids, int len, int t,
                                                int R, uint32_t col, int& bad) {
@@ -234,13 +160,13 @@ __device__ __forceinline__ TileRef<P> tile_ref(const Ctx& p, const TileIds<P>& i
 template <int P>
 __device__ __forceinline__ void load_k(uint4 (&dst)[4], const TileRef<P>& ref) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dst[i] = *ref.k(i);
+  for (int i = 0; i < 4; ++i) dst[i] = load_stream16(ref.k(i));
 }
 
 template <int P>
 __device__ __forceinline__ void load_v(uint4 (&dst)[4], const TileRef<P>& ref) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dst[i] = *ref.v(i);
+  for (int i = 0; i < 4; ++i) dst[i] = load_stream16(ref.v(i));
 }
 
 // K and V rows of one 16-token tile held by this lane.
@@ -494,7 +420,7 @@ hipError_t launch_decode(const DecodeParams& p, int g, int page_size, int num_sl
   }
 }
 
-int decode_blocks_per_cu(int waves_per_block) {
+int decode_blocks_per_cu_dot2(int waves_per_block) {
   int blocks = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<4, 16>,
                                                    64 * waves_per_block, 0) != hipSuccess)

@@ -1,0 +1,121 @@
+// Device helpers shared by the decode kernels: lane exchanges within a
+// wave64, bf16 unpacking and packing, constants.  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pkd {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kLog2e = 1.44269504088896341f;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// DPP controls used below: swap neighbours (quad_perm [1,0,3,2]), swap pairs
+// (quad_perm [2,3,0,1]), mirror within 8 lanes, mirror within 16 lanes.
+// Applied in that order they pair every lane of a 16-lane row with each of
+// the other 15 exactly once, so a row reduction takes 4 steps and leaves
+// identical bits in all 16 lanes.
+constexpr int kDppSwap1 = 0xB1;
+constexpr int kDppSwap2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<kDppSwap1>(v);
+  v += dpp<kDppSwap2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
+  return v;
+}
+
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp<kDppSwap1>(v));
+  v = fmaxf(v, dpp<kDppSwap2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppMirror>(v));
+  return v;
+}
+
+// Exchange with the lane 32 (permlane32) or 16 (permlane16) positions away:
+// each swap instruction returns both registers, so with v in both, lane L
+// ends up holding v[L] in one and v[L ^ 32] (or v[L ^ 16]) in the other.  The
+// pair is read through a 64-bit cast: element access on the builtin's vector
+// result loses the second element with this compiler.
+__device__ __forceinline__ void xswap32(float v, float& a, float& b) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
+                                                  __builtin_bit_cast(uint32_t, v), false, false);
+  const uint64_t u = __builtin_bit_cast(uint64_t, s);
+  a = __uint_as_float(uint32_t(u));
+  b = __uint_as_float(uint32_t(u >> 32));
+}
+
+__device__ __forceinline__ void xswap16(float v, float& a, float& b) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
+                                                  __builtin_bit_cast(uint32_t, v), false, false);
+  const uint64_t u = __builtin_bit_cast(uint64_t, s);
+  a = __uint_as_float(uint32_t(u));
+  b = __uint_as_float(uint32_t(u >> 32));
+}
+
+// Combine the 4 rows of 16 lanes: every lane gets the max (sum) of its
+// column over the rows.
+__device__ __forceinline__ float rows_max(float v) {
+  float a, b;
+  xswap32(v, a, b);
+  xswap16(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+
+__device__ __forceinline__ float rows_sum(float v) {
+  float a, b;
+  xswap32(v, a, b);
+  xswap16(a + b, a, b);
+  return a + b;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v;
+  v.x = (__bf16)lo;
+  v.y = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Streaming loads of the KV cache carry the nontemporal hint: every byte is
+// read once per layer, and keeping it out of the caches' way measurably
+// raises the read rate of paged gathers on gfx950.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream16(const void* ptr) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(ptr));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t load_stream4(const void* ptr) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(ptr));
+}
+
+// Cache-policy operand of the raw buffer load builtins selecting "nt".
+constexpr int kBufferNontemporal = 2;
+
+// A page id outside [0, num_pages) is replaced by page 0 and remembered.
+__device__ __forceinline__ int64_t safe_page(int32_t id, int64_t num_pages, int& bad) {
+  const bool ok = id >= 0 && id < num_pages;
+  bad |= ok ? 0 : 1;
+  return ok ? id : 0;
+}
+
+}  // namespace pkd

@@ -41,12 +41,18 @@ struct MergeParams {
   float* lse_out;      // fp32 [.., H] or null
 };
 
-// Decode kernel for group size g and page size P (both must be built).
+// Decode kernel for group size g and page size P (both must be built):
+// q.k with packed bf16 dot products on the vector ALUs (decode.hip) ...
 hipError_t launch_decode(const DecodeParams& p, int g, int page_size, int num_slots,
                          hipStream_t stream);
+// ... or with the logit tile on the matrix cores (decode_mfma.hip).
+hipError_t launch_decode_mfma(const DecodeParams& p, int g, int page_size, int num_slots,
+                              hipStream_t stream);
 bool decode_variant_built(int g, int page_size);
-// Occupancy (workgroups per CU) of the decode kernel at g=4, P=16.
+// Occupancy (workgroups per CU) of the matrix-core decode kernel at g=4,
+// P=16 (the default kernel), and of the dot-product kernel.
 int decode_blocks_per_cu(int waves_per_block);
+int decode_blocks_per_cu_dot2(int waves_per_block);
 
 // Merge of the split requests of the current plan (reads the plan image).
 hipError_t launch_merge_partials(const MergeParams& p, int grid, hipStream_t stream);

@@ -11,6 +11,8 @@ from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 
+VARIANTS = ["dot2", "mfma"]
+
 
 def _small(seed, lens, P, Hq, Hkv, poison=True, spare=9):
     rng = np.random.default_rng(seed)
@@ -31,12 +33,13 @@ def _check(batch, q, cache, label, sm_scale=None, return_lse=True, r=None, **opt
     return gu.assert_close(o, lse, o_ref, lse_ref, label=label)
 
 
-def test_tiny_workload_writethrough():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_tiny_workload_writethrough(variant):
     spec, rng, b = workloads.workload("tiny")
     batch = b["main"]
     q = workloads.host_query(batch, rng)
     cache = workloads.host_cache(batch, rng, poison=True)
-    _check(batch, q, cache, "tiny")
+    _check(batch, q, cache, f"tiny-{variant}", variant=variant)
 
 
 def test_tiny_worked_example_pages():
@@ -48,69 +51,92 @@ def test_tiny_worked_example_pages():
     _check(batch, q, cache, "worked-example")
 
 
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("fixed", [1, 2])
-def test_tiny_forced_splits(fixed):
+def test_tiny_forced_splits(fixed, variant):
     spec, rng, b = workloads.workload("tiny")
     batch = b["main"]
     q = workloads.host_query(batch, rng)
     cache = workloads.host_cache(batch, rng, poison=True)
-    _check(batch, q, cache, f"tiny-split{fixed}", fixed_chunk_pages=fixed)
+    _check(batch, q, cache, f"tiny-split{fixed}-{variant}", fixed_chunk_pages=fixed,
+           variant=variant)
 
 
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("P", [1, 2, 4, 8, 16, 32, 64])
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
-def test_page_sizes_and_groups(P, G):
+def test_page_sizes_and_groups(P, G, variant):
     Hkv = 8 if G <= 4 else 4
     lens = sorted(set(workloads.edge_lengths(P) + [3 * P + 5, 77, 300]))
     batch, q, cache = _small(10 * P + G, lens, P, Hkv * G, Hkv)
-    _check(batch, q, cache, f"P{P}-G{G}")
-    _check(batch, q, cache, f"P{P}-G{G}-split", fixed_chunk_pages=1 if P >= 16 else max(1, 48 // P))
+    _check(batch, q, cache, f"P{P}-G{G}-{variant}", variant=variant)
+    _check(batch, q, cache, f"P{P}-G{G}-{variant}-split",
+           fixed_chunk_pages=1 if P >= 16 else max(1, 48 // P), variant=variant)
 
 
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("Hkv", [1, 2, 3, 8, 12, 16])
-def test_kv_head_counts(Hkv):
+def test_kv_head_counts(Hkv, variant):
     """Fewer waves than 8 per workgroup (Hkv < 8) and heads looped over
     waves (Hkv > 8)."""
     batch, q, cache = _small(50 + Hkv, [1, 40, 129, 500], 16, 4 * Hkv, Hkv)
-    _check(batch, q, cache, f"Hkv{Hkv}")
-    _check(batch, q, cache, f"Hkv{Hkv}-split", min_chunk_tokens=16)
+    _check(batch, q, cache, f"Hkv{Hkv}-{variant}", variant=variant)
+    _check(batch, q, cache, f"Hkv{Hkv}-{variant}-split", min_chunk_tokens=16, variant=variant)
 
 
-def test_no_lse_and_custom_scale():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_no_lse_and_custom_scale(variant):
     batch, q, cache = _small(7, [100, 33, 1], 16, 32, 8)
-    _check(batch, q, cache, "no-lse", return_lse=False)
-    _check(batch, q, cache, "scale0.3", sm_scale=0.3)
-    _check(batch, q, cache, "scale0.3-split", sm_scale=0.3, fixed_chunk_pages=2)
+    _check(batch, q, cache, "no-lse", return_lse=False, variant=variant)
+    _check(batch, q, cache, "scale0.3", sm_scale=0.3, variant=variant)
+    _check(batch, q, cache, "scale0.3-split", sm_scale=0.3, fixed_chunk_pages=2, variant=variant)
 
 
-def test_single_token_requests():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_single_token_requests(variant):
     batch, q, cache = _small(8, [1] * 37, 16, 32, 8)
-    _check(batch, q, cache, "ones")
+    _check(batch, q, cache, "ones", variant=variant)
 
 
-def test_random_batches_many_splits():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_random_batches_many_splits(variant):
     rng = np.random.default_rng(99)
     for trial in range(4):
         lens = rng.integers(1, 2000, size=int(rng.integers(1, 40)))
         batch, q, cache = _small(200 + trial, lens.tolist(), 16, 32, 8)
-        _check(batch, q, cache, f"random{trial}")
-        _check(batch, q, cache, f"random{trial}-mct16", min_chunk_tokens=16)
+        _check(batch, q, cache, f"random{trial}-{variant}", variant=variant)
+        _check(batch, q, cache, f"random{trial}-{variant}-mct16", min_chunk_tokens=16,
+               variant=variant)
 
 
-def test_few_slots_long_queues():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_few_slots_long_queues(variant):
     """A handle with 3 slots: each workgroup walks many items."""
     r = gu.runner(max_batch=64, max_nnz=1 << 14, num_slots=3)
     assert r.num_slots == 3
     batch, q, cache = _small(31, [700, 20, 1, 999, 64, 65], 16, 32, 8)
-    _check(batch, q, cache, "3slots", r=r)
-    _check(batch, q, cache, "3slots-split", r=r, fixed_chunk_pages=4)
+    _check(batch, q, cache, "3slots", r=r, variant=variant)
+    _check(batch, q, cache, "3slots-split", r=r, fixed_chunk_pages=4, variant=variant)
 
 
-def test_outputs_are_deterministic():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_outputs_are_deterministic(variant):
     import torch
 
     batch, q, cache = _small(12, [3000, 17, 900], 16, 32, 8)
     qd, cd = gu.bits_to_dev(q), gu.bits_to_dev(cache)
-    o1, l1 = gu.decode(batch, qd, cd, min_chunk_tokens=16)
-    o2, l2 = gu.decode(batch, qd, cd, min_chunk_tokens=16)
+    o1, l1 = gu.decode(batch, qd, cd, min_chunk_tokens=16, variant=variant)
+    o2, l2 = gu.decode(batch, qd, cd, min_chunk_tokens=16, variant=variant)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_variants_agree():
+    """The two kernels compute the same states; they may differ only in
+    rounding of the fp32 arithmetic."""
+    batch, q, cache = _small(13, [1, 17, 300, 2000, 4999], 16, 32, 8)
+    qd, cd = gu.bits_to_dev(q), gu.bits_to_dev(cache)
+    o1, l1 = gu.decode(batch, qd, cd, variant="dot2")
+    o2, l2 = gu.decode(batch, qd, cd, variant="mfma")
+    gu.check_o(gu.dev_to_f64(o2), gu.dev_to_f64(o1), "mfma-vs-dot2")
+    gu.check_lse(l2.cpu().numpy().astype(np.float64), l1.cpu().numpy().astype(np.float64),
+                 "mfma-vs-dot2")

@@ -13,7 +13,7 @@ from tests import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 
-def _sampled_check(name, requests, used_only=False, seed_offset=0):
+def _sampled_check(name, requests, used_only=False, seed_offset=0, **opts):
     import torch
 
     spec, rng, b = workloads.workload(name)
@@ -24,7 +24,7 @@ def _sampled_check(name, requests, used_only=False, seed_offset=0):
                                    used_only=used_only)
     q = workloads.host_query(batch, rng)
     r = gu.runner(max_batch=512, max_nnz=1 << 17)
-    o, lse = gu.decode(batch, gu.bits_to_dev(q), cache, r=r)
+    o, lse = gu.decode(batch, gu.bits_to_dev(q), cache, r=r, **opts)
     host, indptr, indices, last = gu.compact_pages(batch, cache, requests)
     del cache
     torch.cuda.empty_cache()
@@ -37,6 +37,10 @@ def test_skewed_full_size():
     # the 100k-token request (index 63, split across most slots) and three
     # 512-token requests
     _sampled_check("skewed", [63, 0, 31, 62])
+
+
+def test_skewed_full_size_dot2_kernel():
+    _sampled_check("skewed", [63, 5], variant="dot2")
 
 
 def test_llama8b_layer_full_size():
