@@ -8,11 +8,11 @@
 // atomics, so results are reproducible (pinghaoyang, Stream-K paragraph).
 //
 // One workgroup (256 lanes) per (row, query head) task, tasks taken in a
-// grid-stride loop so the grid is fixed.  Pass 1 finds M over the task's lse
-// values; pass 2 splits the states over 8 groups of 32 lanes (4 elements of
-// head_dim per lane, state c to group c mod 8), and the 8 group sums are
-// added in group order.  Empty states (lse = -inf) get weight 0; a task with
-// only empty states yields o = 0, lse = -inf.
+// grid-stride loop so the grid is fixed.  Each of 8 groups of 32 lanes
+// (4 elements of head_dim per lane) folds every 8th state into a running
+// (max, weight sum, weighted o); the group states are then merged, in group
+// order, by the same rule.  Empty states (lse = -inf) get weight 0; a task
+// with only empty states yields o = 0, lse = -inf.
 
 #include <hip/hip_runtime.h>
 
@@ -53,62 +53,87 @@ struct Task {
   int64_t out_row;  // output row (request)
 };
 
+// States of a task are dealt to 8 groups of 32 lanes (state c to group
+// c % 8).  A group loads up to kRound of its states -- lse and o together --
+// in one go, folds them into a running (max, sum of weights, weighted o),
+// and repeats; the 8 group states are then combined in group order.  A task
+// with up to 8 * kRound states thus costs one dependent round trip to memory.
+constexpr int kRound = 8;
+
 template <typename OT>
-__device__ void merge_task(const MergeParams& p, const Task& t, int h, float* red,
-                           float* grp_s, float4* grp_acc) {
+__device__ void merge_task(const MergeParams& p, const Task& t, int h, float* grp_m, float* grp_s,
+                           float4* grp_acc) {
   const int tid = threadIdx.x;
   const int grp = tid >> 5;
   const int gl = tid & 31;
   const OT* o_in = static_cast<const OT*>(p.o_in);
 
-  // pass 1: M = max lse
-  float mx = kNegInf;
-  for (int c = tid; c < t.k; c += kMergeThreads)
-    mx = fmaxf(mx, p.lse_in[(t.first + c) * p.lse_stride_c + h]);
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-
-  // pass 2: weighted sums per group
-  float s = 0.f;
+  float m = kNegInf, s = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (mx != kNegInf) {
-#pragma unroll 4
-    for (int c = grp; c < t.k; c += 8) {
-      const int64_t st = t.first + c;
-      const float L = p.lse_in[st * p.lse_stride_c + h];
-      const float4 v = load4(o_in + st * p.o_stride_c + int64_t(h) * kHeadDim + gl * 4);
-      const float w = __builtin_amdgcn_exp2f((L - mx) * kLog2e);
-      s += w;
-      acc.x = fmaf(w, v.x, acc.x);
-      acc.y = fmaf(w, v.y, acc.y);
-      acc.z = fmaf(w, v.z, acc.z);
-      acc.w = fmaf(w, v.w, acc.w);
+  for (int c0 = grp; c0 < t.k; c0 += 8 * kRound) {
+    float L[kRound];
+    float4 v[kRound];
+#pragma unroll
+    for (int r = 0; r < kRound; ++r) {
+      const int c = c0 + 8 * r;
+      L[r] = kNegInf;
+      v[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c < t.k) {
+        const int64_t st = t.first + c;
+        L[r] = p.lse_in[st * p.lse_stride_c + h];
+        v[r] = load4(o_in + st * p.o_stride_c + int64_t(h) * kHeadDim + gl * 4);
+      }
     }
+    float mr = m;
+#pragma unroll
+    for (int r = 0; r < kRound; ++r) mr = fmaxf(mr, L[r]);
+    if (mr == kNegInf) continue;  // only empty states so far
+    const float keep = __builtin_amdgcn_exp2f((m - mr) * kLog2e);  // 0 when m = -inf
+    s *= keep;
+    acc.x *= keep;
+    acc.y *= keep;
+    acc.z *= keep;
+    acc.w *= keep;
+#pragma unroll
+    for (int r = 0; r < kRound; ++r) {
+      const float w = __builtin_amdgcn_exp2f((L[r] - mr) * kLog2e);  // 0 for empty states
+      s += w;
+      acc.x = fmaf(w, v[r].x, acc.x);
+      acc.y = fmaf(w, v[r].y, acc.y);
+      acc.z = fmaf(w, v[r].z, acc.z);
+      acc.w = fmaf(w, v[r].w, acc.w);
+    }
+    m = mr;
   }
-  if (gl == 0) grp_s[grp] = s;
+  if (gl == 0) {
+    grp_m[grp] = m;
+    grp_s[grp] = s;
+  }
   grp_acc[grp * 32 + gl] = acc;
   __syncthreads();
 
   if (grp == 0) {
-    float S = 0.f;
-    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+    float M = kNegInf;
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      S += grp_s[g];
-      const float4 a = grp_acc[g * 32 + gl];
-      A.x += a.x;
-      A.y += a.y;
-      A.z += a.z;
-      A.w += a.w;
-    }
+    for (int g = 0; g < 8; ++g) M = fmaxf(M, grp_m[g]);
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
     float lse = kNegInf;
-    if (mx != kNegInf) {
+    if (M != kNegInf) {
+      float S = 0.f;
+      float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const float w = __builtin_amdgcn_exp2f((grp_m[g] - M) * kLog2e);
+        const float4 a = grp_acc[g * 32 + gl];
+        S = fmaf(w, grp_s[g], S);
+        A.x = fmaf(w, a.x, A.x);
+        A.y = fmaf(w, a.y, A.y);
+        A.z = fmaf(w, a.z, A.z);
+        A.w = fmaf(w, a.w, A.w);
+      }
       const float inv = 1.f / S;
       o = make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
-      lse = mx + __log2f(S) * kLn2;
+      lse = M + __log2f(S) * kLn2;
     }
     uint2 w;
     w.x = pack_bf16x2(o.x, o.y);
@@ -121,7 +146,7 @@ __device__ void merge_task(const MergeParams& p, const Task& t, int h, float* re
 
 // Split requests of the current plan: fp32 partials in the float workspace.
 __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(MergeParams p) {
-  __shared__ float red[4];
+  __shared__ float grp_m[8];
   __shared__ float grp_s[8];
   __shared__ float4 grp_acc[8 * 32];
   const int32_t* hdr = p.ws + PKD_HEADER_BASE;
@@ -139,13 +164,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(MergePara
     t.out_row = merges[4 * e + 0];
     t.first = merges[4 * e + 1];
     t.k = merges[4 * e + 2];
-    merge_task<float>(q, t, h, red, grp_s, grp_acc);
+    merge_task<float>(q, t, h, grp_m, grp_s, grp_acc);
   }
 }
 
 // k bf16 states per row, rows laid out uniformly.
 __global__ __launch_bounds__(kMergeThreads) void merge_states_kernel(MergeParams p) {
-  __shared__ float red[4];
+  __shared__ float grp_m[8];
   __shared__ float grp_s[8];
   __shared__ float4 grp_acc[8 * 32];
   const int64_t tasks = int64_t(p.rows) * p.H;
@@ -156,7 +181,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_states_kernel(MergeParams
     t.out_row = row;
     t.first = row * p.k;
     t.k = p.k;
-    merge_task<uint16_t>(p, t, h, red, grp_s, grp_acc);
+    merge_task<uint16_t>(p, t, h, grp_m, grp_s, grp_acc);
   }
 }
 
