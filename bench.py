@@ -58,7 +58,7 @@ def parse():
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in ("decode.hip", "merge.hip", "kernels.h"):
+    for name in ("decode.hip", "decode_mfma.hip", "merge.hip", "kernels.h", "device_common.h"):
         with open(os.path.join(ROOT, "paged_kv_decode_11_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
