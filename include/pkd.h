@@ -140,8 +140,9 @@ enum {
 
 /* Create a handle bound to HIP device `device`.  `num_slots` is the number
  * of persistent decode workgroups S (the fixed CTA count N_CTA of the
- * pinghaoyang page's chunk bound); 0 picks 2 per compute unit.  No device
- * memory is allocated. */
+ * pinghaoyang page's chunk bound); 0 picks the compute-unit count times the
+ * decode kernel's resident workgroups per unit (one on gfx950), at most 2 per
+ * compute unit.  No device memory is allocated. */
 int pkd_create(pkd_handle** out, int32_t device, int32_t num_slots);
 int pkd_destroy(pkd_handle* h);
 int32_t pkd_num_slots(const pkd_handle* h);
