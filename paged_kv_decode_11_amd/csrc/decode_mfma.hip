@@ -65,7 +65,7 @@ struct MState {
 };
 
 struct MTile {
-  uint4 k[4];      // B operand: token (lane & 15), 8 elements per 32-wide step
+  uint4 k[4];      // K: see MRef (row-major pieces, or the B operand directly)
   uint32_t v[16];  // V[token t][2 lane .. 2 lane + 1]
 };
 
@@ -79,7 +79,7 @@ template <int P>
 struct MRef<P, true> {
   __amdgpu_buffer_rsrc_t page;  // buffer over the tile's page
   uint32_t tile_off;            // byte offset of the tile's first K row in the page
-  uint32_t koff;                // this lane's K row (clamped), head and 8-element group
+  uint32_t koff;                // this lane's row (lane >> 4) and 16-byte piece (lane & 15)
   uint32_t row_bytes;           // token stride
   uint32_t v_off;               // tile_off + size of the page's K half
   int vlast;                    // last valid row of the tile
@@ -125,7 +125,6 @@ __device__ __forceinline__ MRef<P> m_tile_ref(const MCtx& c, const MIds<P>& ids,
                                               int row16, int kg, int& bad) {
   MRef<P> ref;
   const int valid = min(16, len - 16 * t);
-  const int krow = min(row16, valid - 1);
   if constexpr (P % 16 == 0) {
     const int64_t pg = safe_page(ids.id, c.num_pages, bad);
     // raw buffer (stride 0) over one page; 0x00020000 in the last word selects
@@ -133,11 +132,14 @@ __device__ __forceinline__ MRef<P> m_tile_ref(const MCtx& c, const MIds<P>& ids,
     ref.page = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(c.kv + pg * c.page_bytes),
                                                  0, int(c.page_bytes), 0x00020000);
     ref.tile_off = uint32_t((16 * t) % P) * c.row_bytes;
-    ref.koff = uint32_t(krow) * c.row_bytes + c.head_bytes + uint32_t(kg) * 16;
+    // rows past the valid ones are still inside the page; their logits are
+    // masked before use, so K needs no clamping here
+    ref.koff = uint32_t(kg) * c.row_bytes + c.head_bytes + uint32_t(row16) * 16;
     ref.row_bytes = c.row_bytes;
     ref.v_off = ref.tile_off + uint32_t(c.v_bytes);
     ref.vlast = valid - 1;
   } else {
+    const int krow = min(row16, valid - 1);
     const int64_t kp = safe_page(ids.krow_id, c.num_pages, bad);
     ref.krow = c.kv + kp * c.page_bytes + uint64_t(krow % P) * c.row_bytes + c.head_bytes + kg * 16;
 #pragma unroll
@@ -154,10 +156,12 @@ template <int P>
 __device__ __forceinline__ void m_load(MTile& dst, const MRef<P>& ref, int lane,
                                        uint32_t head_bytes) {
   if constexpr (P % 16 == 0) {
+    // K row-major: load j reads rows 4 j .. 4 j + 3, each whole 256-byte head
+    // row by 16 lanes; the transpose to the operand layout goes through LDS
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const auto w = __builtin_amdgcn_raw_buffer_load_b128(ref.page, ref.koff + 64 * j,
-                                                           ref.tile_off, kBufferNontemporal);
+      const auto w = __builtin_amdgcn_raw_buffer_load_b128(
+          ref.page, ref.koff, ref.tile_off + uint32_t(4 * j) * ref.row_bytes, kBufferNontemporal);
       dst.k[j] = make_uint4(w[0], w[1], w[2], w[3]);
     }
     const uint32_t voff = head_bytes + uint32_t(lane) * 4;
@@ -177,6 +181,7 @@ __device__ __forceinline__ void m_load(MTile& dst, const MRef<P>& ref, int lane,
 // Per-wave LDS used to hand the tile's probabilities and rescale factors to
 // every lane of the wave.
 struct MShared {
+  uint4 kt[16][16];  // K tile, row r's 16-byte piece c at [r][c ^ r]
   uint4 qa[4][64];  // A operand of step j for lane l: q row (l & 15), zero for rows >= g
   float4 p[64];     // lane l's p[v] for rows 4 (l >> 4) + v, token l & 15
   float4 scale[4];  // per 16-lane row group: rescale factors (then m at the end)
@@ -201,8 +206,19 @@ __device__ __forceinline__ void m_tile_step(MState<G>& st, const MTile& cur, MTi
     __builtin_amdgcn_sched_barrier(0);
   }
   floatx4_t s = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (P % 16 == 0) {
+    // Row-major K to the B operand (token lane & 15, 8 elements per lane):
+    // through LDS, with the 16-byte pieces of row r rotated by XOR r so that
+    // both the row writes and the column reads hit 16 distinct bank groups.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) s = mfma_qk(sh.qa[j][lane], cur.k[j], s);
+    for (int j = 0; j < 4; ++j) sh.kt[4 * j + kg][row16 ^ (4 * j + kg)] = cur.k[j];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s = mfma_qk(sh.qa[j][lane], sh.kt[row16][(4 * j + kg) ^ row16], s);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s = mfma_qk(sh.qa[j][lane], cur.k[j], s);
+  }
 
   float p[4], alpha[4];
 #pragma unroll
