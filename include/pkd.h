@@ -95,8 +95,15 @@ enum {
  *   [0, 32)                       device-only words (error flag at 0)
  *   [32, 64)                      header, PKD_H_* below at 32 + index
  *   [off_slots, +S+1)             slot_indptr: items of slot s are
- *                                 items[slot_indptr[s] .. slot_indptr[s+1])
- *   [off_items, +8*I)             items, 8 ints each: request, page_begin
+ *                                 items[slot_indptr[s] .. slot_indptr[s+1]);
+ *                                 off_slots = 64
+ *   [off_first, +8*S)             the first item of each slot again (zeros
+ *                                 for a slot without items), so a workgroup
+ *                                 can read it without waiting for
+ *                                 slot_indptr; off_first = 64 + S + 1
+ *                                 rounded up to a multiple of 8
+ *   [off_items, +8*I)             off_items = off_first + 8*S.
+ *                                 Items, 8 ints each: request, page_begin
  *                                 (index into kv_indices), num_pages,
  *                                 last_len, out (partial id, -1 = write the
  *                                 final output directly), length, 0, 0
@@ -130,11 +137,12 @@ enum {
   PKD_H_OFF_INDICES,
   PKD_H_TOTAL_TOKENS_LO,
   PKD_H_TOTAL_TOKENS_HI,
+  PKD_H_OFF_FIRST,
   PKD_H_COUNT
 };
 #define PKD_HEADER_BASE 32
 #define PKD_PLAN_MAGIC 0x31444B50
-#define PKD_PLAN_VERSION 1
+#define PKD_PLAN_VERSION 2
 
 /* ------------------------------- handle ------------------------------- */
 
@@ -163,9 +171,9 @@ const char* pkd_last_error(void);
 size_t pkd_int_workspace_bytes(int32_t max_batch, int32_t max_nnz, int32_t num_slots);
 size_t pkd_float_workspace_bytes(int32_t max_batch, int32_t num_slots, int32_t num_qo_heads,
                                  int32_t head_dim);
-/* Pinned host staging (allocate with hipHostMalloc or torch pin_memory);
- * it holds two plan images so a new plan never overwrites one whose copy to
- * the device is still in flight. */
+/* Pinned host staging (allocate with hipHostMalloc or torch pin_memory;
+ * pkd_plan rejects memory the device cannot map); it holds two plan images so
+ * a new plan never overwrites one whose upload is still in flight. */
 size_t pkd_host_workspace_bytes(int32_t max_batch, int32_t num_slots);
 
 /* -------------------------------- plan -------------------------------- */
@@ -173,9 +181,9 @@ size_t pkd_host_workspace_bytes(int32_t max_batch, int32_t num_slots);
 /* Validate the page table, cut each request's pages into chunks, assign the
  * chunks longest-first to the handle's S slots, and write the schedule
  * (pinghaoyang page, section on splitting long KV then longest-first
- * assignment) into host_workspace; then queue on `stream` an asynchronous
- * copy of it into int_workspace and a device-to-device copy of kv_indices
- * behind it.  kv_indptr and kv_last_page_len are host arrays read during the
+ * assignment) into host_workspace; then queue on `stream` one kernel that
+ * copies it into int_workspace (reading the pinned host memory directly)
+ * together with kv_indices.  kv_indptr and kv_last_page_len are host arrays read during the
  * call; kv_indices is a device array the caller may reuse once `stream` has
  * passed this call.  Only PKD_DTYPE_BF16, PKD_LAYOUT_NHD, head_dim 128,
  * num_qo_heads / num_kv_heads in {1, 2, 4, 8} and page_size in

@@ -33,7 +33,7 @@ HEADER_BASE = 32
 H_FIELDS = ["MAGIC", "VERSION", "BATCH", "QO_HEADS", "KV_HEADS", "HEAD_DIM", "PAGE_SIZE",
             "SLOTS", "CHUNK_PAGES", "ITEMS", "PARTIALS", "SPLIT", "ALPHA", "BETA", "NNZ",
             "PLAN_ID", "OFF_SLOTS", "OFF_ITEMS", "OFF_MERGE", "OFF_INDICES",
-            "TOTAL_TOKENS_LO", "TOTAL_TOKENS_HI"]
+            "TOTAL_TOKENS_LO", "TOTAL_TOKENS_HI", "OFF_FIRST"]
 H = {name: i for i, name in enumerate(H_FIELDS)}
 
 _STATUS_NAMES = {0: "PKD_OK", 1: "PKD_ERR_INVALID_ARG", 2: "PKD_ERR_UNSUPPORTED",

@@ -57,7 +57,7 @@ def plan_host(kv_indptr, kv_last_page_len, num_qo_heads, num_kv_heads, head_dim,
     indptr = _host_i32(kv_indptr)
     last = _host_i32(kv_last_page_len)
     batch = last.shape[0]
-    cap = 64 + num_slots + 1 + 8 * (indptr[-1] + num_slots + 2 * batch) + 4 * batch + 64
+    cap = 64 + num_slots + 1 + 8 * num_slots + 8 * (indptr[-1] + num_slots + 2 * batch) + 4 * batch + 64
     out = np.zeros(int(cap), dtype=np.int32)
     n = ctypes.c_int64(0)
     o = _opts(**opts)
@@ -72,6 +72,7 @@ def plan_host(kv_indptr, kv_last_page_len, num_qo_heads, num_kv_heads, head_dim,
     merges4 = img[f["OFF_MERGE"]: f["OFF_MERGE"] + 4 * ns].reshape(ns, 4)
     return dict(header=f, image=img,
                 slot_indptr=img[f["OFF_SLOTS"]: f["OFF_SLOTS"] + S + 1].copy(),
+                first_items=img[f["OFF_FIRST"]: f["OFF_FIRST"] + 8 * S].reshape(S, 8).copy(),
                 items=items8[:, :5].copy(), item_lengths=items8[:, 5].copy(),
                 item_pad=items8[:, 6:].copy(), merges=merges4[:, :3].copy(),
                 chunk_pages=f["CHUNK_PAGES"], num_items=I, n_partials=f["PARTIALS"],

@@ -40,6 +40,8 @@ struct pkd_handle {
   void* float_ws = nullptr;
   size_t float_bytes = 0;
   void* host_ws = nullptr;
+  void* host_view_for = nullptr;  // host workspace whose device view is host_view
+  int32_t* host_view = nullptr;   // device-visible address of the host workspace
   size_t host_bytes = 0;
   void* err_cleared_for = nullptr;
 
@@ -284,17 +286,27 @@ int pkd_plan(pkd_handle* h, const int32_t* kv_indptr, const int32_t* kv_indices,
     if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync");
     h->err_cleared_for = int_workspace;
   }
+  if (h->host_view_for != host_workspace) {
+    // the GPU reads the staging area directly, so it must be pinned memory
+    void* view = nullptr;
+    e = hipHostGetDevicePointer(&view, host_workspace, 0);
+    if (e != hipSuccess || !view) {
+      (void)hipGetLastError();
+      return fail(PKD_ERR_INVALID_ARG,
+                  "host workspace must be pinned host memory (hipHostMalloc, torch pin_memory)");
+    }
+    h->host_view = static_cast<int32_t*>(view);
+    h->host_view_for = host_workspace;
+  }
   int32_t* dev = static_cast<int32_t*>(int_workspace);
-  e = hipMemcpyAsync(dev + PKD_HEADER_BASE, image + PKD_HEADER_BASE,
-                     ints_to_bytes(layout.off_indices - PKD_HEADER_BASE), hipMemcpyHostToDevice, s);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan)");
+  e = pkd::launch_plan_upload(h->host_view + half * half_ints + PKD_HEADER_BASE,
+                              dev + PKD_HEADER_BASE, layout.off_indices - PKD_HEADER_BASE,
+                              kv_indices, dev + layout.off_indices, layout.nnz, s);
+  if (e != hipSuccess) return hip_fail(e, "plan upload kernel");
   e = hipEventRecord(h->staging_done[half], s);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   h->staging_pending[half] = true;
   h->staging_next = half ^ 1;
-  e = hipMemcpyAsync(dev + layout.off_indices, kv_indices, ints_to_bytes(layout.nnz),
-                     hipMemcpyDeviceToDevice, s);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (kv_indices)");
 
   h->planned = true;
   h->plan_counter += 1;

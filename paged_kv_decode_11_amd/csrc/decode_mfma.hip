@@ -35,6 +35,7 @@
 #include "device_common.h"
 #include "kernels.h"
 #include "pkd.h"
+#include "plan_layout.h"
 
 namespace pkd {
 namespace {
@@ -300,9 +301,13 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __re
   const int kg = lane >> 4;
   MShared& sh = shared[wave];
 
+  // The slot's bounds and its first item sit at offsets fixed by the slot
+  // count (the grid size), so they are read together with the header.
   const int32_t* hdr = ws + PKD_HEADER_BASE;
-  const int32_t* slot_indptr = ws + hdr[PKD_H_OFF_SLOTS];
-  const int32_t* items = ws + hdr[PKD_H_OFF_ITEMS];
+  const int num_slots = gridDim.x;
+  const int32_t* slot_indptr = ws + plan_off_slots();
+  const int32_t* first = ws + plan_off_first(num_slots) + 8 * int64_t(blockIdx.x);
+  const int32_t* items = ws + plan_off_items(num_slots);
   const int32_t* kv_idx = ws + hdr[PKD_H_OFF_INDICES];
   const int64_t n_partials = hdr[PKD_H_PARTIALS];
   const int Hq = num_qo_heads;
@@ -316,28 +321,38 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __re
   c.v_bytes = uint64_t(P) * c.row_bytes;
   c.page_bytes = 2 * c.v_bytes;
 
+  const int it_begin = slot_indptr[blockIdx.x];
   const int it_end = slot_indptr[blockIdx.x + 1];
-  for (int it = slot_indptr[blockIdx.x]; it < it_end; ++it) {
-    const int32_t* item = items + 8 * it;
-    const int req = item[0];
-    const int out = item[4];
-    const int len = item[5];
-    const int32_t* idx = kv_idx + item[1];
+  const int first_req = first[0], first_page = first[1], first_out = first[4],
+            first_len = first[5];
+  for (int it = it_begin; it < it_end; ++it) {
+    int req = first_req, page_begin = first_page, out = first_out, len = first_len;
+    if (it != it_begin) {
+      const int32_t* item = items + 8 * it;
+      req = item[0];
+      page_begin = item[1];
+      out = item[4];
+      len = item[5];
+    }
+    const int32_t* idx = kv_idx + page_begin;
     const int ntiles = (len + 15) >> 4;
 
     for (int kh = wave; kh < num_kv_heads; kh += nwaves) {
       c.head_bytes = uint32_t(kh) * kHeadDim * 2;
       MState<G> st;
+      // q stays in LDS in operand layout and is re-read for each tile, so it
+      // holds no registers while V is accumulated.  It is loaded first and
+      // staged after the first tiles' loads are issued, which do not wait
+      // for it.
+      uint4 qv[4];
       {
-        // q stays in LDS in operand layout and is re-read for each tile, so it
-        // holds no registers while V is accumulated
         const uint16_t* qrow = q_ptr + (int64_t(req) * Hq + kh * G + row16) * kHeadDim + kg * 8;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          sh.qa[j][lane] = row16 < G ? *reinterpret_cast<const uint4*>(qrow + 32 * j)
-                                     : make_uint4(0u, 0u, 0u, 0u);
-        __builtin_amdgcn_wave_barrier();
+          qv[j] = row16 < G ? *reinterpret_cast<const uint4*>(qrow + 32 * j)
+                            : make_uint4(0u, 0u, 0u, 0u);
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         st.m[v] = kNegInf;
@@ -356,6 +371,10 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __re
         m_load<P>(tb, m_tile_ref<P>(c, m_read_ids<P>(idx, len, 1, row16), len, 1, row16, kg, bad),
                   lane, c.head_bytes);
       MIds<P> ids_next = m_read_ids<P>(idx, len, min(2, ntiles - 1), row16);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sh.qa[j][lane] = qv[j];
+      __builtin_amdgcn_wave_barrier();
       const int last_valid = len - 16 * (ntiles - 1);
       const MRef<P> none = {};
       int n = 0;

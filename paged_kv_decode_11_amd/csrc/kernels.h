@@ -54,6 +54,13 @@ bool decode_variant_built(int g, int page_size);
 int decode_blocks_per_cu(int waves_per_block);
 int decode_blocks_per_cu_dot2(int waves_per_block);
 
+// Copy `image_ints` ints (a multiple of 4, 16-byte aligned ends) of a plan
+// image from pinned host memory (device-visible pointer) to the workspace,
+// and `nnz` page ids from `indices` to `dst_indices`, in one kernel.
+hipError_t launch_plan_upload(const int32_t* image, int32_t* dst, int64_t image_ints,
+                              const int32_t* indices, int32_t* dst_indices, int64_t nnz,
+                              hipStream_t stream);
+
 // Merge of the split requests of the current plan (reads the plan image).
 hipError_t launch_merge_partials(const MergeParams& p, int grid, hipStream_t stream);
 // Merge of `k` bf16 states per row, rows laid out uniformly.

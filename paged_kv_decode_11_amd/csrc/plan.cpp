@@ -21,6 +21,7 @@
 #include <algorithm>
 
 #include "pkd.h"
+#include "plan_layout.h"
 
 namespace pkd {
 
@@ -73,8 +74,7 @@ struct SlotHeap {
 int64_t max_items(int64_t max_batch, int64_t num_slots) { return num_slots + 2 * max_batch; }
 
 int64_t plan_image_ints(int64_t num_slots, int64_t num_items, int64_t n_split) {
-  int64_t off_slots = PKD_HEADER_BASE + 32;
-  int64_t off_items = align_up(off_slots + num_slots + 1, 8);
+  int64_t off_items = plan_off_items(num_slots);
   int64_t off_merge = off_items + 8 * num_items;
   return align_up(off_merge + 4 * n_split, 32);
 }
@@ -150,8 +150,9 @@ int plan_measure(const PlanInput& in, PlanScratch& s, PlanLayout* layout, std::s
     }
   }
   const int64_t I = int64_t(s.items.size());
-  layout->off_slots = PKD_HEADER_BASE + 32;
-  layout->off_items = align_up(layout->off_slots + S + 1, 8);
+  layout->off_slots = plan_off_slots();
+  layout->off_first = plan_off_first(S);
+  layout->off_items = plan_off_items(S);
   layout->off_merge = layout->off_items + 8 * I;
   layout->off_indices = align_up(layout->off_merge + 4 * int64_t(n_split), 32);
   layout->nnz = in.indptr[in.batch];
@@ -217,6 +218,7 @@ int plan_build(const PlanInput& in, PlanScratch& s, int32_t* image, int64_t imag
   hdr[PKD_H_OFF_INDICES] = int32_t(layout->off_indices);
   hdr[PKD_H_TOTAL_TOKENS_LO] = int32_t(layout->total_tokens & 0xffffffff);
   hdr[PKD_H_TOTAL_TOKENS_HI] = int32_t(layout->total_tokens >> 32);
+  hdr[PKD_H_OFF_FIRST] = int32_t(layout->off_first);
 
   int32_t* slot_indptr = image + layout->off_slots;
   for (int32_t q = 0; q <= S; ++q) slot_indptr[q] = 0;
@@ -236,6 +238,11 @@ int plan_build(const PlanInput& in, PlanScratch& s, int32_t* image, int64_t imag
     row[4] = it.out;
     row[5] = it.length;
   }
+  int32_t* first = image + layout->off_first;
+  for (int32_t q = 0; q < S; ++q)
+    if (slot_indptr[q] < slot_indptr[q + 1])
+      std::copy(out_items + 8 * int64_t(slot_indptr[q]), out_items + 8 * int64_t(slot_indptr[q]) + 8,
+                first + 8 * int64_t(q));
 
   // Reduction map: split requests in ascending order.
   int32_t* merge = image + layout->off_merge;

@@ -27,6 +27,7 @@ struct PlanInput {
 
 struct PlanLayout {
   int64_t off_slots = 0;
+  int64_t off_first = 0;
   int64_t off_items = 0;
   int64_t off_merge = 0;
   int64_t off_indices = 0;  // == ints in the plan image

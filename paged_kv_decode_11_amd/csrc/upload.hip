@@ -1,0 +1,45 @@
+// Plan upload for gfx950: one kernel on the caller's stream moves the plan
+// image from pinned host memory (read by the GPU over the bus) and the
+// kv_indices snapshot into the int workspace.  Keeping the upload on the
+// compute queue, rather than handing it to a copy engine, leaves no
+// cross-engine wait between the plan and the first decode launch behind it.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.h"
+
+namespace pkd {
+namespace {
+
+constexpr int kUploadThreads = 256;
+
+__global__ __launch_bounds__(kUploadThreads) void plan_upload_kernel(
+    const int4* __restrict__ image, int4* __restrict__ dst, int64_t image_vec4,
+    const int32_t* __restrict__ indices, int32_t* __restrict__ dst_indices, int64_t nnz) {
+  const int64_t stride = int64_t(gridDim.x) * kUploadThreads;
+  const int64_t tid = int64_t(blockIdx.x) * kUploadThreads + threadIdx.x;
+  for (int64_t i = tid; i < image_vec4; i += stride) dst[i] = image[i];
+  for (int64_t i = tid; i < nnz; i += stride) dst_indices[i] = indices[i];
+}
+
+}  // namespace
+
+hipError_t launch_plan_upload(const int32_t* image, int32_t* dst, int64_t image_ints,
+                              const int32_t* indices, int32_t* dst_indices, int64_t nnz,
+                              hipStream_t stream) {
+  if ((reinterpret_cast<uintptr_t>(image) | reinterpret_cast<uintptr_t>(dst)) & 15 ||
+      image_ints % 4 != 0)
+    return hipErrorInvalidValue;
+  const int64_t work = image_ints / 4 > nnz ? image_ints / 4 : nnz;
+  int64_t grid = (work + kUploadThreads - 1) / kUploadThreads;
+  if (grid > 1024) grid = 1024;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(plan_upload_kernel, dim3(unsigned(grid)), dim3(kUploadThreads), 0, stream,
+                     reinterpret_cast<const int4*>(image), reinterpret_cast<int4*>(dst),
+                     image_ints / 4, indices, dst_indices, nnz);
+  return hipGetLastError();
+}
+
+}  // namespace pkd

@@ -62,6 +62,22 @@ def _lengths_ok(p, P):
     it = p["items"].astype(np.int64)
     assert np.array_equal(p["item_lengths"], (it[:, 2] - 1) * P + it[:, 3])
     assert not p["item_pad"].any()
+    _first_items_ok(p)
+
+
+def _first_items_ok(p):
+    """The fixed offsets the kernels compute from the slot count, and the
+    first-item table: slot s's first item again, zeros for an empty slot."""
+    h, img = p["header"], p["image"]
+    S = h["SLOTS"]
+    assert h["OFF_SLOTS"] == 64
+    assert h["OFF_FIRST"] == -(-(64 + S + 1) // 8) * 8
+    assert h["OFF_ITEMS"] == h["OFF_FIRST"] + 8 * S
+    items8 = img[h["OFF_ITEMS"]: h["OFF_ITEMS"] + 8 * h["ITEMS"]].reshape(-1, 8)
+    ind = p["slot_indptr"]
+    for s in range(S):
+        want = items8[ind[s]] if ind[s] < ind[s + 1] else np.zeros(8, np.int32)
+        assert np.array_equal(p["first_items"][s], want), s
 
 
 @pytest.mark.parametrize("S", [1, 3, 7, 512])
@@ -84,7 +100,7 @@ def test_plan_host_matches_oracle_bit_exact(S, seed):
     _compare(p_lib, p_ref)
     _lengths_ok(p_lib, P)
     h = p_lib["header"]
-    assert h["MAGIC"] == 0x31444B50 and h["VERSION"] == 1 and h["BATCH"] == B
+    assert h["MAGIC"] == 0x31444B50 and h["VERSION"] == 2 and h["BATCH"] == B
     assert h["SLOTS"] == S and h["PAGE_SIZE"] == P and h["NNZ"] == int(indptr[-1])
     assert h["TOTAL_TOKENS_LO"] + (h["TOTAL_TOKENS_HI"] << 32) == int(lens.sum())
 

@@ -99,3 +99,22 @@ def test_workspace_too_small():
         r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, 32, 8, 128, 16, fixed_chunk_pages=1)
     assert e.value.code == _lib.PKD_ERR_WORKSPACE_TOO_SMALL
     r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, 32, 8, 128, 16)  # derived chunks fit
+
+
+def test_pageable_host_workspace_rejected():
+    """The plan upload reads the staging area from the GPU, so pkd_plan
+    refuses host memory the device cannot map (checked on the host)."""
+    import torch
+    import paged_kv_decode_11_amd as pkd
+
+    batch, q, cache = _inputs()
+    r = pkd.DecodePlanRun(max_batch=4, max_nnz=64, max_qo_heads=32)
+    idx = torch.from_numpy(batch.kv_indices).cuda()
+    hb = r.host_workspace.numel()
+    raw = torch.empty(hb + 256, dtype=torch.uint8)  # ordinary pageable memory
+    off = (-raw.data_ptr()) % 256
+    r._host_raw, r.host_workspace = raw, raw[off: off + hb]
+    with pytest.raises(pkd.PkdError) as e:
+        r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, 32, 8, 128, 16)
+    assert e.value.code == _lib.PKD_ERR_INVALID_ARG
+    assert r.plan_id == 0
