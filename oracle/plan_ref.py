@@ -151,3 +151,104 @@ def plan_naive(kv_indptr, kv_last_page_len, page_size: int, num_slots: int,
         assignments.append((best, it))
         loads[best] += it["cost"]
     return _assemble(assignments, num_slots, items, merges, n_partials, header)
+
+
+# ---------------------------------------------------------------------------
+# Shared-prefix (composable) plans: a block row of several requests
+# ---------------------------------------------------------------------------
+#
+# The pinghaoyang page, section "Composable Format：共享前缀与独有后缀分开算"
+# (composable format: shared prefix and unique suffixes computed apart), puts
+# a prefix that several requests share in one block row of the KV matrix, so
+# that one workgroup reads each prefix page once for all of those requests;
+# the suffixes stay one-request rows.  Here a *group* is such a block row: a
+# contiguous range of request rows (qo_indptr) that all attend to the same
+# pages (the group's row of kv_indptr / kv_indices / kv_last_page_len).
+#
+# The work of a group is cut the same way as decode work, with the chunk
+# bound of the same section counting query tiles:
+# L_kv = sum_g ceil(R_g / T_q) l_g / N_CTA, where R_g requests of group g are
+# tiled T_q = 128 / gqa requests at a time (128 query rows per workgroup:
+# gqa query heads per request).  Readings:
+# * one workgroup computes one KV head of one (group, row block, chunk), so
+#   N_CTA per KV head is S / Hkv and L_kv = T_eff Hkv / S with
+#   T_eff = sum_g ceil(R_g / T_q) l_g;
+# * cp = fixed_chunk_pages when given, else
+#   max(ceil(min_chunk_tokens / P), ceil(ceil(T_eff Hkv / S) / P));
+# * an item costs alpha l_q + beta l_kv, with l_q the requests in its block;
+# * ties: (-cost, group, block, chunk, head), then the least-loaded slot,
+#   lowest slot id among equals;
+# * a split group g (k_g > 1 chunks) gives each of its requests r (0-based
+#   within the group) the partial ids base_g + r k_g + j, j = 0..k_g-1, with
+#   base_g the partial count of the split groups before it; the merge list
+#   has one entry (request, base_g + r k_g, k_g) per request of every split
+#   group, in request order.
+
+SHARED_ROWS_PER_WORKGROUP = 128
+
+
+def plan_shared(qo_indptr, kv_indptr, kv_last_page_len, page_size: int, num_slots: int,
+                gqa: int, num_kv_heads: int, fixed_chunk_pages: int = 0,
+                min_chunk_tokens: int = DEFAULT_MIN_CHUNK_TOKENS, alpha: int = 1,
+                beta: int = 1):
+    """Schedule of a shared-prefix plan (heap LPT, as ``plan``)."""
+    qo = [int(x) for x in qo_indptr]
+    indptr = [int(x) for x in kv_indptr]
+    last = [int(x) for x in kv_last_page_len]
+    G = len(last)
+    tq = SHARED_ROWS_PER_WORKGROUP // gqa
+    rows = [qo[g + 1] - qo[g] for g in range(G)]
+    npages = [indptr[g + 1] - indptr[g] for g in range(G)]
+    lengths = [page_size * (npages[g] - 1) + last[g] for g in range(G)]
+    blocks = [_ceil_div(rows[g], tq) for g in range(G)]
+    t_eff = sum(blocks[g] * lengths[g] for g in range(G))
+    cp = chunk_pages(t_eff * num_kv_heads, page_size, num_slots, fixed_chunk_pages,
+                     min_chunk_tokens)
+    items, merges, groups = [], [], []
+    next_partial = 0
+    for g in range(G):
+        k = _ceil_div(npages[g], cp)
+        split = k > 1
+        base = next_partial if split else -1
+        if split:
+            for r in range(rows[g]):
+                merges.append((qo[g] + r, next_partial + r * k, k))
+            next_partial += rows[g] * k
+        groups.append((qo[g], rows[g], k, base))
+        for b in range(blocks[g]):
+            lq = min(tq, rows[g] - b * tq)
+            for j in range(k):
+                pages = min(cp, npages[g] - j * cp)
+                last_len = last[g] if j == k - 1 else page_size
+                length = (pages - 1) * page_size + last_len
+                for h in range(num_kv_heads):
+                    items.append(dict(group=g, block=b, chunk=j, head=h,
+                                      page_begin=indptr[g] + j * cp, num_pages=pages,
+                                      last_len=last_len, length=length,
+                                      out=base + j if split else -1,
+                                      cost=alpha * lq + beta * length))
+    order = sorted(items, key=lambda it: (-it["cost"], it["group"], it["block"], it["chunk"],
+                                          it["head"]))
+    heap = [(0, s) for s in range(num_slots)]
+    per_slot = [[] for _ in range(num_slots)]
+    loads = np.zeros(num_slots, dtype=np.int64)
+    for it in order:
+        load, slot = heapq.heappop(heap)
+        per_slot[slot].append(it)
+        loads[slot] += it["cost"]
+        heapq.heappush(heap, (load + it["cost"], slot))
+    slot_indptr = np.zeros(num_slots + 1, dtype=np.int32)
+    out_rows = []
+    for s in range(num_slots):
+        slot_indptr[s + 1] = slot_indptr[s] + len(per_slot[s])
+        for it in per_slot[s]:
+            out_rows.append((it["group"], it["page_begin"], it["num_pages"], it["last_len"],
+                             it["out"], it["length"], it["block"], it["head"]))
+    return dict(num_groups=G, batch=qo[-1], page_size=int(page_size), num_slots=int(num_slots),
+                chunk_pages=cp, total_tokens=int(sum(lengths)), t_eff=int(t_eff),
+                rows_per_block=tq, slot_indptr=slot_indptr,
+                items=np.array(out_rows, dtype=np.int32).reshape(-1, 8),
+                merges=np.array(merges, dtype=np.int32).reshape(-1, 3),
+                groups=np.array(groups, dtype=np.int32).reshape(-1, 4),
+                num_items=len(items), n_partials=next_partial, n_split=len(merges),
+                slot_loads=loads)
