@@ -69,6 +69,9 @@ typedef enum pkd_status {
 enum { PKD_DTYPE_BF16 = 1, PKD_DTYPE_FP16 = 2, PKD_DTYPE_FP8_E4M3 = 3 };
 enum { PKD_LAYOUT_NHD = 0, PKD_LAYOUT_HND = 1 };
 
+/* Plan kinds (header word PKD_H_KIND). */
+enum { PKD_PLAN_DECODE = 0, PKD_PLAN_SHARED = 1 };
+
 /* Device error flags, read with pkd_read_device_error. */
 enum { PKD_DEVERR_PAGE_ID = 1 }; /* a kv_indices entry was < 0 or >= num_pages */
 
@@ -109,7 +112,17 @@ enum {
  *                                 final output directly), length, 0, 0
  *   [off_merge, +4*n_split)       split requests in ascending order: request,
  *                                 first partial id, number of partials, 0
+ *   [off_groups, +4*num_groups)   shared-prefix plans only: per group, its
+ *                                 first request row, request count, chunk
+ *                                 count k and first partial id (-1 when
+ *                                 k = 1)
  *   [off_indices, +nnz)           copy of kv_indices taken by pkd_plan
+ * In a shared-prefix plan (pkd_plan_shared) the KV rows are groups: an item
+ * is one chunk of one group's pages for one row block of its requests
+ * (rows_per_block of them) and one KV head, its fields being group,
+ * page_begin, num_pages, last_len, out, length, block, head; request r
+ * (0-based in the group) of a split group keeps chunk j's state at partial
+ * id out + r k, and the merge list has one entry per such request.
  * The float workspace holds the partial states: o_part fp32
  * [n_partials, num_qo_heads, head_dim] followed by lse_part fp32
  * [n_partials, num_qo_heads].
@@ -138,6 +151,10 @@ enum {
   PKD_H_TOTAL_TOKENS_LO,
   PKD_H_TOTAL_TOKENS_HI,
   PKD_H_OFF_FIRST,
+  PKD_H_KIND,           /* PKD_PLAN_DECODE or PKD_PLAN_SHARED */
+  PKD_H_NUM_GROUPS,     /* shared-prefix plans: groups (KV rows) */
+  PKD_H_OFF_GROUPS,     /* shared-prefix plans: group table */
+  PKD_H_ROWS_PER_BLOCK, /* shared-prefix plans: requests per workgroup (128 / gqa) */
   PKD_H_COUNT
 };
 #define PKD_HEADER_BASE 32
@@ -208,12 +225,65 @@ int pkd_plan_host(const int32_t* kv_indptr, const int32_t* kv_last_page_len, int
                   int32_t page_size, int32_t num_slots, const pkd_plan_opts* opts,
                   int32_t* out, size_t out_bytes, int64_t* out_ints);
 
+/* ------------------------- shared-prefix plans ------------------------- */
+
+/* A shared-prefix (composable) plan: the pinghaoyang page, section
+ * "Composable Format：共享前缀与独有后缀分开算", puts a prefix that several
+ * requests share in one block row of the KV matrix so that one workgroup
+ * reads each prefix page once for all of them (pyshine, "Cascades, Merges,
+ * and the Autotuner": attention over the shared pages once for all queries,
+ * then the exact merge with each request's own suffix state).
+ *
+ * num_groups groups: group g's requests are rows qo_indptr[g] ..
+ * qo_indptr[g+1]-1 of q (host int32 [num_groups+1], qo_indptr[0] = 0, every
+ * group at least one request) and all attend to group g's pages, given by
+ * kv_indptr / kv_indices / kv_last_page_len over groups exactly as for
+ * pkd_plan.  Runs of the plan (pkd_run with batch = qo_indptr[num_groups])
+ * write, for every request and query head, the attention state over its
+ * group's tokens; combine it with the request's own suffix state with
+ * pkd_merge_state.
+ *
+ * Work is cut by the same rule as decode work with the chunk bound counting
+ * query tiles (pinghaoyang, section on splitting long KV then longest-first
+ * assignment): a row block holds 128 / gqa requests (gqa = num_qo_heads /
+ * num_kv_heads), T_eff = sum over groups of row blocks x group tokens,
+ * cp = max(ceil(min_chunk_tokens / P), ceil(ceil(T_eff num_kv_heads / S) /
+ * P)) pages; an item is one KV head of one (group, row block, chunk) and
+ * costs alpha x (requests in its block) + beta x (chunk tokens).  Built for
+ * gqa 1, 2, 4, 8 and page_size 16, 32, 64 (else PKD_ERR_UNSUPPORTED); the
+ * variant option is ignored.  Workspaces: size them with
+ * pkd_shared_workspace_bytes. */
+int pkd_plan_shared(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                    const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                    int32_t num_groups, int32_t num_qo_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t page_size, int32_t q_dtype, int32_t kv_dtype,
+                    int32_t kv_layout, void* int_workspace, size_t int_workspace_bytes,
+                    void* float_workspace, size_t float_workspace_bytes, void* host_workspace,
+                    size_t host_workspace_bytes, const pkd_plan_opts* opts, pkd_stream_t stream);
+
+/* Workspace sizes for shared-prefix plans of up to max_groups groups over
+ * max_batch requests and max_nnz page ids with derived chunks (a forced
+ * fixed_chunk_pages may need more; pkd_plan_shared then returns
+ * PKD_ERR_WORKSPACE_TOO_SMALL).  Writes the three sizes; returns a status. */
+int pkd_shared_workspace_bytes(int32_t max_groups, int32_t max_batch, int32_t max_nnz,
+                               int32_t num_slots, int32_t num_qo_heads, int32_t num_kv_heads,
+                               int32_t head_dim, size_t* int_bytes, size_t* float_bytes,
+                               size_t* host_bytes);
+
+/* The schedule of pkd_plan_shared on the host only, as pkd_plan_host. */
+int pkd_plan_shared_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                         const int32_t* kv_last_page_len, int32_t num_groups,
+                         int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t page_size, int32_t num_slots, const pkd_plan_opts* opts,
+                         int32_t* out, size_t out_bytes, int64_t* out_ints);
+
 /* --------------------------------- run -------------------------------- */
 
 /* Decode attention for the planned batch on one layer's cache: o (and lse
  * when non-NULL) for every request and query head.  Launches exactly two
  * kernels on `stream` with grids fixed by the handle: the decode kernel (S
- * workgroups) and the merge kernel.  `batch` must equal the planned batch
+ * workgroups; the shared-prefix kernel for a plan from pkd_plan_shared) and
+ * the merge kernel.  `batch` must equal the planned batch
  * and the dtypes the planned ones (else PKD_ERR_STALE_PLAN /
  * PKD_ERR_DTYPE_MISMATCH).  sm_scale <= 0 means 1/sqrt(head_dim).  A page id
  * outside [0, num_pages) is not read: the kernel uses page 0 instead and

@@ -30,10 +30,12 @@ PKD_VARIANT_MFMA = 2
 VARIANTS = {"auto": PKD_VARIANT_AUTO, "dot2": PKD_VARIANT_DOT2, "mfma": PKD_VARIANT_MFMA}
 
 HEADER_BASE = 32
+PKD_PLAN_DECODE, PKD_PLAN_SHARED = 0, 1
 H_FIELDS = ["MAGIC", "VERSION", "BATCH", "QO_HEADS", "KV_HEADS", "HEAD_DIM", "PAGE_SIZE",
             "SLOTS", "CHUNK_PAGES", "ITEMS", "PARTIALS", "SPLIT", "ALPHA", "BETA", "NNZ",
             "PLAN_ID", "OFF_SLOTS", "OFF_ITEMS", "OFF_MERGE", "OFF_INDICES",
-            "TOTAL_TOKENS_LO", "TOTAL_TOKENS_HI", "OFF_FIRST"]
+            "TOTAL_TOKENS_LO", "TOTAL_TOKENS_HI", "OFF_FIRST", "KIND", "NUM_GROUPS",
+            "OFF_GROUPS", "ROWS_PER_BLOCK"]
 H = {name: i for i, name in enumerate(H_FIELDS)}
 
 _STATUS_NAMES = {0: "PKD_OK", 1: "PKD_ERR_INVALID_ARG", 2: "PKD_ERR_UNSUPPORTED",
@@ -70,6 +72,15 @@ SIGNATURES = {
     "pkd_plan_host": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                      ctypes.POINTER(pkd_plan_opts), _vp, _sz,
                                      ctypes.POINTER(_i64)]),
+    "pkd_plan_shared": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                       _i32, _i32, _i32, _vp, _sz, _vp, _sz, _vp, _sz,
+                                       ctypes.POINTER(pkd_plan_opts), _vp]),
+    "pkd_plan_shared_host": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                            ctypes.POINTER(pkd_plan_opts), _vp, _sz,
+                                            ctypes.POINTER(_i64)]),
+    "pkd_shared_workspace_bytes": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                  ctypes.POINTER(_sz), ctypes.POINTER(_sz),
+                                                  ctypes.POINTER(_sz)]),
     "pkd_run": (ctypes.c_int, [_vp, _vp, _i32, _vp, _i64, _i32, _i32, _vp, _vp, ctypes.c_float,
                                _vp]),
     "pkd_read_device_error": (ctypes.c_int, [_vp, _pi32, _vp]),

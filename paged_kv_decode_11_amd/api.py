@@ -102,6 +102,14 @@ class DecodePlanRun:
 
     def __init__(self, max_batch: int, max_nnz: int, max_qo_heads: int = 64, head_dim: int = 128,
                  num_slots: int = 0, device=None):
+        self._create(device, num_slots)
+        S = self.num_slots
+        self.max_batch, self.max_nnz = int(max_batch), int(max_nnz)
+        self._allocate(int_workspace_bytes(max_batch, max_nnz, S),
+                       float_workspace_bytes(max_batch, S, max_qo_heads, head_dim),
+                       host_workspace_bytes(max_batch, S))
+
+    def _create(self, device, num_slots):
         import torch
 
         self._L = _lib.load()
@@ -111,11 +119,11 @@ class DecodePlanRun:
         h = ctypes.c_void_p()
         check(self._L.pkd_create(ctypes.byref(h), dev.index or 0, int(num_slots)))
         self._h = h
-        S = self.num_slots
-        self.max_batch, self.max_nnz = int(max_batch), int(max_nnz)
-        ib = int_workspace_bytes(max_batch, max_nnz, S)
-        fb = float_workspace_bytes(max_batch, S, max_qo_heads, head_dim)
-        hb = host_workspace_bytes(max_batch, S)
+
+    def _allocate(self, ib, fb, hb):
+        import torch
+
+        dev = self.device
         self.int_workspace = torch.empty(ib, dtype=torch.uint8, device=dev)
         self.float_workspace = torch.empty(fb, dtype=torch.uint8, device=dev)
         self._host_raw = torch.empty(hb + 256, dtype=torch.uint8, pin_memory=True)
@@ -233,3 +241,84 @@ def merge_states(o, lse, out=None, lse_out=None, stream=None):
     check(_lib.load().pkd_merge_states(o.data_ptr(), lse.data_ptr(), n, k, Hh, D, out.data_ptr(),
                                        lse_out.data_ptr(), _stream_ptr(stream)))
     return out, lse_out
+
+
+def plan_shared_host(qo_indptr, kv_indptr, kv_last_page_len, num_qo_heads, num_kv_heads, head_dim,
+                     page_size, num_slots, **opts) -> dict:
+    """The schedule pkd_plan_shared would upload (pkd_plan_shared_host),
+    decoded into numpy arrays."""
+    L = _lib.load()
+    qo = _host_i32(qo_indptr)
+    indptr = _host_i32(kv_indptr)
+    last = _host_i32(kv_last_page_len)
+    G = last.shape[0]
+    ib, fb, hb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    check(L.pkd_shared_workspace_bytes(G, int(qo[-1]), int(indptr[-1]), num_slots, num_qo_heads,
+                                       num_kv_heads, head_dim, ctypes.byref(ib), ctypes.byref(fb),
+                                       ctypes.byref(hb)))
+    extra = 8 * int(indptr[-1]) * num_kv_heads * (-(-int(qo[-1]) * (num_qo_heads // num_kv_heads)
+                                                   // 128))  # room for forced chunk sizes
+    out = np.zeros(hb.value // 4 + extra + 64, dtype=np.int32)
+    n = ctypes.c_int64(0)
+    o = _opts(**opts)
+    check(L.pkd_plan_shared_host(qo.ctypes.data, indptr.ctypes.data, last.ctypes.data, G,
+                                 num_qo_heads, num_kv_heads, head_dim, page_size, num_slots,
+                                 ctypes.byref(o), out.ctypes.data, out.nbytes, ctypes.byref(n)))
+    img = out[: n.value]
+    hdr = img[_lib.HEADER_BASE: _lib.HEADER_BASE + len(_lib.H_FIELDS)]
+    f = {name: int(hdr[i]) for name, i in _lib.H.items()}
+    S, I, ns, ng = f["SLOTS"], f["ITEMS"], f["SPLIT"], f["NUM_GROUPS"]
+    return dict(header=f, image=img,
+                slot_indptr=img[f["OFF_SLOTS"]: f["OFF_SLOTS"] + S + 1].copy(),
+                first_items=img[f["OFF_FIRST"]: f["OFF_FIRST"] + 8 * S].reshape(S, 8).copy(),
+                items=img[f["OFF_ITEMS"]: f["OFF_ITEMS"] + 8 * I].reshape(I, 8).copy(),
+                merges=img[f["OFF_MERGE"]: f["OFF_MERGE"] + 4 * ns].reshape(ns, 4)[:, :3].copy(),
+                groups=img[f["OFF_GROUPS"]: f["OFF_GROUPS"] + 4 * ng].reshape(ng, 4).copy(),
+                chunk_pages=f["CHUNK_PAGES"], num_items=I, n_partials=f["PARTIALS"], n_split=ns)
+
+
+class SharedPlanRun(DecodePlanRun):
+    """A plan slot for shared-prefix (composable) plans: ``plan`` takes a
+    group table ``qo_indptr`` (requests of each group) and the page table
+    over groups; ``run`` then gives every request's attention state over its
+    group's tokens (combine it with the request's own suffix state with
+    ``merge_state``).  Workspaces are sized for ``max_groups`` groups over
+    ``max_batch`` requests."""
+
+    def __init__(self, max_groups: int, max_batch: int, max_nnz: int, num_qo_heads: int,
+                 num_kv_heads: int, head_dim: int = 128, num_slots: int = 0, device=None):
+        self._create(device, num_slots)
+        S = self.num_slots
+        self.max_batch, self.max_nnz = int(max_batch), int(max_nnz)
+        ib, fb, hb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+        check(self._L.pkd_shared_workspace_bytes(max_groups, max_batch, max_nnz, S, num_qo_heads,
+                                                 num_kv_heads, head_dim, ctypes.byref(ib),
+                                                 ctypes.byref(fb), ctypes.byref(hb)))
+        self._allocate(ib.value, fb.value, hb.value)
+
+    def plan(self, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, num_qo_heads: int,
+             num_kv_heads: int, head_dim: int, page_size: int, q_data_type=None,
+             kv_data_type=None, kv_layout: str = "NHD", stream=None, **opts):
+        import torch
+
+        q_data_type = torch.bfloat16 if q_data_type is None else q_data_type
+        kv_data_type = torch.bfloat16 if kv_data_type is None else kv_data_type
+        qo = _host_i32(qo_indptr)
+        indptr = _host_i32(kv_indptr)
+        last = _host_i32(kv_last_page_len)
+        if not (isinstance(kv_indices, torch.Tensor) and kv_indices.is_cuda
+                and kv_indices.dtype == torch.int32 and kv_indices.is_contiguous()):
+            raise ValueError("kv_indices must be a contiguous int32 tensor on the GPU")
+        layout = {"NHD": _lib.PKD_LAYOUT_NHD, "HND": _lib.PKD_LAYOUT_HND}[kv_layout]
+        o = _opts(**opts)
+        check(self._L.pkd_plan_shared(
+            self._h, qo.ctypes.data, indptr.ctypes.data, kv_indices.data_ptr(), last.ctypes.data,
+            last.shape[0], num_qo_heads, num_kv_heads, head_dim, page_size,
+            _dtype_code(q_data_type), _dtype_code(kv_data_type), layout,
+            self.int_workspace.data_ptr(), self.int_workspace.numel(),
+            self.float_workspace.data_ptr(), self.float_workspace.numel(),
+            self.host_workspace.data_ptr(), self.host_workspace.numel(), ctypes.byref(o),
+            _stream_ptr(stream)))
+        self._planned = (int(qo[-1]), num_qo_heads, head_dim)
+        self._keep = kv_indices
+

@@ -1,14 +1,15 @@
 // C ABI of the paged GQA decode library (declared in include/pkd.h).
 //
-// pkd_plan runs the host scheduler into a pinned staging buffer and queues
-// its copy into the caller's int workspace, then a device-to-device copy of
-// kv_indices behind it (pinghaoyang FlashInfer page, "固定指针比固定内容更重要":
-// the plan is built in page-locked host memory and copied asynchronously into
-// a workspace at fixed offsets, so the run sees the same addresses with new
-// contents).  pkd_run launches the decode kernel on the handle's S slots and
-// the merge kernel on a fixed grid; neither launch depends on the plan's
-// contents, only on its head configuration, so a captured run stays valid
-// across plans with the same configuration and workspaces.
+// pkd_plan (and pkd_plan_shared) run the host scheduler into a pinned
+// staging buffer and queue one kernel that uploads it, with the kv_indices
+// snapshot, into the caller's int workspace (pinghaoyang FlashInfer page,
+// "固定指针比固定内容更重要": the plan is built in page-locked host memory and
+// copied asynchronously into a workspace at fixed offsets, so the run sees
+// the same addresses with new contents).  pkd_run launches the decode (or
+// shared-prefix) kernel on the handle's S slots and the merge kernel on a
+// fixed grid; neither launch depends on the plan's contents, only on its
+// kind and head configuration, so a captured run stays valid across plans of
+// the same kind and configuration on the same workspaces.
 
 #include <hip/hip_runtime_api.h>
 
@@ -133,6 +134,13 @@ int check_shapes(int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t q_dtype,
   return PKD_OK;
 }
 
+int check_shared_shapes(int32_t Hq, int32_t Hkv, int32_t P) {
+  if (!pkd::prefix_variant_built(Hq / Hkv, P))
+    return fail(PKD_ERR_UNSUPPORTED,
+                "shared-prefix plans are built for group size 1, 2, 4 or 8 and page_size 16, 32 or 64");
+  return PKD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -207,6 +215,25 @@ size_t pkd_host_workspace_bytes(int32_t max_batch, int32_t num_slots) {
   return 2 * ints_to_bytes(staging_half_ints(max_batch, num_slots));
 }
 
+int pkd_shared_workspace_bytes(int32_t max_groups, int32_t max_batch, int32_t max_nnz,
+                               int32_t num_slots, int32_t num_qo_heads, int32_t num_kv_heads,
+                               int32_t head_dim, size_t* int_bytes, size_t* float_bytes,
+                               size_t* host_bytes) {
+  if (max_groups < 1 || max_batch < max_groups || max_nnz < 1 || num_slots < 1 ||
+      num_qo_heads < 1 || num_kv_heads < 1 || num_qo_heads % num_kv_heads != 0 || head_dim < 1)
+    return fail(PKD_ERR_INVALID_ARG, "invalid sizes for pkd_shared_workspace_bytes");
+  const int64_t I =
+      pkd::max_items_shared(max_groups, max_batch, num_slots, num_qo_heads, num_kv_heads);
+  int64_t image = pkd::plan_image_ints(num_slots, I, max_batch, max_groups);
+  image = (image + kStagingAlignInts - 1) / kStagingAlignInts * kStagingAlignInts;
+  const int64_t partials = pkd::max_partials_shared(max_batch, num_slots, num_kv_heads);
+  if (int_bytes) *int_bytes = ints_to_bytes(image + max_nnz);
+  if (float_bytes)
+    *float_bytes = size_t(partials) * size_t(num_qo_heads) * size_t(head_dim + 1) * sizeof(float);
+  if (host_bytes) *host_bytes = 2 * ints_to_bytes(image);
+  return PKD_OK;
+}
+
 int pkd_plan_host(const int32_t* kv_indptr, const int32_t* kv_last_page_len, int32_t batch,
                   int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
                   int32_t page_size, int32_t num_slots, const pkd_plan_opts* opts, int32_t* out,
@@ -222,17 +249,40 @@ int pkd_plan_host(const int32_t* kv_indptr, const int32_t* kv_last_page_len, int
   return PKD_OK;
 }
 
-int pkd_plan(pkd_handle* h, const int32_t* kv_indptr, const int32_t* kv_indices,
-             const int32_t* kv_last_page_len, int32_t batch, int32_t num_qo_heads,
-             int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t q_dtype,
-             int32_t kv_dtype, int32_t kv_layout, void* int_workspace,
-             size_t int_workspace_bytes, void* float_workspace, size_t float_workspace_bytes,
-             void* host_workspace, size_t host_workspace_bytes, const pkd_plan_opts* opts,
-             pkd_stream_t stream) {
+int pkd_plan_shared_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                         const int32_t* kv_last_page_len, int32_t num_groups,
+                         int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t page_size, int32_t num_slots, const pkd_plan_opts* opts,
+                         int32_t* out, size_t out_bytes, int64_t* out_ints) {
+  if (!qo_indptr) return fail(PKD_ERR_INVALID_ARG, "qo_indptr must be non-null");
+  pkd::PlanInput in = make_input(kv_indptr, kv_last_page_len, num_groups, num_qo_heads,
+                                 num_kv_heads, head_dim, page_size, num_slots, opts);
+  in.qo_indptr = qo_indptr;
+  pkd::PlanScratch scratch;
+  pkd::PlanLayout layout;
+  std::string err;
+  int rc = pkd::plan_build(in, scratch, out, int64_t(out_bytes / sizeof(int32_t)), &layout, &err);
+  if (rc != PKD_OK) return fail(rc, err);
+  if (out_ints) *out_ints = layout.off_indices;
+  return PKD_OK;
+}
+
+// Both plan kinds: qo_indptr is null for a decode plan, the group table of
+// requests for a shared-prefix plan (then `batch` counts groups).
+static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                     const int32_t* kv_indices, const int32_t* kv_last_page_len, int32_t batch,
+                     int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t page_size, int32_t q_dtype, int32_t kv_dtype, int32_t kv_layout,
+                     void* int_workspace, size_t int_workspace_bytes, void* float_workspace,
+                     size_t float_workspace_bytes, void* host_workspace,
+                     size_t host_workspace_bytes, const pkd_plan_opts* opts,
+                     pkd_stream_t stream) {
   if (!h) return fail(PKD_ERR_INVALID_ARG, "null handle");
   int rc = check_shapes(num_qo_heads, num_kv_heads, head_dim, page_size, q_dtype, kv_dtype,
                         kv_layout);
   if (rc != PKD_OK) return rc;
+  if (qo_indptr && (rc = check_shared_shapes(num_qo_heads, num_kv_heads, page_size)) != PKD_OK)
+    return rc;
   if (!kv_indices || !int_workspace || !float_workspace || !host_workspace)
     return fail(PKD_ERR_INVALID_ARG, "kv_indices and the three workspaces must be non-null");
   if ((reinterpret_cast<uintptr_t>(int_workspace) & 255) ||
@@ -261,6 +311,7 @@ int pkd_plan(pkd_handle* h, const int32_t* kv_indptr, const int32_t* kv_indices,
 
   pkd::PlanInput in = make_input(kv_indptr, kv_last_page_len, batch, num_qo_heads, num_kv_heads,
                                  head_dim, page_size, h->num_slots, opts);
+  in.qo_indptr = qo_indptr;
   in.plan_id = h->plan_counter + 1;
   pkd::PlanLayout layout;
   std::string err;
@@ -310,7 +361,7 @@ int pkd_plan(pkd_handle* h, const int32_t* kv_indptr, const int32_t* kv_indices,
 
   h->planned = true;
   h->plan_counter += 1;
-  h->batch = batch;
+  h->batch = layout.num_requests;
   h->Hq = num_qo_heads;
   h->Hkv = num_kv_heads;
   h->D = head_dim;
@@ -326,6 +377,34 @@ int pkd_plan(pkd_handle* h, const int32_t* kv_indptr, const int32_t* kv_indices,
   h->host_ws = host_workspace;
   h->host_bytes = host_workspace_bytes;
   return PKD_OK;
+}
+
+int pkd_plan(pkd_handle* h, const int32_t* kv_indptr, const int32_t* kv_indices,
+             const int32_t* kv_last_page_len, int32_t batch, int32_t num_qo_heads,
+             int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t q_dtype,
+             int32_t kv_dtype, int32_t kv_layout, void* int_workspace,
+             size_t int_workspace_bytes, void* float_workspace, size_t float_workspace_bytes,
+             void* host_workspace, size_t host_workspace_bytes, const pkd_plan_opts* opts,
+             pkd_stream_t stream) {
+  return plan_impl(h, nullptr, kv_indptr, kv_indices, kv_last_page_len, batch, num_qo_heads,
+                   num_kv_heads, head_dim, page_size, q_dtype, kv_dtype, kv_layout,
+                   int_workspace, int_workspace_bytes, float_workspace, float_workspace_bytes,
+                   host_workspace, host_workspace_bytes, opts, stream);
+}
+
+int pkd_plan_shared(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                    const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                    int32_t num_groups, int32_t num_qo_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t page_size, int32_t q_dtype, int32_t kv_dtype,
+                    int32_t kv_layout, void* int_workspace, size_t int_workspace_bytes,
+                    void* float_workspace, size_t float_workspace_bytes, void* host_workspace,
+                    size_t host_workspace_bytes, const pkd_plan_opts* opts,
+                    pkd_stream_t stream) {
+  if (!qo_indptr) return fail(PKD_ERR_INVALID_ARG, "qo_indptr must be non-null");
+  return plan_impl(h, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, num_groups,
+                   num_qo_heads, num_kv_heads, head_dim, page_size, q_dtype, kv_dtype, kv_layout,
+                   int_workspace, int_workspace_bytes, float_workspace, float_workspace_bytes,
+                   host_workspace, host_workspace_bytes, opts, stream);
 }
 
 int pkd_run(pkd_handle* h, const void* q, int32_t batch, const void* kv_cache, int64_t num_pages,
@@ -397,9 +476,12 @@ int pkd_run(pkd_handle* h, const void* q, int32_t batch, const void* kv_cache, i
 
   hipError_t e;
   if (prof && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  e = h->variant == PKD_VARIANT_DOT2
-          ? pkd::launch_decode(dp, h->Hq / h->Hkv, h->P, h->num_slots, s)
-          : pkd::launch_decode_mfma(dp, h->Hq / h->Hkv, h->P, h->num_slots, s);
+  if (h->layout.kind == PKD_PLAN_SHARED)
+    e = pkd::launch_prefix_mfma(dp, h->Hq / h->Hkv, h->P, h->num_slots, s);
+  else if (h->variant == PKD_VARIANT_DOT2)
+    e = pkd::launch_decode(dp, h->Hq / h->Hkv, h->P, h->num_slots, s);
+  else
+    e = pkd::launch_decode_mfma(dp, h->Hq / h->Hkv, h->P, h->num_slots, s);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
   if (prof && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   e = pkd::launch_merge_partials(mp, h->merge_grid, s);

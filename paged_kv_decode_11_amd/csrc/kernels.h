@@ -49,6 +49,11 @@ hipError_t launch_decode(const DecodeParams& p, int g, int page_size, int num_sl
 hipError_t launch_decode_mfma(const DecodeParams& p, int g, int page_size, int num_slots,
                               hipStream_t stream);
 bool decode_variant_built(int g, int page_size);
+// Shared-prefix kernel (prefix_mfma.hip): one KV head of one (group, row
+// block, chunk) item per workgroup, 128 query rows sharing each K/V tile.
+hipError_t launch_prefix_mfma(const DecodeParams& p, int g, int page_size, int num_slots,
+                              hipStream_t stream);
+bool prefix_variant_built(int g, int page_size);
 // Occupancy (workgroups per CU) of the matrix-core decode kernel at g=4,
 // P=16 (the default kernel), and of the dot-product kernel.
 int decode_blocks_per_cu(int waves_per_block);

@@ -73,10 +73,21 @@ struct SlotHeap {
 
 int64_t max_items(int64_t max_batch, int64_t num_slots) { return num_slots + 2 * max_batch; }
 
-int64_t plan_image_ints(int64_t num_slots, int64_t num_items, int64_t n_split) {
+int64_t max_items_shared(int64_t max_groups, int64_t max_requests, int64_t num_slots,
+                         int64_t num_qo_heads, int64_t num_kv_heads) {
+  const int64_t gqa = num_qo_heads / num_kv_heads;
+  return num_slots + 2 * num_kv_heads * (max_groups + ceil_div(max_requests * gqa, 128));
+}
+
+int64_t max_partials_shared(int64_t max_requests, int64_t num_slots, int64_t num_kv_heads) {
+  return max_requests * (ceil_div(num_slots, num_kv_heads) + 2);
+}
+
+int64_t plan_image_ints(int64_t num_slots, int64_t num_items, int64_t n_merge,
+                        int64_t num_groups) {
   int64_t off_items = plan_off_items(num_slots);
   int64_t off_merge = off_items + 8 * num_items;
-  return align_up(off_merge + 4 * n_split, 32);
+  return align_up(off_merge + 4 * n_merge + 4 * num_groups, 32);
 }
 
 int plan_validate(const PlanInput& in, std::string* err) {
@@ -94,6 +105,15 @@ int plan_validate(const PlanInput& in, std::string* err) {
     return fail(PKD_ERR_INVALID_ARG, "num_qo_heads must be a multiple of num_kv_heads");
   if (in.head_dim < 1) return fail(PKD_ERR_INVALID_ARG, "head_dim must be >= 1");
   if (in.indptr[0] != 0) return fail(PKD_ERR_INVALID_ARG, "kv_indptr[0] must be 0");
+  if (in.qo_indptr) {
+    const int32_t gqa = in.num_qo_heads / in.num_kv_heads;
+    if (kSharedRowsPerWorkgroup % gqa != 0)
+      return fail(PKD_ERR_UNSUPPORTED, "shared-prefix plans need num_qo_heads / num_kv_heads to divide 128");
+    if (in.qo_indptr[0] != 0) return fail(PKD_ERR_INVALID_ARG, "qo_indptr[0] must be 0");
+    for (int32_t g = 0; g < in.batch; ++g)
+      if (in.qo_indptr[g + 1] - in.qo_indptr[g] < 1)
+        return fail(PKD_ERR_INVALID_ARG, "every group needs at least one request (qo_indptr must increase)");
+  }
   for (int32_t i = 0; i < in.batch; ++i) {
     if (in.indptr[i + 1] - in.indptr[i] < 1)
       return fail(PKD_ERR_INVALID_ARG, "every request needs at least one page (kv_indptr must increase)");
@@ -112,55 +132,88 @@ int plan_measure(const PlanInput& in, PlanScratch& s, PlanLayout* layout, std::s
   const int64_t beta = in.beta <= 0 ? 1 : in.beta;
   const int64_t min_chunk = in.min_chunk_tokens <= 0 ? 128 : in.min_chunk_tokens;
 
-  int64_t total = 0;
-  for (int32_t i = 0; i < in.batch; ++i)
-    total += P * (int64_t(in.indptr[i + 1] - in.indptr[i]) - 1) + in.last[i];
+  const bool shared = in.qo_indptr != nullptr;
+  const int32_t gqa = in.num_qo_heads / in.num_kv_heads;
+  const int64_t tq = shared ? kSharedRowsPerWorkgroup / gqa : 1;  // requests per row block
+  const int64_t heads = shared ? in.num_kv_heads : 1;  // items per chunk and block
+  auto rows_of = [&](int32_t i) -> int64_t { return shared ? in.qo_indptr[i + 1] - in.qo_indptr[i] : 1; };
+
+  // Total work: KV tokens times query tiles (row blocks), times the KV heads
+  // when each head is an item of its own.
+  int64_t total = 0, work = 0;
+  for (int32_t i = 0; i < in.batch; ++i) {
+    const int64_t l = P * (int64_t(in.indptr[i + 1] - in.indptr[i]) - 1) + in.last[i];
+    total += l;
+    work += ceil_div(rows_of(i), tq) * l;
+  }
+  work *= heads;
 
   int64_t cp = in.fixed_chunk_pages > 0
                    ? int64_t(in.fixed_chunk_pages)
-                   : std::max<int64_t>({1, ceil_div(min_chunk, P), ceil_div(ceil_div(total, S), P)});
+                   : std::max<int64_t>({1, ceil_div(min_chunk, P), ceil_div(ceil_div(work, S), P)});
   if (cp > INT32_MAX) cp = INT32_MAX;
 
   s.items.clear();
-  int32_t next_partial = 0, n_split = 0;
+  s.merges.clear();
+  s.groups.clear();
+  int64_t next_partial = 0;
   for (int32_t i = 0; i < in.batch; ++i) {
     const int64_t n = in.indptr[i + 1] - in.indptr[i];
     const int64_t k = ceil_div(n, cp);
+    const int64_t rows = rows_of(i);
     const bool split = k > 1;
-    const int32_t base = next_partial;
+    const int64_t base = split ? next_partial : -1;
     if (split) {
-      if (int64_t(next_partial) + k > INT32_MAX) {
+      if (next_partial + rows * k > INT32_MAX) {
         if (err) *err = "too many partial states";
         return PKD_ERR_INVALID_ARG;
       }
-      next_partial += int32_t(k);
-      ++n_split;
+      const int32_t row0 = shared ? in.qo_indptr[i] : i;
+      for (int64_t r = 0; r < rows; ++r)
+        s.merges.push_back({int32_t(row0 + r), int32_t(next_partial + r * k), int32_t(k)});
+      next_partial += rows * k;
     }
-    for (int64_t j = 0; j < k; ++j) {
-      PlanItem it;
-      it.request = i;
-      it.chunk = int32_t(j);
-      it.page_begin = int32_t(in.indptr[i] + j * cp);
-      it.num_pages = int32_t(std::min<int64_t>(cp, n - j * cp));
-      it.last_len = j == k - 1 ? in.last[i] : int32_t(P);
-      it.length = int32_t((it.num_pages - 1) * P + it.last_len);
-      it.out = split ? base + int32_t(j) : -1;
-      it.cost = alpha + beta * it.length;
-      s.items.push_back(it);
+    if (shared) s.groups.push_back({in.qo_indptr[i], int32_t(rows), int32_t(k), int32_t(base)});
+    const int64_t blocks = ceil_div(rows, tq);
+    for (int64_t b = 0; b < blocks; ++b) {
+      const int64_t lq = std::min<int64_t>(tq, rows - b * tq);
+      for (int64_t j = 0; j < k; ++j) {
+        PlanItem it;
+        it.request = i;
+        it.chunk = int32_t(j);
+        it.page_begin = int32_t(in.indptr[i] + j * cp);
+        it.num_pages = int32_t(std::min<int64_t>(cp, n - j * cp));
+        it.last_len = j == k - 1 ? in.last[i] : int32_t(P);
+        it.length = int32_t((it.num_pages - 1) * P + it.last_len);
+        it.out = split ? int32_t(base + j) : -1;
+        it.cost = alpha * lq + beta * it.length;
+        it.block = int32_t(b);
+        for (int64_t h = 0; h < heads; ++h) {
+          it.head = int32_t(h);
+          s.items.push_back(it);
+        }
+      }
     }
   }
   const int64_t I = int64_t(s.items.size());
+  const int64_t n_merge = int64_t(s.merges.size());
+  const int64_t n_groups = int64_t(s.groups.size());
+  layout->kind = shared ? PKD_PLAN_SHARED : PKD_PLAN_DECODE;
+  layout->num_requests = shared ? in.qo_indptr[in.batch] : in.batch;
+  layout->num_groups = int32_t(n_groups);
+  layout->rows_per_block = int32_t(tq);
   layout->off_slots = plan_off_slots();
   layout->off_first = plan_off_first(S);
   layout->off_items = plan_off_items(S);
   layout->off_merge = layout->off_items + 8 * I;
-  layout->off_indices = align_up(layout->off_merge + 4 * int64_t(n_split), 32);
+  layout->off_groups = layout->off_merge + 4 * n_merge;
+  layout->off_indices = align_up(layout->off_groups + 4 * n_groups, 32);
   layout->nnz = in.indptr[in.batch];
   layout->total_tokens = total;
   layout->chunk_pages = int32_t(cp);
   layout->num_items = int32_t(I);
-  layout->n_partials = next_partial;
-  layout->n_split = n_split;
+  layout->n_partials = int32_t(next_partial);
+  layout->n_split = int32_t(n_merge);
   return PKD_OK;
 }
 
@@ -184,7 +237,9 @@ int plan_build(const PlanInput& in, PlanScratch& s, int32_t* image, int64_t imag
     const PlanItem& B = items[b];
     if (A.cost != B.cost) return A.cost > B.cost;
     if (A.request != B.request) return A.request < B.request;
-    return A.chunk < B.chunk;
+    if (A.block != B.block) return A.block < B.block;
+    if (A.chunk != B.chunk) return A.chunk < B.chunk;
+    return A.head < B.head;
   });
 
   // Each item to the least-loaded slot.
@@ -198,7 +253,7 @@ int plan_build(const PlanInput& in, PlanScratch& s, int32_t* image, int64_t imag
   int32_t* hdr = image + PKD_HEADER_BASE;
   hdr[PKD_H_MAGIC] = PKD_PLAN_MAGIC;
   hdr[PKD_H_VERSION] = PKD_PLAN_VERSION;
-  hdr[PKD_H_BATCH] = in.batch;
+  hdr[PKD_H_BATCH] = layout->num_requests;
   hdr[PKD_H_QO_HEADS] = in.num_qo_heads;
   hdr[PKD_H_KV_HEADS] = in.num_kv_heads;
   hdr[PKD_H_HEAD_DIM] = in.head_dim;
@@ -219,6 +274,10 @@ int plan_build(const PlanInput& in, PlanScratch& s, int32_t* image, int64_t imag
   hdr[PKD_H_TOTAL_TOKENS_LO] = int32_t(layout->total_tokens & 0xffffffff);
   hdr[PKD_H_TOTAL_TOKENS_HI] = int32_t(layout->total_tokens >> 32);
   hdr[PKD_H_OFF_FIRST] = int32_t(layout->off_first);
+  hdr[PKD_H_KIND] = layout->kind;
+  hdr[PKD_H_NUM_GROUPS] = layout->num_groups;
+  hdr[PKD_H_OFF_GROUPS] = int32_t(layout->off_groups);
+  hdr[PKD_H_ROWS_PER_BLOCK] = layout->rows_per_block;
 
   int32_t* slot_indptr = image + layout->off_slots;
   for (int32_t q = 0; q <= S; ++q) slot_indptr[q] = 0;
@@ -237,6 +296,8 @@ int plan_build(const PlanInput& in, PlanScratch& s, int32_t* image, int64_t imag
     row[3] = it.last_len;
     row[4] = it.out;
     row[5] = it.length;
+    row[6] = it.block;
+    row[7] = it.head;
   }
   int32_t* first = image + layout->off_first;
   for (int32_t q = 0; q < S; ++q)
@@ -244,19 +305,20 @@ int plan_build(const PlanInput& in, PlanScratch& s, int32_t* image, int64_t imag
       std::copy(out_items + 8 * int64_t(slot_indptr[q]), out_items + 8 * int64_t(slot_indptr[q]) + 8,
                 first + 8 * int64_t(q));
 
-  // Reduction map: split requests in ascending order.
+  // Reduction map (request order) and, for shared-prefix plans, the group
+  // table.
   int32_t* merge = image + layout->off_merge;
-  int32_t e = 0;
-  for (int32_t x = 0; x < I; ++x) {
-    const PlanItem& it = items[x];  // request/chunk order
-    if (it.out >= 0 && it.chunk == 0) {
-      int32_t k = 1;
-      while (x + k < I && items[x + k].request == it.request) ++k;
-      merge[4 * e + 0] = it.request;
-      merge[4 * e + 1] = it.out;
-      merge[4 * e + 2] = k;
-      ++e;
-    }
+  for (size_t e = 0; e < s.merges.size(); ++e) {
+    merge[4 * e + 0] = s.merges[e].request;
+    merge[4 * e + 1] = s.merges[e].first;
+    merge[4 * e + 2] = s.merges[e].k;
+  }
+  int32_t* groups = image + layout->off_groups;
+  for (size_t g = 0; g < s.groups.size(); ++g) {
+    groups[4 * g + 0] = s.groups[g].row0;
+    groups[4 * g + 1] = s.groups[g].rows;
+    groups[4 * g + 2] = s.groups[g].k;
+    groups[4 * g + 3] = s.groups[g].base;
   }
   return PKD_OK;
 }

@@ -11,6 +11,10 @@
 
 namespace pkd {
 
+// Query rows one workgroup of the shared-prefix kernel covers (8 waves of
+// 16 rows): a row block holds 128 / gqa requests.
+constexpr int kSharedRowsPerWorkgroup = 128;
+
 constexpr int64_t plan_off_slots() { return PKD_HEADER_BASE + 32; }
 constexpr int64_t plan_off_first(int64_t num_slots) {
   return (plan_off_slots() + num_slots + 1 + 7) / 8 * 8;

@@ -163,3 +163,40 @@ def test_item_bound_holds_for_derived_chunks():
         p = pkd.plan_host(indptr, last, 32, 8, 128, P, S)
         assert p["num_items"] <= S + 2 * B
         assert p["n_partials"] <= p["num_items"]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_plan_shared_host_matches_oracle_bit_exact(seed):
+    rng = np.random.default_rng(500 + seed)
+    P = [16, 32, 64, 16, 16, 32, 64, 16][seed]
+    Hq, Hkv = [(32, 8), (32, 4), (64, 8), (8, 8), (16, 2), (32, 32), (64, 8), (32, 8)][seed]
+    G = int(rng.integers(1, 7))
+    rows = rng.integers(1, 200, size=G)
+    qo = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    lens = rng.integers(1, 12000, size=G)
+    indptr, _, last = pt.page_table(lens, P)
+    S = [256, 7, 1, 512, 33, 256, 64, 100][seed]
+    opts = [dict(), dict(min_chunk_tokens=16), dict(fixed_chunk_pages=3), dict(alpha=5, beta=2),
+            dict(min_chunk_tokens=1024), dict(), dict(fixed_chunk_pages=1), dict()][seed]
+    lib = pkd.plan_shared_host(qo, indptr, last, Hq, Hkv, 128, P, S, **opts)
+    ref = plan_ref.plan_shared(qo, indptr, last, P, S, Hq // Hkv, Hkv, **opts)
+    assert lib["chunk_pages"] == ref["chunk_pages"]
+    assert lib["num_items"] == ref["num_items"] and lib["n_partials"] == ref["n_partials"]
+    assert np.array_equal(lib["slot_indptr"], ref["slot_indptr"])
+    assert np.array_equal(lib["items"], ref["items"])
+    assert np.array_equal(lib["merges"], ref["merges"])
+    assert np.array_equal(lib["groups"], ref["groups"])
+    h = lib["header"]
+    assert h["KIND"] == 1 and h["BATCH"] == int(qo[-1]) and h["NUM_GROUPS"] == G
+    assert h["ROWS_PER_BLOCK"] == 128 // (Hq // Hkv)
+    _first_items_ok(dict(lib, first_items=lib["first_items"]))
+
+
+def test_plan_shared_host_rejects_bad_groups():
+    indptr, _, last = pt.page_table([100], 16)
+    with pytest.raises(pkd.PkdError) as e:  # gqa 3 does not divide the 128-row block
+        pkd.plan_shared_host([0, 2], indptr, last, 24, 8, 128, 16, 16)
+    assert e.value.code == _lib.PKD_ERR_UNSUPPORTED
+    with pytest.raises(pkd.PkdError) as e:
+        pkd.plan_shared_host([0, 0], indptr, last, 32, 8, 128, 16, 16)
+    assert e.value.code == _lib.PKD_ERR_INVALID_ARG

@@ -1,0 +1,157 @@
+"""Shared-prefix (composable) plans on the GPU, through the C ABI: every
+request's attention state over its group's pages, from the shared-prefix
+kernel (each K/V tile read once per row block of the group), against the fp64
+oracle run on the same table expanded to one page list per request.  Bar:
+max abs error <= 1e-2 on the bf16 output and <= 1e-3 on lse."""
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import attention as att
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+_SHARED = {}
+
+
+def shared_runner(max_groups=8, max_batch=512, max_nnz=1 << 15, Hq=32, Hkv=8, num_slots=0):
+    import paged_kv_decode_11_amd as pkd
+
+    key = (max_groups, max_batch, max_nnz, Hq, Hkv, num_slots)
+    if key not in _SHARED:
+        _SHARED[key] = pkd.SharedPlanRun(max_groups, max_batch, max_nnz, Hq, Hkv, 128, num_slots)
+    return _SHARED[key]
+
+
+def _groups(seed, rows, lens, P, Hq, Hkv, spare=7, poison=True):
+    """Seeded groups: group g has rows[g] requests over lens[g] tokens."""
+    rng = np.random.default_rng(seed)
+    gb = workloads.make_batch(lens, P, int(sum(-(-l // P) for l in lens)) + spare, Hq, Hkv, 128,
+                              rng)
+    qo = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    B = int(qo[-1])
+    q = workloads.normal_bf16(rng, (B, Hq, 128))
+    cache = workloads.host_cache(gb, rng, poison=poison)
+    return gb, qo, q, cache
+
+
+def _expanded(gb, qo):
+    """The per-request page table: request r of group g gets group g's pages."""
+    G = len(qo) - 1
+    indptr, indices, last = [0], [], []
+    for g in range(G):
+        pages = gb.kv_indices[gb.kv_indptr[g]:gb.kv_indptr[g + 1]]
+        for _ in range(qo[g + 1] - qo[g]):
+            indices.extend(pages.tolist())
+            indptr.append(len(indices))
+            last.append(int(gb.kv_last_page_len[g]))
+    return (np.array(indptr, np.int32), np.array(indices, np.int32), np.array(last, np.int32))
+
+
+def _run_shared(gb, qo, q_dev, cache_dev, r=None, sm_scale=None, **opts):
+    import torch
+
+    r = r or shared_runner(Hq=gb.num_qo_heads, Hkv=gb.num_kv_heads)
+    idx = torch.from_numpy(gb.kv_indices.astype(np.int32)).cuda()
+    r.plan(qo, gb.kv_indptr, idx, gb.kv_last_page_len, gb.num_qo_heads, gb.num_kv_heads, 128,
+           gb.page_size, **opts)
+    o, lse = r.run(q_dev, cache_dev, return_lse=True, sm_scale=sm_scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _check(seed, rows, lens, P, Hq, Hkv, label, sm_scale=None, **opts):
+    gb, qo, q, cache = _groups(seed, rows, lens, P, Hq, Hkv)
+    gu.say(label, "groups", len(rows), "rows", list(rows), "lens", list(lens), "P", P, "Hq", Hq,
+           "Hkv", Hkv, opts)
+    o, lse = _run_shared(gb, qo, gu.bits_to_dev(q), gu.bits_to_dev(cache), sm_scale=sm_scale,
+                         **opts)
+    indptr, indices, last = _expanded(gb, qo)
+    o_ref, lse_ref = att.decode(q, cache, indptr, indices, last, Hkv, sm_scale=sm_scale)
+    return gu.assert_close(o, lse, o_ref, lse_ref, label=label)
+
+
+@pytest.mark.parametrize("P", [16, 32, 64])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_one_group_page_sizes_and_gqa(P, G):
+    Hkv = 8 if G <= 4 else 4
+    tq = 128 // G
+    # a full row block, a partial one, and a tail tile of 9 tokens
+    _check(10 * P + G, [tq + 3], [5 * P + 9], P, Hkv * G, Hkv, f"P{P}-G{G}")
+    _check(11 * P + G, [tq + 3], [5 * P + 9], P, Hkv * G, Hkv, f"P{P}-G{G}-split",
+           fixed_chunk_pages=1)
+
+
+@pytest.mark.parametrize("rows", [1, 5, 31, 32, 33, 100])
+def test_row_counts(rows):
+    _check(40 + rows, [rows], [700], 16, 32, 8, f"rows{rows}")
+    _check(41 + rows, [rows], [700], 16, 32, 8, f"rows{rows}-mct16", min_chunk_tokens=16)
+
+
+def test_several_groups_mixed():
+    _check(70, [3, 1, 40, 17], [1, 2000, 333, 16], 16, 32, 8, "groups")
+    _check(71, [3, 1, 40, 17], [1, 2000, 333, 16], 16, 32, 8, "groups-split", fixed_chunk_pages=2)
+    _check(72, [3, 1, 40, 17], [1, 2000, 333, 16], 16, 32, 8, "groups-scale", sm_scale=0.2,
+           min_chunk_tokens=16)
+
+
+def test_kv_head_counts():
+    _check(80, [9, 4], [500, 77], 16, 8, 8, "Hkv8-G1")
+    _check(81, [9, 4], [500, 77], 16, 16, 16, "Hkv16-G1")
+    _check(82, [9, 4], [500, 77], 16, 8, 2, "Hkv2-G4", min_chunk_tokens=16)
+
+
+def test_deterministic():
+    import torch
+
+    gb, qo, q, cache = _groups(90, [40, 7], [3000, 900], 16, 32, 8)
+    qd, cd = gu.bits_to_dev(q), gu.bits_to_dev(cache)
+    o1, l1 = _run_shared(gb, qo, qd, cd, min_chunk_tokens=16)
+    o2, l2 = _run_shared(gb, qo, qd, cd, min_chunk_tokens=16)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_unbuilt_page_size_rejected():
+    import torch
+    import paged_kv_decode_11_amd as pkd
+    from paged_kv_decode_11_amd import _lib
+
+    gb, qo, q, cache = _groups(91, [4], [100], 8, 32, 8)
+    r = shared_runner()
+    idx = torch.from_numpy(gb.kv_indices.astype(np.int32)).cuda()
+    with pytest.raises(pkd.PkdError) as e:
+        r.plan(qo, gb.kv_indptr, idx, gb.kv_last_page_len, 32, 8, 128, 8)
+    assert e.value.code == _lib.PKD_ERR_UNSUPPORTED
+
+
+def test_shared_prefix_workload_composable_full():
+    """The shared-prefix workload at full size: the prefix state of all 32
+    requests from one shared-prefix plan (the 512 prefix pages read once per
+    KV head), the suffix states from a decode plan, merged, against the
+    single-format oracle on 8 requests."""
+    import torch
+    import paged_kv_decode_11_amd as pkd
+
+    spec, rng, b = workloads.workload("shared_prefix")
+    main, prefix, suffix = b["main"], b["prefix"], b["suffix"]
+    q = workloads.host_query(main, rng)
+    cache = workloads.host_cache(main, rng)
+    gu.say("shared_prefix composable (shared kernel)", main.batch, main.total_tokens)
+    qd, cd = gu.bits_to_dev(q), gu.bits_to_dev(cache)
+    # the prefix as one group of all 32 requests
+    n_pages = int(prefix.kv_indptr[1])
+    qo = np.array([0, main.batch], np.int32)
+    kv_indptr = np.array([0, n_pages], np.int32)
+    pages = torch.from_numpy(prefix.kv_indices[:n_pages].astype(np.int32)).cuda()
+    r = shared_runner(max_groups=4, max_batch=64, max_nnz=1 << 12)
+    r.plan(qo, kv_indptr, pages, prefix.kv_last_page_len[:1], 32, 8, 128, 16)
+    o_p, l_p = r.run(qd, cd, return_lse=True)
+    o_s, l_s = gu.decode(suffix, qd, cd, r=gu.runner(max_batch=64, max_nnz=1 << 12))
+    o, lse = pkd.merge_state(o_p, l_p, o_s, l_s)
+    torch.cuda.synchronize()
+    req = [0, 3, 7, 12, 18, 24, 29, 31]
+    o_ref, lse_ref = att.decode(q, cache, main.kv_indptr, main.kv_indices, main.kv_last_page_len,
+                                main.num_kv_heads, requests=req)
+    gu.assert_close(o, lse, o_ref, lse_ref, requests=req, label="composable-shared-kernel")
