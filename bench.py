@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_step",
-                    choices=["llama8b_step", "skewed", "wide_gqa", "token_sparse", "tiny"])
+                    choices=["llama8b_step", "skewed", "wide_gqa", "token_sparse", "tiny",
+                             "shared_prefix"])
     ap.add_argument("--slots", type=int, default=0, help="persistent workgroups (0 = default)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="oracle time budget for cpu_baseline (0 disables)")
@@ -146,6 +147,159 @@ def calibrate_copy(mib: int) -> None:
                       "copies": 5, "gbs_read_plus_write": round(2 * n / dt / 1e9, 1)}), flush=True)
 
 
+def time_graph(fn, steps: int, warmup: int, before=None) -> float:
+    """ms per replay of a graph holding fn(); `before` runs on the host ahead
+    of each replay (a plan)."""
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        fn()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        if before:
+            before()
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        if before:
+            before()
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del g
+    return ms
+
+
+def bench_shared_prefix(args):
+    """32 requests over one 8192-token prefix plus their own suffixes, one
+    layer, caches rotated over R copies.  Composable: the prefix state of all
+    requests from one shared-prefix plan (the prefix read once per KV head),
+    the suffix states from a decode plan, merged row by row.  Single format:
+    one decode plan over each request's prefix + suffix pages.  `value` is
+    the KV bytes the composable step streams (prefix once, suffixes) over its
+    time."""
+    import numpy as np
+    import torch
+
+    import paged_kv_decode_11_amd as pkd
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    spec, rng, b = workloads.workload("shared_prefix")
+    main, prefix, suffix = b["main"], b["prefix"], b["suffix"]
+    kv_tok = main.kv_bytes_per_token()
+    n_prefix_pages = int(prefix.kv_indptr[1])
+    prefix_tokens = int(prefix.kv_lens[0])
+    unique_bytes = (prefix_tokens + suffix.total_tokens) * kv_tok
+    single_bytes = main.total_tokens * kv_tok
+    R = 8  # cache copies: R x unique bytes well above the last-level cache
+    log(f"shared_prefix: B={main.batch} prefix={prefix_tokens} suffix tokens={suffix.total_tokens} "
+        f"unique {unique_bytes / 1e6:.1f} MB, single-format {single_bytes / 1e6:.1f} MB, R={R}")
+    base = workloads.device_cache(main, spec.seed * 1000, dev, used_only=True)
+    caches = [base] + [base.clone() for _ in range(R - 1)]
+    qs = [workloads.device_query(main, spec.seed * 7919 + j, dev) for j in range(R)]
+    H = main.num_qo_heads
+
+    # single format
+    r1 = pkd.DecodePlanRun(max_batch=main.batch, max_nnz=main.nnz, max_qo_heads=H, device=0)
+    idx_main = torch.from_numpy(main.kv_indices.astype(np.int32)).to(dev)
+    outs1 = [torch.empty_like(qs[0]) for _ in range(R)]
+    lses1 = [torch.empty((main.batch, H), dtype=torch.float32, device=dev) for _ in range(R)]
+
+    def plan1():
+        r1.plan(main.kv_indptr, idx_main, main.kv_last_page_len, H, main.num_kv_heads, 128, 16)
+
+    def run1():
+        for j in range(R):
+            r1.run(qs[j], caches[j], out=outs1[j], lse=lses1[j])
+
+    # composable
+    rp = pkd.SharedPlanRun(4, main.batch, n_prefix_pages, H, main.num_kv_heads, device=0)
+    rs = pkd.DecodePlanRun(max_batch=suffix.batch, max_nnz=suffix.nnz, max_qo_heads=H, device=0)
+    qo = np.array([0, main.batch], np.int32)
+    kv_indptr = np.array([0, n_prefix_pages], np.int32)
+    idx_pre = torch.from_numpy(prefix.kv_indices[:n_prefix_pages].astype(np.int32)).to(dev)
+    idx_suf = torch.from_numpy(suffix.kv_indices.astype(np.int32)).to(dev)
+    op = [torch.empty_like(qs[0]) for _ in range(R)]
+    lp = [torch.empty((main.batch, H), dtype=torch.float32, device=dev) for _ in range(R)]
+    os_ = [torch.empty_like(qs[0]) for _ in range(R)]
+    ls = [torch.empty((main.batch, H), dtype=torch.float32, device=dev) for _ in range(R)]
+    outs2 = [torch.empty_like(qs[0]) for _ in range(R)]
+    lses2 = [torch.empty((main.batch, H), dtype=torch.float32, device=dev) for _ in range(R)]
+
+    def plan2():
+        rp.plan(qo, kv_indptr, idx_pre, prefix.kv_last_page_len[:1], H, main.num_kv_heads, 128, 16)
+        rs.plan(suffix.kv_indptr, idx_suf, suffix.kv_last_page_len, H, main.num_kv_heads, 128, 16)
+
+    def run2():
+        for j in range(R):
+            rp.run(qs[j], caches[j], out=op[j], lse=lp[j])
+            rs.run(qs[j], caches[j], out=os_[j], lse=ls[j])
+            pkd.merge_state(op[j], lp[j], os_[j], ls[j], out=outs2[j], lse_out=lses2[j])
+
+    plan1()
+    plan2()
+    run1()
+    run2()
+    torch.cuda.synchronize()
+    # the two formats agree (both are checked against the oracle by the tests)
+    diff = max(float((outs1[j].float() - outs2[j].float()).abs().max()) for j in range(R))
+    dlse = max(float((lses1[j] - lses2[j]).abs().max()) for j in range(R))
+    log(f"formats agree: max |o1 - o2| {diff:.3g}, max |lse1 - lse2| {dlse:.3g}")
+
+    # per-kernel time of the shared-prefix kernel (eager, HIP events)
+    rp.profile_enable(True)
+    for _ in range(args.steps):
+        plan2()
+        run2()
+    torch.cuda.synchronize()
+    pre_ms, pre_merge_ms, runs = rp.profile_read()
+    rp.profile_enable(False)
+    prefix_us = pre_ms * 1e3 / runs
+    prefix_merge_us = pre_merge_ms * 1e3 / runs
+
+    ms1 = time_graph(run1, args.steps, args.warmup, plan1)
+    ms2 = time_graph(run2, args.steps, args.warmup, plan2)
+    us1, us2 = ms1 * 1e3 / R, ms2 * 1e3 / R
+    value = unique_bytes * R / (ms2 / 1e3) / 1e9
+    prefix_bytes = prefix_tokens * kv_tok
+    achieved = prefix_bytes / (prefix_us / 1e6) / 1e9
+    log(f"single format {us1:.1f} us/layer, composable {us2:.1f} us/layer "
+        f"(prefix kernel {prefix_us:.1f} us + its merge {prefix_merge_us:.1f} us)")
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms2, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/K/V, seeded lengths and page placement)",
+        "config": {"workload": "shared_prefix", "batch": main.batch, "layers": R,
+                   "prefix_tokens": prefix_tokens, "suffix_tokens": suffix.total_tokens,
+                   "num_qo_heads": H, "num_kv_heads": main.num_kv_heads, "head_dim": 128,
+                   "page_size": 16, "slots": rp.num_slots, "parallelism": "single GPU"},
+        "us_per_layer_step": round(us2, 2),
+        "frac_of_hbm_peak": round(value / PEAK_HBM_GBS, 4),
+        "composable_us_per_layer": round(us2, 2),
+        "single_format_us_per_layer": round(us1, 2),
+        "speedup_over_single_format": round(us1 / us2, 2),
+        "unique_kv_bytes_per_layer": unique_bytes,
+        "single_format_kv_bytes_per_layer": single_bytes,
+        "single_format_kv_gbs": round(single_bytes * R / (ms1 / 1e3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "prefix_mfma_kernel", "avg_launch_us": round(prefix_us, 2),
+                     "algorithmic_bytes_per_launch": prefix_bytes,
+                     "merge_avg_launch_us": round(prefix_merge_us, 2)},
+        "formats_max_abs_diff": {"o": diff, "lse": dlse},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -155,6 +309,9 @@ def main():
         print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU sharding is a design "
                                    "note only (see the design document)", "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.workload == "shared_prefix":
+        bench_shared_prefix(args)
+        return
     import numpy as np
     import torch
 

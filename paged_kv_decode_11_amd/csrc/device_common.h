@@ -111,6 +111,15 @@ __device__ __forceinline__ uint32_t load_stream4(const void* ptr) {
 // Cache-policy operand of the raw buffer load builtins selecting "nt".
 constexpr int kBufferNontemporal = 2;
 
+// Workgroup barrier for hand-offs through LDS: orders LDS accesses around
+// the barrier without waiting for the wave's outstanding global loads, as a
+// full __syncthreads() would (which would drain any prefetch in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // A page id outside [0, num_pages) is replaced by page 0 and remembered.
 __device__ __forceinline__ int64_t safe_page(int32_t id, int64_t num_pages, int& bad) {
   const bool ok = id >= 0 && id < num_pages;

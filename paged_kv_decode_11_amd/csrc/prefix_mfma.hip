@@ -13,20 +13,22 @@
 // One workgroup (8 waves) takes one item: one KV head of one (group, row
 // block, chunk).  Wave w owns 16 query rows, 16 / g requests times the g
 // query heads of the KV head, so the workgroup covers 128 / g requests.
-// Per 16-token tile:
-//   * the 512 lanes load the head's K and V rows of the tile (16 rows x 256
-//     bytes each, one 16-byte piece per lane) into registers, kDepth tiles
-//     ahead, and stage them in LDS: K row-major with its 16-byte pieces
-//     rotated by XOR of the row, V transposed to [d][token];
-//   * S^T = K Q^T on the matrix cores (v_mfma_f32_16x16x32_bf16, K from LDS
-//     as the A operand, the wave's q rows as B), which leaves lane l with the
-//     logits of query row l & 15 for tokens 4 (l >> 4) .. +3;
-//   * the online softmax per query row: a max over those 4 tokens and over
+// Per 32-token tile (two 16-token halves, each within one page):
+//   * every lane loads one 16-byte piece of one K row and of one V row of
+//     the head (32 rows x 256 bytes each), kDepth tiles ahead, and stages
+//     them in LDS row-major, the 16-byte pieces of row r rotated by XOR r;
+//   * S^T = K Q^T on the matrix cores (v_mfma_f32_16x16x32_bf16 per half, K
+//     from LDS as the A operand, the wave's q rows as B), which leaves lane l
+//     with the logits of query row l & 15 for tokens 4 (l >> 4) .. +3 of each
+//     half;
+//   * the online softmax per query row: a max over those 8 tokens and over
 //     the 4 lanes holding the same row (permlane swaps), exponentials in base
 //     2;
-//   * O += P V on the matrix cores (v_mfma_f32_16x16x16_bf16, P as bf16
-//     straight from the softmax registers as the A operand, V^T from LDS as
-//     B), 8 column blocks of 16 elements of head_dim.
+//   * O += P V on the matrix cores (v_mfma_f32_16x16x32_bf16, 32 tokens per
+//     instruction, 8 column blocks of 16 elements of head_dim): P as bf16
+//     straight from the softmax registers is the A operand, and the
+//     transposing LDS read (ds_read_b64_tr_b16) gives each lane the B operand
+//     of its column: 4 consecutive tokens of each half.
 // The rescale factors and the final max and sum move from "row l & 15" to the
 // accumulator's "rows 4 (l >> 4) + v" layout through a per-wave LDS row.
 
@@ -48,24 +50,28 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kDepth = 8;       // tiles in flight per workgroup
-constexpr int kVtStride = 20;   // bf16 per head_dim row of the transposed V tile (16 + pad)
+constexpr int kTile = 32;   // tokens per tile (two halves of 16)
+constexpr int kDepth = 8;   // tiles in flight per workgroup
 
 struct PShared {
-  uint4 kt[2][16][16];                   // K tile: row r's 16-byte piece c at [r][c ^ r]
-  uint16_t vt[2][kHeadDim * kVtStride];  // V tile transposed: [d][token]
-  float xa[kWaves][16];                  // per wave, per query row: rescale factor, then max
-  float xl[kWaves][16];                  // per wave, per query row: final sum
+  uint4 k[2][kTile][16];  // K tile, row r's 16-byte piece c at [r][c ^ (r & 15)]
+  uint4 v[2][kTile][16];  // V tile, same layout
+  float xa[kWaves][16];   // per wave, per query row: rescale factor, then max
+  float xl[kWaves][16];   // per wave, per query row: final sum
 };
 
-__device__ __forceinline__ floatx4_t mfma_kq(uint4 a, uint4 b, floatx4_t c) {
+__device__ __forceinline__ floatx4_t mfma32(uint4 a, uint4 b, floatx4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ floatx4_t mfma_pv(uint2 a, uint2 b, floatx4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a),
-                                                   __builtin_bit_cast(short4_t, b), c, 0, 0, 0);
+// Transposing LDS read: for the 16 lanes of a row group, lane i receives
+// element i % 4 of the 8-byte piece addressed by lane 4 r + i / 4 of its
+// group, for r = 0..3.
+__device__ __forceinline__ uint2 lds_read_tr(const void* p) {
+  typedef __attribute__((address_space(3))) short4_t lds_short4;
+  const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p));
+  return __builtin_bit_cast(uint2, v);
 }
 
 template <int G, int P>
@@ -75,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
     float* __restrict__ fws, int32_t* __restrict__ err, int64_t num_pages, float scale_log2,
     int num_qo_heads, int num_kv_heads) {
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
-  static_assert(P % 16 == 0, "a 16-token tile must lie in one page");
+  static_assert(P % 16 == 0, "a 16-token half tile must lie in one page");
   constexpr int kReqPerWave = 16 / G;
   __shared__ PShared sh;
 
@@ -84,10 +90,11 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row16 = lane & 15;
   const int kg = lane >> 4;
-  // load role: half of the lanes move K, half V; 16 lanes per 256-byte row
-  const int ld_v = tid >> 8;
-  const int ld_row = (tid >> 4) & 15;
+  // load role: tile row tid >> 4 (0..31, half tid >> 8), 16-byte piece tid & 15
+  const int ld_row = tid >> 4;
+  const int ld_half = tid >> 8;
   const int ld_piece = tid & 15;
+  const int ld_slot = ld_piece ^ (ld_row & 15);
 
   const int32_t* hdr = ws + PKD_HEADER_BASE;
   const int num_slots = gridDim.x;
@@ -119,8 +126,9 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
     const int row0 = groups[4 * grp + 0];
     const int rows = groups[4 * grp + 1];
     const int kchunks = groups[4 * grp + 2];
-    const int ntiles = (len + 15) >> 4;
-    const int last_valid = len - 16 * (ntiles - 1);
+    const int ntiles = (len + kTile - 1) / kTile;
+    const int last_valid = len - kTile * (ntiles - 1);
+    const int last_token = len - 1;
 
     // this wave's requests: first row (group-relative) and count
     const int wrow = block * rows_per_block + wave * kReqPerWave;
@@ -146,87 +154,126 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) acc[cb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    // this lane's piece of tile t
-    auto tile_addr = [&](int t) -> const uint4* {
-      const int64_t pg = safe_page(idx[(16 * t) / P], num_pages, bad);
-      const uint64_t off = uint64_t(pg) * page_bytes + (ld_v ? v_bytes : 0) +
-                           uint64_t((16 * t) % P + ld_row) * row_bytes +
+    // This lane's token of tile t (clamped to the chunk: rows past its end
+    // repeat the last token; they are masked, and V of those rows is zeroed
+    // when staged) and the page id of that token.
+    auto token_of = [&](int t) { return min(kTile * t + ld_row, last_token); };
+    // (threadIdx.y is 0 in this one-dimensional launch; adding it makes the
+    // page-id load a per-lane one, so its wait sits where the id is used)
+    auto page_of = [&](int t) -> int32_t { return idx[token_of(t) / P + int(threadIdx.y)]; };
+    auto piece_addr = [&](int t, int32_t id) -> const uint4* {
+      const int64_t pg = safe_page(id, num_pages, bad);
+      const uint64_t off = uint64_t(pg) * page_bytes + uint64_t(token_of(t) % P) * row_bytes +
                            uint64_t(kh) * kHeadDim * 2 + uint64_t(ld_piece) * 16;
       return reinterpret_cast<const uint4*>(kv + off);
     };
 
-    uint4 ring[kDepth];
+    // Ring of kDepth tiles in registers (K and V piece per lane) and the page
+    // ids of the tiles each slot loads next.  Loads are issued
+    // unconditionally and in the same order in the prologue and the loop
+    // (tile, then a page id), so every wait is for one specific older load.
+    uint4 rk[kDepth], rv[kDepth];
+    int32_t pid[kDepth];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) pid[d] = page_of(min(d, ntiles - 1));
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const uint4* a = piece_addr(min(d, ntiles - 1), pid[d]);
+      rk[d] = load_stream16(a);
+      rv[d] = load_stream16(reinterpret_cast<const char*>(a) + v_bytes);
+      pid[d] = page_of(min(d + kDepth, ntiles - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    auto step = [&](uint4& sk, uint4& sv, int32_t& next_page, int n, bool reload) {
+      const int stage = n & 1;
+      const bool last = n == ntiles - 1;
+      const int valid = last ? last_valid : kTile;
+      // stage tile n; V rows past the valid ones are zero (a zero probability
+      // must not meet a repeated or NaN value)
+      sh.k[stage][ld_row][ld_slot] = sk;
+      sh.v[stage][ld_row][ld_slot] = ld_row < valid ? sv : make_uint4(0u, 0u, 0u, 0u);
+      lds_barrier();
+      if (reload) {
+        const int32_t page = next_page;
+        const uint4* a = piece_addr(min(n + kDepth, ntiles - 1), page);
+        sk = load_stream16(a);
+        sv = load_stream16(reinterpret_cast<const char*>(a) + v_bytes);
+        next_page = page_of(min(n + 2 * kDepth, ntiles - 1));
+      }
+      if (!compute) return;
+
+      // S^T = K Q^T per half: lane l gets query row l & 15, tokens
+      // 16 h + 4 kg + v
+      floatx4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s0 = mfma32(sh.k[stage][row16][(4 * j + kg) ^ row16], qv[j], s0);
+        s1 = mfma32(sh.k[stage][16 + row16][(4 * j + kg) ^ row16], qv[j], s1);
+      }
+      float sc[8];
+      float mx = kNegInf;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        sc[v] = (4 * kg + v < valid) ? s0[v] * scale_log2 : kNegInf;
+        sc[4 + v] = (16 + 4 * kg + v < valid) ? s1[v] * scale_log2 : kNegInf;
+      }
+#pragma unroll
+      for (int v = 0; v < 8; ++v) mx = fmaxf(mx, sc[v]);
+      const float mn = fmaxf(m, rows_max(mx));
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 while m = -inf
+      float p[8];
+      float ps = 0.f;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        p[v] = __builtin_amdgcn_exp2f(sc[v] - mn);
+        ps += p[v];
+      }
+      lsum = fmaf(lsum, alpha, ps);
+      m = mn;
+      // rescale factors to the accumulator's row layout (rows 4 kg + v)
+      if (kg == 0) sh.xa[wave][row16] = alpha;
+      __builtin_amdgcn_wave_barrier();
+      const float4 a4 = *reinterpret_cast<const float4*>(&sh.xa[wave][4 * kg]);
+      __builtin_amdgcn_wave_barrier();
+      // P as the A operand: k = 8 kg + j <-> token 4 kg + j (j < 4) of the
+      // first half and 16 + 4 kg + j - 4 of the second
+      const uint4 pa = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                  pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+      // B operand of column block cb: lane (kg, i = 4 r + q) points the
+      // transposing read at row 4 kg + r, elements cb 16 + 4 q .. + 3 of each
+      // half
+      const int tr_row = 4 * kg + (row16 >> 2);
+      const int tr_q = row16 & 3;
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) {
+        const int piece = 2 * cb + (tr_q >> 1);
+        const char* r0 = reinterpret_cast<const char*>(&sh.v[stage][tr_row][piece ^ tr_row]) +
+                         8 * (tr_q & 1);
+        const char* r1 =
+            reinterpret_cast<const char*>(&sh.v[stage][16 + tr_row][piece ^ tr_row]) +
+            8 * (tr_q & 1);
+        const uint2 b0 = lds_read_tr(r0);
+        const uint2 b1 = lds_read_tr(r1);
+        acc[cb][0] *= a4.x;
+        acc[cb][1] *= a4.y;
+        acc[cb][2] *= a4.z;
+        acc[cb][3] *= a4.w;
+        acc[cb] = mfma32(pa, make_uint4(b0.x, b0.y, b1.x, b1.y), acc[cb]);
+      }
+    };
+
+    // Whole rounds of kDepth tiles always reload (past the end, the last
+    // tile again), so every round leaves the same loads in flight; the
+    // partial round after them does not reload.
+    const int full = ntiles / kDepth;
+    for (int r = 0; r < full; ++r) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) step(rk[d], rv[d], pid[d], r * kDepth + d, true);
+    }
 #pragma unroll
     for (int d = 0; d < kDepth; ++d)
-      if (d < ntiles) ring[d] = load_stream16(tile_addr(d));
-
-    for (int n0 = 0; n0 < ntiles; n0 += kDepth) {
-#pragma unroll
-      for (int d = 0; d < kDepth; ++d) {
-        const int n = n0 + d;
-        if (n >= ntiles) break;
-        const int stage = n & 1;
-        const bool last = n == ntiles - 1;
-        const int valid = last ? last_valid : 16;
-        // stage tile n in LDS; rows past the valid ones hold zeros in V (a
-        // zero probability must not meet a stale or NaN value)
-        if (!ld_v) {
-          sh.kt[stage][ld_row][ld_piece ^ ld_row] = ring[d];
-        } else {
-          const uint4 w = ld_row < valid ? ring[d] : make_uint4(0u, 0u, 0u, 0u);
-          const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-          uint16_t* col = sh.vt[stage] + (ld_piece * 8) * kVtStride + ld_row;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            col[(2 * e) * kVtStride] = uint16_t(ww[e] & 0xffffu);
-            col[(2 * e + 1) * kVtStride] = uint16_t(ww[e] >> 16);
-          }
-        }
-        __syncthreads();
-        if (n + kDepth < ntiles) ring[d] = load_stream16(tile_addr(n + kDepth));
-        if (!compute) continue;
-
-        // S^T = K Q^T: lane l gets query row l & 15, tokens 4 kg + v
-        floatx4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          s = mfma_kq(sh.kt[stage][row16][(4 * j + kg) ^ row16], qv[j], s);
-        float sv[4];
-        float mx = kNegInf;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          sv[v] = (4 * kg + v < valid) ? s[v] * scale_log2 : kNegInf;
-          mx = fmaxf(mx, sv[v]);
-        }
-        const float mn = fmaxf(m, rows_max(mx));
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 while m = -inf
-        float p[4];
-        float ps = 0.f;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          p[v] = __builtin_amdgcn_exp2f(sv[v] - mn);
-          ps += p[v];
-        }
-        lsum = fmaf(lsum, alpha, ps);
-        m = mn;
-        // rescale factors to the accumulator's row layout (rows 4 kg + v)
-        if (kg == 0) sh.xa[wave][row16] = alpha;
-        __builtin_amdgcn_wave_barrier();
-        const float4 a4 = *reinterpret_cast<const float4*>(&sh.xa[wave][4 * kg]);
-        __builtin_amdgcn_wave_barrier();
-        const uint2 pa = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
-        const uint16_t* vcol = sh.vt[stage] + row16 * kVtStride + 4 * kg;
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) {
-          acc[cb][0] *= a4.x;
-          acc[cb][1] *= a4.y;
-          acc[cb][2] *= a4.z;
-          acc[cb][3] *= a4.w;
-          const uint2 vb = *reinterpret_cast<const uint2*>(vcol + cb * 16 * kVtStride);
-          acc[cb] = mfma_pv(pa, vb, acc[cb]);
-        }
-      }
-    }
+      if (full * kDepth + d < ntiles) step(rk[d], rv[d], pid[d], full * kDepth + d, false);
 
     if (compute) {
       // final per-row max and sum, to the accumulator's row layout
@@ -257,16 +304,16 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
             orow[cb * 16] = uint16_t(pack_bf16x2(acc[cb][v] * inv, 0.f) & 0xffffu);
           if (lse_ptr && row16 == 0) lse_ptr[(int64_t(row0) + req_in_group) * Hq + qh] = lse_nat;
         } else {
-          const int64_t pid = int64_t(out) + int64_t(req_in_group) * kchunks;
-          float* prow = o_part + (pid * Hq + qh) * kHeadDim + row16;
+          const int64_t pid_out = int64_t(out) + int64_t(req_in_group) * kchunks;
+          float* prow = o_part + (pid_out * Hq + qh) * kHeadDim + row16;
 #pragma unroll
           for (int cb = 0; cb < 8; ++cb) prow[cb * 16] = acc[cb][v] * inv;
-          if (row16 == 0) lse_part[pid * Hq + qh] = lse_nat;
+          if (row16 == 0) lse_part[pid_out * Hq + qh] = lse_nat;
         }
       }
     }
     // the next item's first tile reuses LDS stage 0
-    __syncthreads();
+    lds_barrier();
   }
   if (bad && lane == 0) err[0] = PKD_DEVERR_PAGE_ID;
 }
