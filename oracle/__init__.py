@@ -10,7 +10,10 @@ What it computes, in float64 with numpy:
   disjoint key sets;
 * ``plan_ref``    -- the split-KV work schedule (chunking, longest-first
   assignment to a fixed number of workgroups, reduction map) that the
-  library's host planner must reproduce bit for bit.
+  library's host planner must reproduce bit for bit, for decode plans and
+  shared-prefix (composable) plans;
+* ``append``      -- writing new tokens' K and V rows into their page slots,
+  and the request / position of every new token.
 
 Sources: the three FlashInfer pages (aicassindra "FlashInfer, in depth";
 pyshine "FlashInfer" source tour; pinghaoyang "FlashInfer 完全拆解").  Each
@@ -27,4 +30,4 @@ scaled_dot_product_attention in float64) or brute force.  No function is
 "parity unpinned".
 """
 
-from . import attention, merge, page_table, plan_ref  # noqa: F401
+from . import append, attention, merge, page_table, plan_ref  # noqa: F401
