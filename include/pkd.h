@@ -296,6 +296,38 @@ int pkd_run(pkd_handle* h, const void* q, int32_t batch, const void* kv_cache,
  * the last read (PKD_DEVERR_*, 0 if none) and clears them. */
 int pkd_read_device_error(pkd_handle* h, int32_t* flags, pkd_stream_t stream);
 
+/* ------------------------------- append ------------------------------- */
+
+/* The step before decode (pyshine, "The Paged KV Cache Layer"): copy new
+ * tokens' K and V rows into their page slots.  All arrays are device arrays.
+ *
+ * pkd_append_positions: for request i (batch requests), the new tokens
+ * append_indptr[i] .. append_indptr[i+1]-1 (int32 [batch+1]) are its last
+ * a_i tokens, a_i = append_indptr[i+1] - append_indptr[i]; writes, for each
+ * new token, batch_indices[t] = i and positions[t] = L_i - a_i + j, where L_i
+ * = page_size (n_i - 1) + kv_last_page_len[i] is the request's length in the
+ * page table that already covers the new tokens.
+ *
+ * pkd_append_paged_kv: new token t (nnz_append of them) with K and V rows
+ * k_new[t], v_new[t] (bf16 [nnz_append, num_kv_heads, head_dim], contiguous)
+ * goes to request batch_indices[t] at sequence position positions[t], i.e.
+ * page kv_indices[kv_indptr[b] + pos / page_size], slot pos % page_size of
+ * kv_cache ([num_pages, 2, page_size, num_kv_heads, head_dim], NHD bf16).  A
+ * token whose request, position or page id is out of range is not written
+ * and sets *device_error (an int32 on the device, may be NULL) to
+ * PKD_DEVERR_PAGE_ID.  Only bf16, NHD and head_dim 128 are built
+ * (PKD_ERR_UNSUPPORTED otherwise).  Asynchronous on `stream`; tokens must
+ * not share a slot (the order of such writes is not defined). */
+int pkd_append_positions(const int32_t* append_indptr, const int32_t* kv_indptr,
+                         const int32_t* kv_last_page_len, int32_t batch, int32_t page_size,
+                         int32_t* batch_indices, int32_t* positions, pkd_stream_t stream);
+int pkd_append_paged_kv(const void* k_new, const void* v_new, const int32_t* batch_indices,
+                        const int32_t* positions, int64_t nnz_append, const int32_t* kv_indptr,
+                        const int32_t* kv_indices, int32_t batch, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t page_size, int32_t kv_dtype,
+                        int32_t kv_layout, void* kv_cache, int64_t num_pages,
+                        int32_t* device_error, pkd_stream_t stream);
+
 /* -------------------------------- merge ------------------------------- */
 
 /* Merge two attention states row by row: for each of n*H rows,

@@ -13,6 +13,8 @@ from ._lib import PkdError, header_functions, load  # noqa: F401
 from .api import (  # noqa: F401
     DecodePlanRun,
     SharedPlanRun,
+    append_paged_kv_cache,
+    append_positions,
     float_workspace_bytes,
     host_workspace_bytes,
     int_workspace_bytes,

@@ -81,6 +81,9 @@ SIGNATURES = {
     "pkd_shared_workspace_bytes": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                                   ctypes.POINTER(_sz), ctypes.POINTER(_sz),
                                                   ctypes.POINTER(_sz)]),
+    "pkd_append_positions": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp]),
+    "pkd_append_paged_kv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _i32,
+                                           _i32, _i32, _i32, _vp, _i64, _vp, _vp]),
     "pkd_run": (ctypes.c_int, [_vp, _vp, _i32, _vp, _i64, _i32, _i32, _vp, _vp, ctypes.c_float,
                                _vp]),
     "pkd_read_device_error": (ctypes.c_int, [_vp, _pi32, _vp]),

@@ -322,3 +322,43 @@ class SharedPlanRun(DecodePlanRun):
         self._planned = (int(qo[-1]), num_qo_heads, head_dim)
         self._keep = kv_indices
 
+
+def append_positions(append_indptr, kv_indptr, kv_last_page_len, page_size, stream=None):
+    """Request and sequence position of every new token (device int32
+    tensors in, device int32 tensors out); see pkd_append_positions."""
+    import torch
+
+    for t in (append_indptr, kv_indptr, kv_last_page_len):
+        if not (t.is_cuda and t.dtype == torch.int32 and t.is_contiguous()):
+            raise ValueError("append_positions needs contiguous int32 GPU tensors")
+    batch = kv_last_page_len.shape[0]
+    nnz = int(append_indptr[-1].item())
+    b = torch.empty(nnz, dtype=torch.int32, device=append_indptr.device)
+    p = torch.empty(nnz, dtype=torch.int32, device=append_indptr.device)
+    if nnz:
+        check(_lib.load().pkd_append_positions(append_indptr.data_ptr(), kv_indptr.data_ptr(),
+                                               kv_last_page_len.data_ptr(), batch, page_size,
+                                               b.data_ptr(), p.data_ptr(), _stream_ptr(stream)))
+    return b, p
+
+
+def append_paged_kv_cache(k_new, v_new, batch_indices, positions, kv_cache, kv_indices, kv_indptr,
+                          device_error=None, stream=None):
+    """Write new tokens' K and V rows ([nnz, Hkv, 128] bf16 each) into the
+    paged cache [pages, 2, P, Hkv, 128] in place; see pkd_append_paged_kv."""
+    import torch
+
+    nnz, Hkv, D = k_new.shape
+    for t in (k_new, v_new, kv_cache):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("k_new, v_new and kv_cache must be contiguous GPU tensors")
+    for t in (batch_indices, positions, kv_indices, kv_indptr):
+        if not (t.is_cuda and t.dtype == torch.int32 and t.is_contiguous()):
+            raise ValueError("index arrays must be contiguous int32 GPU tensors")
+    check(_lib.load().pkd_append_paged_kv(
+        k_new.data_ptr(), v_new.data_ptr(), batch_indices.data_ptr(), positions.data_ptr(), nnz,
+        kv_indptr.data_ptr(), kv_indices.data_ptr(), kv_indptr.shape[0] - 1, Hkv, D,
+        kv_cache.shape[2], _dtype_code(kv_cache.dtype), _lib.PKD_LAYOUT_NHD, kv_cache.data_ptr(),
+        kv_cache.shape[0], device_error.data_ptr() if device_error is not None else None,
+        _stream_ptr(stream)))
+

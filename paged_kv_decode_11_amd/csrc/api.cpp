@@ -511,6 +511,47 @@ int pkd_read_device_error(pkd_handle* h, int32_t* flags, pkd_stream_t stream) {
   return PKD_OK;
 }
 
+int pkd_append_positions(const int32_t* append_indptr, const int32_t* kv_indptr,
+                         const int32_t* kv_last_page_len, int32_t batch, int32_t page_size,
+                         int32_t* batch_indices, int32_t* positions, pkd_stream_t stream) {
+  if (batch < 0 || page_size < 1)
+    return fail(PKD_ERR_INVALID_ARG, "batch must be >= 0 and page_size >= 1");
+  if (batch == 0) return PKD_OK;
+  if (!append_indptr || !kv_indptr || !kv_last_page_len || !batch_indices || !positions)
+    return fail(PKD_ERR_INVALID_ARG, "pkd_append_positions: null array");
+  hipError_t e = pkd::launch_append_positions(append_indptr, kv_indptr, kv_last_page_len, batch,
+                                              page_size, batch_indices, positions,
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKD_OK : hip_fail(e, "append positions kernel launch");
+}
+
+int pkd_append_paged_kv(const void* k_new, const void* v_new, const int32_t* batch_indices,
+                        const int32_t* positions, int64_t nnz_append, const int32_t* kv_indptr,
+                        const int32_t* kv_indices, int32_t batch, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t page_size, int32_t kv_dtype,
+                        int32_t kv_layout, void* kv_cache, int64_t num_pages,
+                        int32_t* device_error, pkd_stream_t stream) {
+  if (kv_dtype != PKD_DTYPE_BF16) return fail(PKD_ERR_UNSUPPORTED, "only bf16 KV is built");
+  if (kv_layout != PKD_LAYOUT_NHD) return fail(PKD_ERR_UNSUPPORTED, "only the NHD layout is built");
+  if (head_dim != pkd::kHeadDim) return fail(PKD_ERR_UNSUPPORTED, "only head_dim 128 is built");
+  if (nnz_append < 0 || batch < 1 || num_kv_heads < 1 || page_size < 1 || num_pages < 1)
+    return fail(PKD_ERR_INVALID_ARG, "invalid sizes for pkd_append_paged_kv");
+  if (nnz_append == 0) return PKD_OK;
+  if (!k_new || !v_new || !batch_indices || !positions || !kv_indptr || !kv_indices || !kv_cache)
+    return fail(PKD_ERR_INVALID_ARG, "pkd_append_paged_kv: null array");
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new) |
+       reinterpret_cast<uintptr_t>(kv_cache)) & 15)
+    return fail(PKD_ERR_INVALID_ARG, "k_new, v_new and kv_cache must be 16-byte aligned");
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "device query");
+  e = pkd::launch_append_kv(k_new, v_new, batch_indices, positions, nnz_append, kv_indptr,
+                            kv_indices, batch, num_kv_heads, page_size, kv_cache, num_pages,
+                            device_error, 8 * cus, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKD_OK : hip_fail(e, "append kernel launch");
+}
+
 int pkd_merge_state(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
                     int32_t n, int32_t H, int32_t D, void* o_out, float* lse_out,
                     pkd_stream_t stream) {

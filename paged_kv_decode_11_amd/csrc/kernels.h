@@ -66,6 +66,18 @@ hipError_t launch_plan_upload(const int32_t* image, int32_t* dst, int64_t image_
                               const int32_t* indices, int32_t* dst_indices, int64_t nnz,
                               hipStream_t stream);
 
+// New tokens' requests and positions, and their K/V rows into the paged
+// cache (append.hip).
+hipError_t launch_append_positions(const int32_t* append_indptr, const int32_t* kv_indptr,
+                                   const int32_t* kv_last_page_len, int batch, int page_size,
+                                   int32_t* batch_indices, int32_t* positions,
+                                   hipStream_t stream);
+hipError_t launch_append_kv(const void* k_new, const void* v_new, const int32_t* batch_indices,
+                            const int32_t* positions, int64_t nnz, const int32_t* kv_indptr,
+                            const int32_t* kv_indices, int batch, int num_kv_heads,
+                            int page_size, void* cache, int64_t num_pages, int32_t* err,
+                            int grid_cap, hipStream_t stream);
+
 // Merge of the split requests of the current plan (reads the plan image).
 hipError_t launch_merge_partials(const MergeParams& p, int grid, hipStream_t stream);
 // Merge of `k` bf16 states per row, rows laid out uniformly.
