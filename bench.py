@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_step",
                     choices=["llama8b_step", "skewed", "wide_gqa", "token_sparse", "tiny",
-                             "shared_prefix"])
+                             "shared_prefix", "append"])
     ap.add_argument("--slots", type=int, default=0, help="persistent workgroups (0 = default)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="oracle time budget for cpu_baseline (0 disables)")
@@ -300,6 +300,79 @@ def bench_shared_prefix(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_append(args):
+    """The append kernel on the Llama-3-8B-like batch's page table: every
+    token of the batch written at once (a prefill-sized append, about 1 GB
+    of K/V), and one new token per request (a decode step's append).  `value`
+    is the bytes the prefill-sized append moves (new rows read, cache slots
+    written) over its time."""
+    import numpy as np
+    import torch
+
+    import paged_kv_decode_11_amd as pkd
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    spec, rng, b = workloads.workload("llama8b_step")
+    batch = b["main"]
+    Hkv, P = batch.num_kv_heads, batch.page_size
+    row = Hkv * 128 * 2
+    cache = torch.zeros(batch.cache_shape(), dtype=torch.bfloat16, device=dev)
+    indptr = torch.from_numpy(batch.kv_indptr.astype(np.int32)).to(dev)
+    indices = torch.from_numpy(batch.kv_indices.astype(np.int32)).to(dev)
+    last = torch.from_numpy(batch.kv_last_page_len.astype(np.int32)).to(dev)
+    lens = batch.kv_lens.astype(np.int64)
+
+    def setup(add):
+        a_ind = torch.from_numpy(np.concatenate([[0], np.cumsum(add)]).astype(np.int32)).to(dev)
+        bi, pos = pkd.append_positions(a_ind, indptr, last, P)
+        n = int(np.sum(add))
+        k = workloads.device_query(batch, 11, dev).new_empty((n, Hkv, 128)).normal_()
+        v = torch.empty_like(k).normal_()
+        return bi, pos, k, v, n
+
+    def timed(bi, pos, k, v, steps):
+        run = lambda: pkd.append_paged_kv_cache(k, v, bi, pos, cache, indices, indptr)
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(steps):
+            run()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    bi, pos, k, v, n_full = setup(lens)
+    ms_full = timed(bi, pos, k, v, args.steps)
+    moved = 2 * (2 * n_full * row)  # K and V rows, read once and written once
+    value = moved / (ms_full / 1e3) / 1e9
+    del k, v
+    bi1, pos1, k1, v1, n1 = setup(np.ones_like(lens))
+    ms_one = timed(bi1, pos1, k1, v1, max(args.steps, 20))
+    log(f"append: {n_full} tokens in {ms_full * 1e3:.1f} us ({value:.0f} GB/s); "
+        f"one token per request ({n1}): {ms_one * 1e3:.2f} us")
+    line = {
+        "metric": "paged KV append: achieved GB/s (new rows read + cache slots written)",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_full, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 rows, the Llama-3-8B-like batch's page table)",
+        "config": {"workload": "append", "tokens": n_full, "batch": batch.batch,
+                   "num_kv_heads": Hkv, "head_dim": 128, "page_size": P,
+                   "parallelism": "single GPU"},
+        "decode_step_append_us": round(ms_one * 1e3, 2),
+        "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(value / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "append_kv_kernel", "avg_launch_us": round(ms_full * 1e3, 2),
+                     "algorithmic_bytes_per_launch": moved},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -311,6 +384,9 @@ def main():
         sys.exit(2)
     if args.workload == "shared_prefix":
         bench_shared_prefix(args)
+        return
+    if args.workload == "append":
+        bench_append(args)
         return
     import numpy as np
     import torch
