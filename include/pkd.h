@@ -155,6 +155,8 @@ enum {
   PKD_H_NUM_GROUPS,     /* shared-prefix plans: groups (KV rows) */
   PKD_H_OFF_GROUPS,     /* shared-prefix plans: group table */
   PKD_H_ROWS_PER_BLOCK, /* shared-prefix plans: requests per workgroup (128 / gqa) */
+  PKD_H_MIN_CHUNKS,     /* fewest partial states of a merge-list entry (0 if none) */
+  PKD_H_MAX_CHUNKS,     /* most partial states of a merge-list entry (0 if none) */
   PKD_H_COUNT
 };
 #define PKD_HEADER_BASE 32

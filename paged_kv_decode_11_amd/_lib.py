@@ -35,7 +35,7 @@ H_FIELDS = ["MAGIC", "VERSION", "BATCH", "QO_HEADS", "KV_HEADS", "HEAD_DIM", "PA
             "SLOTS", "CHUNK_PAGES", "ITEMS", "PARTIALS", "SPLIT", "ALPHA", "BETA", "NNZ",
             "PLAN_ID", "OFF_SLOTS", "OFF_ITEMS", "OFF_MERGE", "OFF_INDICES",
             "TOTAL_TOKENS_LO", "TOTAL_TOKENS_HI", "OFF_FIRST", "KIND", "NUM_GROUPS",
-            "OFF_GROUPS", "ROWS_PER_BLOCK"]
+            "OFF_GROUPS", "ROWS_PER_BLOCK", "MIN_CHUNKS", "MAX_CHUNKS"]
 H = {name: i for i, name in enumerate(H_FIELDS)}
 
 _STATUS_NAMES = {0: "PKD_OK", 1: "PKD_ERR_INVALID_ARG", 2: "PKD_ERR_UNSUPPORTED",

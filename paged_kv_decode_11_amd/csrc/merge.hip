@@ -144,7 +144,58 @@ __device__ void merge_task(const MergeParams& p, const Task& t, int h, float* gr
   __syncthreads();
 }
 
+// A task of at most kSmallK fp32 states done by one group of 32 lanes: all
+// its states loaded at once, then folded in order.
+constexpr int kSmallK = 16;
+
+__device__ void merge_small(const MergeParams& p, const Task& t, int h, int gl) {
+  const float* o_in = static_cast<const float*>(p.o_in);
+  float L[kSmallK];
+  float4 v[kSmallK];
+#pragma unroll
+  for (int c = 0; c < kSmallK; ++c) {
+    L[c] = kNegInf;
+    v[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < t.k) {
+      const int64_t st = t.first + c;
+      L[c] = p.lse_in[st * p.lse_stride_c + h];
+      v[c] = load4(o_in + st * p.o_stride_c + int64_t(h) * kHeadDim + gl * 4);
+    }
+  }
+  float M = kNegInf;
+#pragma unroll
+  for (int c = 0; c < kSmallK; ++c) M = fmaxf(M, L[c]);
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float lse = kNegInf;
+  if (M != kNegInf) {
+    float S = 0.f;
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int c = 0; c < kSmallK; ++c) {
+      const float w = __builtin_amdgcn_exp2f((L[c] - M) * kLog2e);  // 0 past k
+      S += w;
+      A.x = fmaf(w, v[c].x, A.x);
+      A.y = fmaf(w, v[c].y, A.y);
+      A.z = fmaf(w, v[c].z, A.z);
+      A.w = fmaf(w, v[c].w, A.w);
+    }
+    const float inv = 1.f / S;
+    o = make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
+    lse = M + __log2f(S) * kLn2;
+  }
+  uint2 w;
+  w.x = pack_bf16x2(o.x, o.y);
+  w.y = pack_bf16x2(o.z, o.w);
+  *reinterpret_cast<uint2*>(p.o_out + (t.out_row * p.H + h) * kHeadDim + gl * 4) = w;
+  if (p.lse_out && gl == 0) p.lse_out[t.out_row * p.H + h] = lse;
+}
+
 // Split requests of the current plan: fp32 partials in the float workspace.
+// Tasks (split request e, q head h) = e H + h form blocks of 8.  A block where
+// no task has more than kSmallK states is one work unit: each group of 32
+// lanes does one of its tasks in a single round trip to memory.  The tasks of
+// the other blocks are work units of their own, done with all 256 lanes
+// (merge_task), so a few long tasks still spread over many workgroups.
 __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(MergeParams p) {
   __shared__ float grp_m[8];
   __shared__ float grp_s[8];
@@ -157,14 +208,41 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(MergePara
   MergeParams q = p;
   q.lse_in = static_cast<const float*>(p.o_in) + n_partials * H * kHeadDim;
   const int tasks = n_split * H;
-  for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+  const int blocks = (tasks + 7) / 8;
+  const int grp = threadIdx.x >> 5;
+  const int gl = threadIdx.x & 31;
+  auto task_of = [&](int task) {
     const int e = task / H;
-    const int h = task - e * H;
     Task t;
     t.out_row = merges[4 * e + 0];
     t.first = merges[4 * e + 1];
     t.k = merges[4 * e + 2];
-    merge_task<float>(q, t, h, grp_m, grp_s, grp_acc);
+    return t;
+  };
+  auto small_block = [&](int blk) {
+    int kmax = 0;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int task = 8 * blk + g;
+      if (task < tasks) kmax = max(kmax, merges[4 * (task / H) + 2]);
+    }
+    return kmax <= kSmallK;
+  };
+  // the plan's fewest and most states per entry tell which passes have work
+  const bool some_small = hdr[PKD_H_MIN_CHUNKS] <= kSmallK;
+  const bool some_large = hdr[PKD_H_MAX_CHUNKS] > kSmallK;
+  if (some_small) {
+    for (int blk = blockIdx.x; blk < blocks; blk += gridDim.x) {
+      if (some_large && !small_block(blk)) continue;
+      const int task = 8 * blk + grp;
+      if (task < tasks) merge_small(q, task_of(task), task % H, gl);
+    }
+  }
+  if (some_large) {
+    for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+      if (some_small && small_block(task / 8)) continue;
+      merge_task<float>(q, task_of(task), task % H, grp_m, grp_s, grp_acc);
+    }
   }
 }
 

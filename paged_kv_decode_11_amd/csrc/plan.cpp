@@ -278,6 +278,13 @@ int plan_build(const PlanInput& in, PlanScratch& s, int32_t* image, int64_t imag
   hdr[PKD_H_NUM_GROUPS] = layout->num_groups;
   hdr[PKD_H_OFF_GROUPS] = int32_t(layout->off_groups);
   hdr[PKD_H_ROWS_PER_BLOCK] = layout->rows_per_block;
+  int32_t kmin = 0, kmax = 0;
+  for (const PlanMerge& m : s.merges) {
+    kmin = kmin == 0 ? m.k : std::min(kmin, m.k);
+    kmax = std::max(kmax, m.k);
+  }
+  hdr[PKD_H_MIN_CHUNKS] = kmin;
+  hdr[PKD_H_MAX_CHUNKS] = kmax;
 
   int32_t* slot_indptr = image + layout->off_slots;
   for (int32_t q = 0; q <= S; ++q) slot_indptr[q] = 0;
