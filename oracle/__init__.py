@@ -13,7 +13,10 @@ What it computes, in float64 with numpy:
   library's host planner must reproduce bit for bit, for decode plans and
   shared-prefix (composable) plans;
 * ``append``      -- writing new tokens' K and V rows into their page slots,
-  and the request / position of every new token.
+  and the request / position of every new token;
+* ``fp8``         -- FP8 E4M3 cache values and the scale contract (decode
+  over an FP8 cache is ``attention.decode_fp8``, quantising appends
+  ``append.append_quantized``).
 
 Sources: the three FlashInfer pages (aicassindra "FlashInfer, in depth";
 pyshine "FlashInfer" source tour; pinghaoyang "FlashInfer 完全拆解").  Each
@@ -30,4 +33,4 @@ scaled_dot_product_attention in float64) or brute force.  No function is
 "parity unpinned".
 """
 
-from . import append, attention, merge, page_table, plan_ref  # noqa: F401
+from . import append, attention, fp8, merge, page_table, plan_ref  # noqa: F401

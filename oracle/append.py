@@ -58,3 +58,25 @@ def append(cache_bits, k_new_bits, v_new_bits, batch_indices, positions, kv_indp
         out[page, 0, pos % P] = k_new_bits[t]
         out[page, 1, pos % P] = v_new_bits[t]
     return out
+
+
+def append_quantized(cache_codes, k_new_bits, v_new_bits, batch_indices, positions, kv_indptr,
+                     kv_indices, k_scale: float = 1.0, v_scale: float = 1.0):
+    """``append`` into an FP8 E4M3 cache: new bf16 rows are stored as
+    e4m3(x / k_scale) and e4m3(x / v_scale) (nearest, ties to even,
+    saturated; oracle.fp8), fused with the write as the pyshine page
+    describes for quantising appends.
+
+    The code is a rounding decision, so it is taken in the precision the
+    library computes x / scale in: float32, as x times the float32 value of
+    1 / scale."""
+    from . import fp8
+    from .attention import bf16_to_f64
+
+    def scaled(bits, scale):
+        inv = np.float32(1.0 / float(scale))
+        return (bf16_to_f64(bits).astype(np.float32) * inv).astype(np.float64)
+
+    k = fp8.f64_to_e4m3(scaled(k_new_bits, k_scale))
+    v = fp8.f64_to_e4m3(scaled(v_new_bits, v_scale))
+    return append(cache_codes, k, v, batch_indices, positions, kv_indptr, kv_indices)

@@ -140,3 +140,28 @@ def decode_bruteforce(q_bits, cache_bits, kv_indptr, kv_indices, kv_last_page_le
             for d in range(D):
                 o[i][h][d] = math.fsum(w * r[d] for w, r in zip(weights, rows)) / total
     return np.array(o), np.array(lse)
+
+
+def decode_fp8(q_bits, cache_codes, kv_indptr, kv_indices, kv_last_page_len, num_kv_heads: int,
+               sm_scale=None, k_scale: float = 1.0, v_scale: float = 1.0, requests=None):
+    """``decode`` over an FP8 E4M3 cache ([pages, 2, P, Hkv, D] uint8 codes)
+    with per-tensor scales: the keys are e4m3(code) * k_scale, the values
+    e4m3(code) * v_scale (the dequantising key and value transforms; see
+    oracle.fp8 for the format and the scale contract)."""
+    from . import fp8
+
+    q_bits = np.asarray(q_bits)
+    B, Hq, D = q_bits.shape
+    g = Hq // num_kv_heads
+    scale = default_scale(D) if sm_scale is None else float(sm_scale)
+    o = np.full((B, Hq, D), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    for i in (range(B) if requests is None else requests):
+        k_codes, v_codes = gather_request(cache_codes, kv_indptr, kv_indices, kv_last_page_len, i)
+        K = fp8.e4m3_to_f64(k_codes) * float(k_scale)
+        V = fp8.e4m3_to_f64(v_codes) * float(v_scale)
+        q = bf16_to_f64(q_bits[i])
+        for h in range(Hq):
+            kh = h // g
+            o[i, h], lse[i, h] = attention_state(q[h], K[:, kh], V[:, kh], scale)
+    return o, lse
