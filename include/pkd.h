@@ -22,7 +22,8 @@
  * Data layouts (all row-major, contiguous):
  *   q         bf16 [batch, num_qo_heads, head_dim]
  *   kv_cache  bf16 [num_pages, 2, page_size, num_kv_heads, head_dim]
- *             (NHD; index 0 of the second axis is K, 1 is V)
+ *             (NHD; index 0 of the second axis is K, 1 is V), or the same
+ *             shape of FP8 E4M3 codes (one byte each, see pkd_run_scaled)
  *   o         bf16 [batch, num_qo_heads, head_dim]
  *   lse       fp32 [batch, num_qo_heads], natural-log log-sum-exp of the
  *             scaled logits
@@ -204,9 +205,11 @@ size_t pkd_host_workspace_bytes(int32_t max_batch, int32_t num_slots);
  * copies it into int_workspace (reading the pinned host memory directly)
  * together with kv_indices.  kv_indptr and kv_last_page_len are host arrays read during the
  * call; kv_indices is a device array the caller may reuse once `stream` has
- * passed this call.  Only PKD_DTYPE_BF16, PKD_LAYOUT_NHD, head_dim 128,
- * num_qo_heads / num_kv_heads in {1, 2, 4, 8} and page_size in
- * {1, 2, 4, 8, 16, 32, 64} are built.  Rejects (PKD_ERR_INVALID_ARG)
+ * passed this call.  Built: bf16 q, PKD_LAYOUT_NHD, head_dim 128,
+ * num_qo_heads / num_kv_heads in {1, 2, 4, 8}, and either a bf16 cache with
+ * page_size in {1, 2, 4, 8, 16, 32, 64} or an FP8 E4M3 cache
+ * (kv_dtype PKD_DTYPE_FP8_E4M3, matrix-core variant only) with page_size in
+ * {16, 32, 64}; else PKD_ERR_UNSUPPORTED.  Rejects (PKD_ERR_INVALID_ARG)
  * kv_indptr[0] != 0, a request with no page, last_page_len outside
  * [1, page_size], batch < 1, num_qo_heads not a multiple of num_kv_heads.
  * The workspaces passed here are the ones later runs use. */
@@ -294,6 +297,19 @@ int pkd_run(pkd_handle* h, const void* q, int32_t batch, const void* kv_cache,
             int64_t num_pages, int32_t q_dtype, int32_t kv_dtype, void* o, float* lse,
             float sm_scale, pkd_stream_t stream);
 
+/* pkd_run over a cache of FP8 E4M3 codes with one scale per tensor: a K
+ * code c stands for e4m3(c) * k_scale and a V code for e4m3(c) * v_scale
+ * (OCP E4M3: bias 7, subnormals, no infinities, 0x7F / 0xFF NaN, largest
+ * finite 448).  The pinghaoyang page, table of customisable hooks in
+ * "可定制注意力模板：把变化留给 JIT" and section "适用边界与工程取舍", treats such a
+ * cache as a dequantising key/value transform with a scale contract.  The
+ * plan must have been made with kv_dtype PKD_DTYPE_FP8_E4M3.  k_scale and
+ * v_scale must be finite and > 0 (else PKD_ERR_INVALID_ARG), and 1 for a
+ * bf16 cache.  pkd_run is this call with both scales 1. */
+int pkd_run_scaled(pkd_handle* h, const void* q, int32_t batch, const void* kv_cache,
+                   int64_t num_pages, int32_t q_dtype, int32_t kv_dtype, void* o, float* lse,
+                   float sm_scale, float k_scale, float v_scale, pkd_stream_t stream);
+
 /* Waits for `stream`, returns the device error flags raised by runs since
  * the last read (PKD_DEVERR_*, 0 if none) and clears them. */
 int pkd_read_device_error(pkd_handle* h, int32_t* flags, pkd_stream_t stream);
@@ -317,9 +333,20 @@ int pkd_read_device_error(pkd_handle* h, int32_t* flags, pkd_stream_t stream);
  * kv_cache ([num_pages, 2, page_size, num_kv_heads, head_dim], NHD bf16).  A
  * token whose request, position or page id is out of range is not written
  * and sets *device_error (an int32 on the device, may be NULL) to
- * PKD_DEVERR_PAGE_ID.  Only bf16, NHD and head_dim 128 are built
- * (PKD_ERR_UNSUPPORTED otherwise).  Asynchronous on `stream`; tokens must
- * not share a slot (the order of such writes is not defined). */
+ * PKD_DEVERR_PAGE_ID.  Only NHD and head_dim 128 are built
+ * (PKD_ERR_UNSUPPORTED otherwise); kv_dtype is PKD_DTYPE_BF16 (rows copied
+ * bit for bit) or PKD_DTYPE_FP8_E4M3 (rows quantised with scales 1, as
+ * pkd_append_paged_kv_scaled).  Asynchronous on `stream`; tokens must not
+ * share a slot (the order of such writes is not defined).
+ *
+ * pkd_append_paged_kv_scaled: pkd_append_paged_kv into an FP8 E4M3 cache
+ * with per-tensor scales, quantising as it writes (pyshine, "The Paged KV
+ * Cache Layer", on fusing quantisation with the append): a new bf16 value x
+ * of K is stored as the E4M3 code nearest to x * (1 / k_scale) (the product
+ * in fp32, 1 / k_scale rounded to fp32 once; ties to even; magnitudes above
+ * 448 saturate to 448; NaN gives a NaN code), V likewise with v_scale.
+ * Scales must be finite and > 0, and 1 with a bf16 cache
+ * (PKD_ERR_INVALID_ARG). */
 int pkd_append_positions(const int32_t* append_indptr, const int32_t* kv_indptr,
                          const int32_t* kv_last_page_len, int32_t batch, int32_t page_size,
                          int32_t* batch_indices, int32_t* positions, pkd_stream_t stream);
@@ -329,6 +356,14 @@ int pkd_append_paged_kv(const void* k_new, const void* v_new, const int32_t* bat
                         int32_t head_dim, int32_t page_size, int32_t kv_dtype,
                         int32_t kv_layout, void* kv_cache, int64_t num_pages,
                         int32_t* device_error, pkd_stream_t stream);
+int pkd_append_paged_kv_scaled(const void* k_new, const void* v_new,
+                               const int32_t* batch_indices, const int32_t* positions,
+                               int64_t nnz_append, const int32_t* kv_indptr,
+                               const int32_t* kv_indices, int32_t batch, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t page_size, int32_t kv_dtype,
+                               int32_t kv_layout, void* kv_cache, int64_t num_pages,
+                               float k_scale, float v_scale, int32_t* device_error,
+                               pkd_stream_t stream);
 
 /* -------------------------------- merge ------------------------------- */
 

@@ -75,7 +75,8 @@ def append_quantized(cache_codes, k_new_bits, v_new_bits, batch_indices, positio
 
     def scaled(bits, scale):
         inv = np.float32(1.0 / float(scale))
-        return (bf16_to_f64(bits).astype(np.float32) * inv).astype(np.float64)
+        with np.errstate(over="ignore"):  # a product past float32's range is inf, then saturates
+            return (bf16_to_f64(bits).astype(np.float32) * inv).astype(np.float64)
 
     k = fp8.f64_to_e4m3(scaled(k_new_bits, k_scale))
     v = fp8.f64_to_e4m3(scaled(v_new_bits, v_scale))

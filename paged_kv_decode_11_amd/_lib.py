@@ -84,8 +84,13 @@ SIGNATURES = {
     "pkd_append_positions": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp]),
     "pkd_append_paged_kv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _i32,
                                            _i32, _i32, _i32, _vp, _i64, _vp, _vp]),
+    "pkd_append_paged_kv_scaled": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _i32,
+                                                  _i32, _i32, _i32, _i32, _vp, _i64,
+                                                  ctypes.c_float, ctypes.c_float, _vp, _vp]),
     "pkd_run": (ctypes.c_int, [_vp, _vp, _i32, _vp, _i64, _i32, _i32, _vp, _vp, ctypes.c_float,
                                _vp]),
+    "pkd_run_scaled": (ctypes.c_int, [_vp, _vp, _i32, _vp, _i64, _i32, _i32, _vp, _vp,
+                                      ctypes.c_float, ctypes.c_float, ctypes.c_float, _vp]),
     "pkd_read_device_error": (ctypes.c_int, [_vp, _pi32, _vp]),
     "pkd_merge_state": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "pkd_merge_states": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),

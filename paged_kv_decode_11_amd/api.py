@@ -171,7 +171,9 @@ class DecodePlanRun:
         self._keep = kv_indices  # the copy is queued on the stream; keep the source alive
 
     def run(self, q, kv_cache, out=None, lse=None, return_lse: bool = False, sm_scale=None,
-            stream=None):
+            stream=None, k_scale=None, v_scale=None):
+        """Decode for the planned batch; a float8_e4m3fn cache takes per-tensor
+        k_scale / v_scale (pkd_run_scaled when a scale is given)."""
         import torch
 
         if self._planned is None:
@@ -187,11 +189,16 @@ class DecodePlanRun:
                               device=q.device)
         if return_lse and lse is None:
             lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=q.device)
-        check(self._L.pkd_run(self._h, q.data_ptr(), q.shape[0], kv_cache.data_ptr(),
-                              kv_cache.shape[0], _dtype_code(q.dtype), _dtype_code(kv_cache.dtype),
-                              out.data_ptr(), lse.data_ptr() if lse is not None else None,
-                              float(sm_scale) if sm_scale is not None else 0.0,
-                              _stream_ptr(stream)))
+        args = (self._h, q.data_ptr(), q.shape[0], kv_cache.data_ptr(), kv_cache.shape[0],
+                _dtype_code(q.dtype), _dtype_code(kv_cache.dtype), out.data_ptr(),
+                lse.data_ptr() if lse is not None else None,
+                float(sm_scale) if sm_scale is not None else 0.0)
+        if k_scale is None and v_scale is None:
+            check(self._L.pkd_run(*args, _stream_ptr(stream)))
+        else:
+            check(self._L.pkd_run_scaled(*args, float(1.0 if k_scale is None else k_scale),
+                                         float(1.0 if v_scale is None else v_scale),
+                                         _stream_ptr(stream)))
         return (out, lse) if (return_lse or lse is not None) else out
 
     def read_device_error(self, stream=None) -> int:
@@ -343,22 +350,32 @@ def append_positions(append_indptr, kv_indptr, kv_last_page_len, page_size, stre
 
 
 def append_paged_kv_cache(k_new, v_new, batch_indices, positions, kv_cache, kv_indices, kv_indptr,
-                          device_error=None, stream=None):
+                          device_error=None, stream=None, k_scale=None, v_scale=None):
     """Write new tokens' K and V rows ([nnz, Hkv, 128] bf16 each) into the
-    paged cache [pages, 2, P, Hkv, 128] in place; see pkd_append_paged_kv."""
+    paged cache [pages, 2, P, Hkv, 128] in place; see pkd_append_paged_kv.
+    A float8_e4m3fn cache takes the rows quantised with per-tensor scales
+    (pkd_append_paged_kv_scaled when a scale is given)."""
     import torch
 
     nnz, Hkv, D = k_new.shape
     for t in (k_new, v_new, kv_cache):
         if not (t.is_cuda and t.is_contiguous()):
             raise ValueError("k_new, v_new and kv_cache must be contiguous GPU tensors")
+    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise ValueError("k_new and v_new must be bf16")
     for t in (batch_indices, positions, kv_indices, kv_indptr):
         if not (t.is_cuda and t.dtype == torch.int32 and t.is_contiguous()):
             raise ValueError("index arrays must be contiguous int32 GPU tensors")
-    check(_lib.load().pkd_append_paged_kv(
-        k_new.data_ptr(), v_new.data_ptr(), batch_indices.data_ptr(), positions.data_ptr(), nnz,
-        kv_indptr.data_ptr(), kv_indices.data_ptr(), kv_indptr.shape[0] - 1, Hkv, D,
-        kv_cache.shape[2], _dtype_code(kv_cache.dtype), _lib.PKD_LAYOUT_NHD, kv_cache.data_ptr(),
-        kv_cache.shape[0], device_error.data_ptr() if device_error is not None else None,
-        _stream_ptr(stream)))
+    args = (k_new.data_ptr(), v_new.data_ptr(), batch_indices.data_ptr(), positions.data_ptr(), nnz,
+            kv_indptr.data_ptr(), kv_indices.data_ptr(), kv_indptr.shape[0] - 1, Hkv, D,
+            kv_cache.shape[2], _dtype_code(kv_cache.dtype), _lib.PKD_LAYOUT_NHD,
+            kv_cache.data_ptr(), kv_cache.shape[0])
+    err = device_error.data_ptr() if device_error is not None else None
+    L = _lib.load()
+    if k_scale is None and v_scale is None:
+        check(L.pkd_append_paged_kv(*args, err, _stream_ptr(stream)))
+    else:
+        check(L.pkd_append_paged_kv_scaled(
+            *args, float(1.0 if k_scale is None else k_scale),
+            float(1.0 if v_scale is None else v_scale), err, _stream_ptr(stream)))
 

@@ -122,12 +122,19 @@ pkd::PlanInput make_input(const int32_t* indptr, const int32_t* last, int32_t ba
 
 int check_shapes(int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t q_dtype, int32_t kv_dtype,
                  int32_t layout) {
-  if (q_dtype != PKD_DTYPE_BF16 || kv_dtype != PKD_DTYPE_BF16)
-    return fail(PKD_ERR_UNSUPPORTED, "only bf16 q and bf16 KV are built (pass PKD_DTYPE_BF16)");
+  if (q_dtype != PKD_DTYPE_BF16 || (kv_dtype != PKD_DTYPE_BF16 && kv_dtype != PKD_DTYPE_FP8_E4M3))
+    return fail(PKD_ERR_UNSUPPORTED,
+                "q must be bf16 and the KV cache bf16 or fp8 e4m3 (PKD_DTYPE_BF16 / _FP8_E4M3)");
   if (layout != PKD_LAYOUT_NHD) return fail(PKD_ERR_UNSUPPORTED, "only the NHD cache layout is built");
   if (D != pkd::kHeadDim) return fail(PKD_ERR_UNSUPPORTED, "only head_dim 128 is built");
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
     return fail(PKD_ERR_INVALID_ARG, "num_qo_heads must be a positive multiple of num_kv_heads");
+  if (kv_dtype == PKD_DTYPE_FP8_E4M3) {
+    if (!pkd::fp8_variant_built(Hq / Hkv, P))
+      return fail(PKD_ERR_UNSUPPORTED,
+                  "an fp8 e4m3 cache is built for group size 1, 2, 4 or 8 and page_size 16, 32 or 64");
+    return PKD_OK;
+  }
   if (!pkd::decode_variant_built(Hq / Hkv, P))
     return fail(PKD_ERR_UNSUPPORTED,
                 "group size must be 1, 2, 4 or 8 and page_size 1, 2, 4, 8, 16, 32 or 64");
@@ -283,6 +290,8 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
   if (rc != PKD_OK) return rc;
   if (qo_indptr && (rc = check_shared_shapes(num_qo_heads, num_kv_heads, page_size)) != PKD_OK)
     return rc;
+  if (qo_indptr && kv_dtype != PKD_DTYPE_BF16)
+    return fail(PKD_ERR_UNSUPPORTED, "shared-prefix plans are built for a bf16 cache only");
   if (!kv_indices || !int_workspace || !float_workspace || !host_workspace)
     return fail(PKD_ERR_INVALID_ARG, "kv_indices and the three workspaces must be non-null");
   if ((reinterpret_cast<uintptr_t>(int_workspace) & 255) ||
@@ -293,6 +302,8 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
   const int32_t variant = opts ? opts->variant : PKD_VARIANT_AUTO;
   if (variant != PKD_VARIANT_AUTO && variant != PKD_VARIANT_DOT2 && variant != PKD_VARIANT_MFMA)
     return fail(PKD_ERR_INVALID_ARG, "unknown decode kernel variant");
+  if (variant == PKD_VARIANT_DOT2 && kv_dtype == PKD_DTYPE_FP8_E4M3)
+    return fail(PKD_ERR_UNSUPPORTED, "an fp8 e4m3 cache has only the matrix-core kernel");
 
   DeviceGuard guard(h->device);
   if (!guard.ok) return hip_fail(guard.err, "hipSetDevice");
@@ -410,6 +421,13 @@ int pkd_plan_shared(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_i
 int pkd_run(pkd_handle* h, const void* q, int32_t batch, const void* kv_cache, int64_t num_pages,
             int32_t q_dtype, int32_t kv_dtype, void* o, float* lse, float sm_scale,
             pkd_stream_t stream) {
+  return pkd_run_scaled(h, q, batch, kv_cache, num_pages, q_dtype, kv_dtype, o, lse, sm_scale,
+                        1.f, 1.f, stream);
+}
+
+int pkd_run_scaled(pkd_handle* h, const void* q, int32_t batch, const void* kv_cache,
+                   int64_t num_pages, int32_t q_dtype, int32_t kv_dtype, void* o, float* lse,
+                   float sm_scale, float k_scale, float v_scale, pkd_stream_t stream) {
   if (!h) return fail(PKD_ERR_INVALID_ARG, "null handle");
   if (!h->planned) return fail(PKD_ERR_STALE_PLAN, "pkd_run before any pkd_plan on this handle");
   if (batch != h->batch)
@@ -423,6 +441,10 @@ int pkd_run(pkd_handle* h, const void* q, int32_t batch, const void* kv_cache, i
       (reinterpret_cast<uintptr_t>(o) & 15))
     return fail(PKD_ERR_INVALID_ARG, "q, kv_cache and o must be 16-byte aligned");
   if (!(std::isfinite(sm_scale))) return fail(PKD_ERR_INVALID_ARG, "sm_scale must be finite");
+  if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return fail(PKD_ERR_INVALID_ARG, "k_scale and v_scale must be finite and > 0");
+  if (h->kv_dtype != PKD_DTYPE_FP8_E4M3 && (k_scale != 1.f || v_scale != 1.f))
+    return fail(PKD_ERR_INVALID_ARG, "k_scale and v_scale apply to an fp8 e4m3 cache only");
 
   DeviceGuard guard(h->device);
   if (!guard.ok) return hip_fail(guard.err, "hipSetDevice");
@@ -438,7 +460,8 @@ int pkd_run(pkd_handle* h, const void* q, int32_t batch, const void* kv_cache, i
   dp.fws = static_cast<float*>(h->float_ws);
   dp.err = static_cast<int32_t*>(h->int_ws);
   dp.num_pages = num_pages;
-  dp.scale_log2 = scale * 1.44269504088896341f;
+  dp.scale_log2 = scale * k_scale * 1.44269504088896341f;
+  dp.out_scale = v_scale;
   dp.num_qo_heads = h->Hq;
   dp.num_kv_heads = h->Hkv;
 
@@ -478,6 +501,8 @@ int pkd_run(pkd_handle* h, const void* q, int32_t batch, const void* kv_cache, i
   if (prof && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if (h->layout.kind == PKD_PLAN_SHARED)
     e = pkd::launch_prefix_mfma(dp, h->Hq / h->Hkv, h->P, h->num_slots, s);
+  else if (h->kv_dtype == PKD_DTYPE_FP8_E4M3)
+    e = pkd::launch_decode_fp8(dp, h->Hq / h->Hkv, h->P, h->num_slots, s);
   else if (h->variant == PKD_VARIANT_DOT2)
     e = pkd::launch_decode(dp, h->Hq / h->Hkv, h->P, h->num_slots, s);
   else
@@ -531,7 +556,26 @@ int pkd_append_paged_kv(const void* k_new, const void* v_new, const int32_t* bat
                         int32_t head_dim, int32_t page_size, int32_t kv_dtype,
                         int32_t kv_layout, void* kv_cache, int64_t num_pages,
                         int32_t* device_error, pkd_stream_t stream) {
-  if (kv_dtype != PKD_DTYPE_BF16) return fail(PKD_ERR_UNSUPPORTED, "only bf16 KV is built");
+  return pkd_append_paged_kv_scaled(k_new, v_new, batch_indices, positions, nnz_append, kv_indptr,
+                                    kv_indices, batch, num_kv_heads, head_dim, page_size, kv_dtype,
+                                    kv_layout, kv_cache, num_pages, 1.f, 1.f, device_error,
+                                    stream);
+}
+
+int pkd_append_paged_kv_scaled(const void* k_new, const void* v_new,
+                               const int32_t* batch_indices, const int32_t* positions,
+                               int64_t nnz_append, const int32_t* kv_indptr,
+                               const int32_t* kv_indices, int32_t batch, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t page_size, int32_t kv_dtype,
+                               int32_t kv_layout, void* kv_cache, int64_t num_pages,
+                               float k_scale, float v_scale, int32_t* device_error,
+                               pkd_stream_t stream) {
+  if (kv_dtype != PKD_DTYPE_BF16 && kv_dtype != PKD_DTYPE_FP8_E4M3)
+    return fail(PKD_ERR_UNSUPPORTED, "the cache must be bf16 or fp8 e4m3");
+  if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return fail(PKD_ERR_INVALID_ARG, "k_scale and v_scale must be finite and > 0");
+  if (kv_dtype == PKD_DTYPE_BF16 && (k_scale != 1.f || v_scale != 1.f))
+    return fail(PKD_ERR_INVALID_ARG, "k_scale and v_scale apply to an fp8 e4m3 cache only");
   if (kv_layout != PKD_LAYOUT_NHD) return fail(PKD_ERR_UNSUPPORTED, "only the NHD layout is built");
   if (head_dim != pkd::kHeadDim) return fail(PKD_ERR_UNSUPPORTED, "only head_dim 128 is built");
   if (nnz_append < 0 || batch < 1 || num_kv_heads < 1 || page_size < 1 || num_pages < 1)
@@ -546,9 +590,15 @@ int pkd_append_paged_kv(const void* k_new, const void* v_new, const int32_t* bat
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "device query");
-  e = pkd::launch_append_kv(k_new, v_new, batch_indices, positions, nnz_append, kv_indptr,
-                            kv_indices, batch, num_kv_heads, page_size, kv_cache, num_pages,
-                            device_error, 8 * cus, static_cast<hipStream_t>(stream));
+  if (kv_dtype == PKD_DTYPE_FP8_E4M3)
+    e = pkd::launch_append_kv_fp8(k_new, v_new, batch_indices, positions, nnz_append, kv_indptr,
+                                  kv_indices, batch, num_kv_heads, page_size, kv_cache, num_pages,
+                                  float(1.0 / double(k_scale)), float(1.0 / double(v_scale)),
+                                  device_error, 8 * cus, static_cast<hipStream_t>(stream));
+  else
+    e = pkd::launch_append_kv(k_new, v_new, batch_indices, positions, nnz_append, kv_indptr,
+                              kv_indices, batch, num_kv_heads, page_size, kv_cache, num_pages,
+                              device_error, 8 * cus, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKD_OK : hip_fail(e, "append kernel launch");
 }
 

@@ -1,0 +1,469 @@
+// Paged GQA decode over an FP8 (E4M3) KV cache, for gfx950.
+//
+// Same work items and outputs as the bf16 kernels (pinghaoyang FlashInfer
+// page, sections "从推理形状出发" and "在线 Softmax 为什么允许任意切块"); the
+// cache holds E4M3 codes and one scale per tensor, a stored K code c standing
+// for e4m3(c) * k_scale (pinghaoyang page, table of customisable hooks in
+// "可定制注意力模板：把变化留给 JIT": dequantisation is a key/value transform
+// with a scale contract).  k_scale is folded into the logit scale and v_scale
+// into the final normalisation, so the kernel works on the codes' values.
+//
+// Halving the bytes per token halves the time HBM allows per token, so both
+// products go to the matrix cores and the vector ALUs are left with the
+// conversions and the softmax.  A step covers 32 tokens of one KV head:
+//
+// * S^T = K Q^T: two v_mfma_f32_16x16x32_bf16 chains (tokens 0..15 and
+//   16..31), K as the A operand straight from the cache (lane l holds 32
+//   bytes of token l & 15's row), Q^T as the B operand (rows g..15 zero).
+//   Every E4M3 value is exact in bf16 and bf16 x bf16 products are exact in
+//   fp32, so the logits carry only fp32 summation error.  The contraction
+//   order over head_dim is permuted the same way in both operands so that
+//   each lane's K bytes are 2 x 16 contiguous bytes.
+// * The result leaves lane l with row l & 15 and tokens 4 (l >> 4) + v of
+//   each half: the row maximum is an in-lane max over 8 values and a swap
+//   across the four 16-lane groups; the 8 probabilities of a lane are, in
+//   fp16, exactly the B operand of the P V product, so they never leave the
+//   registers.
+// * O^T += V^T P^T: eight v_mfma_f32_16x16x32_f16 (16 head dims each). V
+//   rows are written to LDS in token order permuted to match P's layout and
+//   read back transposed with ds_read_b64_tr_b8, 8 tokens of one head dim
+//   per lane, then widened to fp16 (exact).  The probabilities are scaled by
+//   2^15 before the fp16 conversion (folded into the exponent), which keeps
+//   them in fp16's normal range down to 2^-29; the scale cancels in o = acc
+//   / l.
+//
+// K and V of the next two steps stream into registers while the current one
+// is computed (three steps in a ring), one wave per KV head as in the bf16
+// matrix-core kernel.  Page sizes 16, 32 and 64: each 16-token half of a
+// step lies in one page, addressed through a buffer descriptor over that
+// page.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "device_common.h"
+#include "kernels.h"
+#include "pkd.h"
+#include "plan_layout.h"
+
+namespace pkd {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef int32_t i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
+
+constexpr int kStep = 32;
+// probabilities enter fp16 as p * 2^kPShift
+constexpr float kPShift = 15.f;
+
+// 8 E4M3 codes (two dwords) to 8 bf16 (exact).
+__device__ __forceinline__ uint4 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  return make_uint4(
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true)));
+}
+
+// 8 E4M3 codes to 8 fp16 (exact).
+__device__ __forceinline__ uint4 fp8x8_to_f16(uint32_t w0, uint32_t w1) {
+  return make_uint4(
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.f, true)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.f, true)));
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f16x2_t v;
+  v.x = (_Float16)lo;
+  v.y = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ floatx4_t mfma_bf16(uint4 a, uint4 b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4_t mfma_f16(uint4 a, uint4 b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// LDS row (slot) of step token t.  P^T's B operand gives lane group kg the
+// tokens 4 kg .. 4 kg + 3 of both halves as its 8 contraction slots
+// 8 kg .. 8 kg + 7; V rows are stored in that slot order.
+__device__ __forceinline__ int v_slot(int t) {
+  const int u = t & 15;
+  return 8 * (u >> 2) + 4 * (t >> 4) + (u & 3);
+}
+
+// V rows sit 144 bytes apart in LDS: the 16 rows that two lane groups read
+// at the same head dims then fall on 16 distinct 4-bank groups, and every
+// lane's read and write addresses are one base plus constant offsets.
+constexpr int kVRowBytes = 144;
+
+struct FShared {
+  uint4 v[kStep * kVRowBytes / 16];  // V rows of the step by slot, kVRowBytes apart
+};
+
+struct FStep {
+  uint4 k[2][2];  // half h, load i: K[token 16 h + (l & 15)] bytes 64 i + 16 (l >> 4) .. + 16
+  uint4 v[4];     // load i: V[token 8 i + (l >> 3)] bytes 16 (l & 7) .. + 16
+};
+
+// Buffers over the pages of the two halves of a step and the byte offset of
+// each half's first token row within its page.
+struct FRef {
+  __amdgpu_buffer_rsrc_t page[2];
+  uint32_t off[2];
+};
+
+struct FIds {
+  int32_t id[2];
+};
+
+struct FCtx {
+  const char* __restrict__ kv;
+  int64_t num_pages;
+  uint32_t row_bytes;   // one token's K (or V) codes of all KV heads
+  uint32_t v_bytes;     // K half of a page
+  uint32_t page_bytes;
+  uint32_t k_lane;      // this lane's K offset in a half: (l & 15) rows + head + 16 (l >> 4)
+  uint32_t v_lane;      // this lane's V offset in a load: (l >> 3) rows + head + 16 (l & 7)
+};
+
+// Page ids of step s's halves; a half past the item's last page (possible
+// when P = 16) reads that last page and is masked.
+template <int P>
+__device__ __forceinline__ FIds f_read_ids(const int32_t* idx, int len, int s) {
+  FIds ids;
+  const int last = (len - 1) / P;
+  ids.id[0] = idx[min((kStep * s) / P, last)];
+  if constexpr (P == 16) {
+    ids.id[1] = idx[min((kStep * s + 16) / P, last)];
+  } else {
+    ids.id[1] = ids.id[0];
+  }
+  return ids;
+}
+
+template <int P>
+__device__ __forceinline__ FRef f_ref(const FCtx& c, const FIds& ids, int s, int& bad) {
+  FRef r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t pg = safe_page(ids.id[h], c.num_pages, bad);
+    // raw buffer over one page (32-bit data format word as raw loads need);
+    // offsets past the page read zeros
+    r.page[h] = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(c.kv + pg * c.page_bytes), 0,
+                                                  int(c.page_bytes), 0x00020000);
+    r.off[h] = uint32_t((kStep * s + 16 * h) % P) * c.row_bytes;
+  }
+  return r;
+}
+
+__device__ __forceinline__ void f_load(FStep& d, const FCtx& c, const FRef& r) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const auto w = __builtin_amdgcn_raw_buffer_load_b128(r.page[h], c.k_lane, r.off[h] + 64 * i,
+                                                           kBufferNontemporal);
+      d.k[h][i] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto w = __builtin_amdgcn_raw_buffer_load_b128(
+        r.page[i >> 1], c.v_lane, r.off[i >> 1] + c.v_bytes + 8 * (i & 1) * c.row_bytes,
+        kBufferNontemporal);
+    d.v[i] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+template <int G>
+struct FState {
+  float m;          // running max (base 2) of row l & 15
+  float lp;         // this lane's share of the row's sum of 2^15 p
+  floatx4_t o[8];   // O^T block b: dims 16 b + 4 (l >> 4) + v of row l & 15, scaled by 2^15
+};
+
+// One 32-token step.  With kPrefetch a later step's loads are issued first;
+// the last step (kLast) masks tokens >= valid: their logits to -inf and
+// their V rows to zero (a slot past the sequence may hold any code).
+template <int G, bool kPrefetch, bool kLast>
+__device__ __forceinline__ void f_step(FState<G>& st, const FStep& cur, FStep& nxt,
+                                       const FCtx& c, const FRef& next, const uint4 (&qop)[4],
+                                       int valid, int lane, float scale_log2, FShared& sh,
+                                       uint32_t v_wr, uint32_t v_rd) {
+  const int kg = lane >> 4;
+  if constexpr (kPrefetch) {
+    __builtin_amdgcn_sched_barrier(0);
+    f_load(nxt, c, next);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // V rows to LDS in slot order (the previous step's transposed reads come
+  // first in program order, and one wave's LDS accesses complete in order).
+  // Load i of lane l holds token 8 i + (l >> 3), whose slot is
+  // 16 (i & 1) + 4 (i >> 1) + v_slot(l >> 3).
+  {
+    char* vb = reinterpret_cast<char*>(sh.v) + v_wr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 w = cur.v[i];
+      if constexpr (kLast) {
+        if (8 * i + (lane >> 3) >= valid) w = make_uint4(0u, 0u, 0u, 0u);
+      }
+      *reinterpret_cast<uint4*>(vb + (16 * (i & 1) + 4 * (i >> 1)) * kVRowBytes) = w;
+    }
+  }
+
+  // S^T for both halves: A = K rows, B = Q^T; MFMA j takes head dims
+  // 64 (j >> 1) + 16 kg + 8 (j & 1) .. + 7 at contraction slots 8 kg ..
+  floatx4_t s[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    s[h] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 kw = cur.k[h][j >> 1];
+      const uint4 ka = (j & 1) ? fp8x8_to_bf16(kw.z, kw.w) : fp8x8_to_bf16(kw.x, kw.y);
+      s[h] = mfma_bf16(ka, qop[j], s[h]);
+    }
+  }
+
+  // online softmax on row l & 15, tokens 16 h + 4 kg + v
+  float x[2][4];
+  float mx = kNegInf;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float sv = s[h][v] * scale_log2;
+      if constexpr (kLast) {
+        if (16 * h + 4 * kg + v >= valid) sv = kNegInf;
+      }
+      x[h][v] = sv;
+      mx = fmaxf(mx, sv);
+    }
+  const float mn = fmaxf(st.m, rows_max(mx));
+  const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
+  const float base = mn - kPShift;
+  float p[2][4];
+  float psum = 0.f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      p[h][v] = __builtin_amdgcn_exp2f(x[h][v] - base);
+      psum += p[h][v];
+    }
+  st.lp = fmaf(st.lp, alpha, psum);
+  st.m = mn;
+  const uint4 pb = make_uint4(pack_f16x2(p[0][0], p[0][1]), pack_f16x2(p[0][2], p[0][3]),
+                              pack_f16x2(p[1][0], p[1][1]), pack_f16x2(p[1][2], p[1][3]));
+#pragma unroll
+  for (int b = 0; b < 8; ++b) st.o[b] *= alpha;
+
+  __builtin_amdgcn_wave_barrier();
+  // O^T block b += V^T[16 b .. 16 b + 15][slots] P^T[slots][rows].  In the
+  // transposed read, lane j of each 16-lane group names an 8-byte piece:
+  // slot 8 kg + (j >> 1), head dims 16 b + 8 (j & 1) .. + 7 (v_rd + 16 b);
+  // lane i then receives byte i & 7 of the pieces of lanes i >> 3,
+  // 2 + (i >> 3), ..., that is head dim 16 b + i at slots 8 kg .. 8 kg + 7.
+  char* vr = reinterpret_cast<char*>(sh.v) + v_rd;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const i32x2_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (lds_i32x2_t*)((__attribute__((address_space(3))) char*)vr + 16 * b));
+    st.o[b] = mfma_f16(fp8x8_to_f16(uint32_t(w[0]), uint32_t(w[1])), pb, st.o[b]);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int G, int P>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void decode_fp8_kernel(const uint16_t* __restrict__ q_ptr, const uint8_t* __restrict__ kv_ptr,
+                       uint16_t* __restrict__ o_ptr, float* __restrict__ lse_ptr,
+                       const int32_t* __restrict__ ws, float* __restrict__ fws,
+                       int32_t* __restrict__ err, int64_t num_pages, float scale_log2,
+                       float out_scale, int num_qo_heads, int num_kv_heads) {
+  static_assert(G >= 1 && G <= 8, "group size");
+  static_assert(P == 16 || P == 32 || P == 64, "page size");
+  __shared__ FShared shared[kMaxWavesPerBlock];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int row16 = lane & 15;
+  const int kg = lane >> 4;
+  FShared& sh = shared[wave];
+  // this lane's LDS write base (slot of token l >> 3, piece l & 7) and
+  // transposed-read base (slot 8 kg + ((l & 15) >> 1), byte 8 (l & 1))
+  const uint32_t v_wr = uint32_t(v_slot(lane >> 3)) * kVRowBytes + 16 * uint32_t(lane & 7);
+  const uint32_t v_rd = uint32_t(8 * kg + (row16 >> 1)) * kVRowBytes + 8 * uint32_t(lane & 1);
+
+  const int32_t* hdr = ws + PKD_HEADER_BASE;
+  const int num_slots = gridDim.x;
+  const int32_t* slot_indptr = ws + plan_off_slots();
+  const int32_t* first = ws + plan_off_first(num_slots) + 8 * int64_t(blockIdx.x);
+  const int32_t* items = ws + plan_off_items(num_slots);
+  const int32_t* kv_idx = ws + hdr[PKD_H_OFF_INDICES];
+  const int64_t n_partials = hdr[PKD_H_PARTIALS];
+  const int Hq = num_qo_heads;
+  float* o_part = fws;
+  float* lse_part = fws + n_partials * Hq * kHeadDim;
+
+  FCtx c;
+  c.kv = reinterpret_cast<const char*>(kv_ptr);
+  c.num_pages = num_pages;
+  c.row_bytes = uint32_t(num_kv_heads) * kHeadDim;
+  c.v_bytes = uint32_t(P) * c.row_bytes;
+  c.page_bytes = 2 * c.v_bytes;
+
+  const int it_begin = slot_indptr[blockIdx.x];
+  const int it_end = slot_indptr[blockIdx.x + 1];
+  const int first_req = first[0], first_page = first[1], first_out = first[4],
+            first_len = first[5];
+  for (int it = it_begin; it < it_end; ++it) {
+    int req = first_req, page_begin = first_page, out = first_out, len = first_len;
+    if (it != it_begin) {
+      const int32_t* item = items + 8 * it;
+      req = item[0];
+      page_begin = item[1];
+      out = item[4];
+      len = item[5];
+    }
+    const int32_t* idx = kv_idx + page_begin;
+    const int nsteps = (len + kStep - 1) / kStep;
+
+    for (int kh = wave; kh < num_kv_heads; kh += nwaves) {
+      const uint32_t head = uint32_t(kh) * kHeadDim;
+      c.k_lane = uint32_t(row16) * c.row_bytes + head + 16 * uint32_t(kg);
+      c.v_lane = uint32_t(lane >> 3) * c.row_bytes + head + 16 * uint32_t(lane & 7);
+
+      // Q^T operand: lane (row l & 15, kg) holds head dims
+      // 64 (j >> 1) + 16 kg + 8 (j & 1) .. + 7 for MFMA j; rows >= g are zero
+      uint4 qop[4];
+      {
+        const uint16_t* qrow = q_ptr + (int64_t(req) * Hq + kh * G + row16) * kHeadDim + 16 * kg;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          qop[j] = row16 < G
+                       ? *reinterpret_cast<const uint4*>(qrow + 64 * (j >> 1) + 8 * (j & 1))
+                       : make_uint4(0u, 0u, 0u, 0u);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      FState<G> st;
+      st.m = kNegInf;
+      st.lp = 0.f;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) st.o[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+      int bad = 0;
+      FStep ta, tb, tc;
+      f_load(ta, c, f_ref<P>(c, f_read_ids<P>(idx, len, 0), 0, bad));
+      if (nsteps > 1) f_load(tb, c, f_ref<P>(c, f_read_ids<P>(idx, len, 1), 1, bad));
+      FIds ids_next = f_read_ids<P>(idx, len, min(2, nsteps - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      const int last_valid = len - kStep * (nsteps - 1);
+      const FRef none = {};
+      int n = 0;
+      auto step = [&](FStep& cur, FStep& nxt) -> bool {
+        if (n == nsteps - 1) {
+          f_step<G, false, true>(st, cur, nxt, c, none, qop, last_valid, lane, scale_log2, sh,
+                                 v_wr, v_rd);
+          return true;
+        }
+        if (n + 2 < nsteps) {
+          const FRef ref = f_ref<P>(c, ids_next, n + 2, bad);
+          ids_next = f_read_ids<P>(idx, len, min(n + 3, nsteps - 1));
+          f_step<G, true, false>(st, cur, nxt, c, ref, qop, kStep, lane, scale_log2, sh, v_wr,
+                                 v_rd);
+        } else {
+          f_step<G, false, false>(st, cur, nxt, c, none, qop, kStep, lane, scale_log2, sh, v_wr,
+                                  v_rd);
+        }
+        ++n;
+        return false;
+      };
+      for (;;) {
+        if (step(ta, tc)) break;
+        if (step(tb, ta)) break;
+        if (step(tc, tb)) break;
+      }
+      if (bad && lane == 0) err[0] = PKD_DEVERR_PAGE_ID;
+
+      // lane (row l & 15, kg) holds head dims 16 b + 4 kg + v of its row
+      const float l_row = rows_sum(st.lp);
+      if (row16 < G) {
+        const float inv = out_scale / l_row;
+        const float lse_nat = (st.m + __log2f(l_row) - kPShift) * kLn2;
+        const int64_t qh = int64_t(kh) * G + row16;
+        if (out < 0) {
+          uint16_t* orow = o_ptr + (int64_t(req) * Hq + qh) * kHeadDim + 4 * kg;
+#pragma unroll
+          for (int b = 0; b < 8; ++b)
+            *reinterpret_cast<uint2*>(orow + 16 * b) =
+                make_uint2(pack_bf16x2(st.o[b][0] * inv, st.o[b][1] * inv),
+                           pack_bf16x2(st.o[b][2] * inv, st.o[b][3] * inv));
+          if (lse_ptr && kg == 0) lse_ptr[int64_t(req) * Hq + qh] = lse_nat;
+        } else {
+          float* orow = o_part + (int64_t(out) * Hq + qh) * kHeadDim + 4 * kg;
+#pragma unroll
+          for (int b = 0; b < 8; ++b)
+            *reinterpret_cast<float4*>(orow + 16 * b) =
+                make_float4(st.o[b][0] * inv, st.o[b][1] * inv, st.o[b][2] * inv,
+                            st.o[b][3] * inv);
+          if (kg == 0) lse_part[int64_t(out) * Hq + qh] = lse_nat;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
+template <int G, int P>
+hipError_t launch_f(const DecodeParams& p, int num_slots, hipStream_t stream) {
+  const int waves = p.num_kv_heads < kMaxWavesPerBlock ? p.num_kv_heads : kMaxWavesPerBlock;
+  hipLaunchKernelGGL((decode_fp8_kernel<G, P>), dim3(num_slots), dim3(64 * waves), 0, stream,
+                     p.q, reinterpret_cast<const uint8_t*>(p.kv), p.o, p.lse, p.ws, p.fws, p.err,
+                     p.num_pages, p.scale_log2, p.out_scale, p.num_qo_heads, p.num_kv_heads);
+  return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_fg(const DecodeParams& p, int page_size, int num_slots, hipStream_t stream) {
+  switch (page_size) {
+    case 16: return launch_f<G, 16>(p, num_slots, stream);
+    case 32: return launch_f<G, 32>(p, num_slots, stream);
+    case 64: return launch_f<G, 64>(p, num_slots, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool fp8_variant_built(int g, int page_size) {
+  return (g == 1 || g == 2 || g == 4 || g == 8) &&
+         (page_size == 16 || page_size == 32 || page_size == 64);
+}
+
+hipError_t launch_decode_fp8(const DecodeParams& p, int g, int page_size, int num_slots,
+                             hipStream_t stream) {
+  switch (g) {
+    case 1: return launch_fg<1>(p, page_size, num_slots, stream);
+    case 2: return launch_fg<2>(p, page_size, num_slots, stream);
+    case 4: return launch_fg<4>(p, page_size, num_slots, stream);
+    case 8: return launch_fg<8>(p, page_size, num_slots, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pkd

@@ -13,14 +13,15 @@ constexpr int kMaxWavesPerBlock = 8;
 
 struct DecodeParams {
   const uint16_t* q;   // bf16 [B, Hq, 128]
-  const uint16_t* kv;  // bf16 [num_pages, 2, P, Hkv, 128]
+  const uint16_t* kv;  // [num_pages, 2, P, Hkv, 128]: bf16, or E4M3 codes (fp8 kernel)
   uint16_t* o;         // bf16 [B, Hq, 128]
   float* lse;          // fp32 [B, Hq] or null
   const int32_t* ws;   // int workspace (plan image + kv_indices copy)
   float* fws;          // float workspace (partial states)
   int32_t* err;        // device error word
   int64_t num_pages;
-  float scale_log2;    // sm_scale * log2(e)
+  float scale_log2;    // sm_scale * log2(e) (times k_scale for an E4M3 cache)
+  float out_scale;     // E4M3 cache: v_scale, applied to o; unused by the bf16 kernels
   int32_t num_qo_heads;
   int32_t num_kv_heads;
 };
@@ -49,6 +50,11 @@ hipError_t launch_decode(const DecodeParams& p, int g, int page_size, int num_sl
 hipError_t launch_decode_mfma(const DecodeParams& p, int g, int page_size, int num_slots,
                               hipStream_t stream);
 bool decode_variant_built(int g, int page_size);
+// Decode over an E4M3 cache (decode_fp8.hip): both products on the matrix
+// cores, V transposed through LDS.
+hipError_t launch_decode_fp8(const DecodeParams& p, int g, int page_size, int num_slots,
+                             hipStream_t stream);
+bool fp8_variant_built(int g, int page_size);
 // Shared-prefix kernel (prefix_mfma.hip): one KV head of one (group, row
 // block, chunk) item per workgroup, 128 query rows sharing each K/V tile.
 hipError_t launch_prefix_mfma(const DecodeParams& p, int g, int page_size, int num_slots,
@@ -77,6 +83,13 @@ hipError_t launch_append_kv(const void* k_new, const void* v_new, const int32_t*
                             const int32_t* kv_indices, int batch, int num_kv_heads,
                             int page_size, void* cache, int64_t num_pages, int32_t* err,
                             int grid_cap, hipStream_t stream);
+// The same into an E4M3 cache: code = e4m3(x * inv_scale), saturated.
+hipError_t launch_append_kv_fp8(const void* k_new, const void* v_new,
+                                const int32_t* batch_indices, const int32_t* positions,
+                                int64_t nnz, const int32_t* kv_indptr, const int32_t* kv_indices,
+                                int batch, int num_kv_heads, int page_size, void* cache,
+                                int64_t num_pages, float k_inv_scale, float v_inv_scale,
+                                int32_t* err, int grid_cap, hipStream_t stream);
 
 // Merge of the split requests of the current plan (reads the plan image).
 hipError_t launch_merge_partials(const MergeParams& p, int grid, hipStream_t stream);

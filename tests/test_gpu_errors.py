@@ -71,6 +71,52 @@ def test_dtype_and_layout_errors():
     assert e.value.code == _lib.PKD_ERR_DTYPE_MISMATCH
 
 
+def test_fp8_cache_errors():
+    """An E4M3 cache: page sizes and kernels it is not built for, scales on a
+    bf16 cache, invalid scales, and a run whose cache dtype is not the plan's."""
+    import torch
+    import paged_kv_decode_11_amd as pkd
+
+    batch, q, cache = _inputs()
+    fp8 = torch.float8_e4m3fn
+    r = pkd.DecodePlanRun(max_batch=4, max_nnz=64, max_qo_heads=32)
+    idx = torch.from_numpy(batch.kv_indices).cuda()
+    args = (batch.kv_indptr, idx, batch.kv_last_page_len, 32, 8, 128)
+    with pytest.raises(pkd.PkdError) as e:
+        r.plan(*args, 8, kv_data_type=fp8)
+    assert e.value.code == _lib.PKD_ERR_UNSUPPORTED
+    with pytest.raises(pkd.PkdError) as e:
+        r.plan(*args, 16, kv_data_type=fp8, variant="dot2")
+    assert e.value.code == _lib.PKD_ERR_UNSUPPORTED
+    r.plan(*args, 16)
+    with pytest.raises(pkd.PkdError) as e:
+        r.run(q, cache, k_scale=0.5)
+    assert e.value.code == _lib.PKD_ERR_INVALID_ARG
+    codes = torch.zeros(cache.shape, dtype=torch.uint8, device="cuda").view(fp8)
+    with pytest.raises(pkd.PkdError) as e:
+        r.run(q, codes)
+    assert e.value.code == _lib.PKD_ERR_DTYPE_MISMATCH
+    r.plan(*args, 16, kv_data_type=fp8)
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(pkd.PkdError) as e:
+            r.run(q, codes, v_scale=bad)
+        assert e.value.code == _lib.PKD_ERR_INVALID_ARG
+    with pytest.raises(pkd.PkdError) as e:
+        r.run(q, cache)
+    assert e.value.code == _lib.PKD_ERR_DTYPE_MISMATCH
+    sr = pkd.SharedPlanRun(2, 4, 64, 32, 8)
+    with pytest.raises(pkd.PkdError) as e:
+        sr.plan(np.array([0, 2]), batch.kv_indptr[:2], idx[:3].contiguous(),
+                batch.kv_last_page_len[:1], 32, 8, 128, 16, kv_data_type=fp8)
+    assert e.value.code == _lib.PKD_ERR_UNSUPPORTED
+    k = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
+    i32 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(pkd.PkdError) as e:
+        pkd.append_paged_kv_cache(k, k, i32, i32, cache, idx, torch.from_numpy(
+            batch.kv_indptr).cuda(), k_scale=2.0)
+    assert e.value.code == _lib.PKD_ERR_INVALID_ARG
+
+
 def test_bad_page_table_rejected():
     import torch
     import paged_kv_decode_11_amd as pkd

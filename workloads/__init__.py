@@ -12,10 +12,13 @@ from .synth import (  # noqa: F401
     WORKLOADS,
     allocate_pages,
     device_cache,
+    device_cache_e4m3,
     device_query,
+    e4m3_codes,
     edge_lengths,
     f32_to_bf16_bits,
     host_cache,
+    host_cache_e4m3,
     host_query,
     make_batch,
     normal_bf16,

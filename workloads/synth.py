@@ -1,7 +1,8 @@
 """Seeded synthetic batches for paged GQA decode.
 
 Everything here is input generation: request lengths, where each request's
-pages sit in the pool, and N(0, 1) values rounded to bf16 for q, K and V.
+pages sit in the pool, and N(0, 1) values rounded to bf16 for q, K and V (or
+uniformly drawn FP8 E4M3 codes for an FP8 cache).
 The page-table layout is the one the FlashInfer pages describe (aicassindra
 "FlashInfer, in depth", section "The block-sparse page table"): a CSR triple
 (kv_indptr, kv_indices, kv_last_page_len) over a pool of fixed-size pages, and
@@ -167,6 +168,53 @@ def device_cache(batch: PagedBatch, seed: int, device, chunk_pages: int = 4096,
         else:
             flat.index_copy_(0, pages[p0:p1], vals)
     return cache
+
+
+E4M3_NAN = np.uint8(0x7F)
+
+
+def e4m3_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    """Uniformly drawn FP8 E4M3 codes (uint8) other than the two NaN codes
+    0x7F and 0xFF, which are replaced by the largest finite codes of their
+    sign: every exponent field equally likely, so values span 2^-9 .. 448
+    before the tensor's scale."""
+    c = rng.integers(0, 256, size=shape, dtype=np.uint16).astype(np.uint8)
+    return np.where((c & 0x7F) == 0x7F, c - 1, c).astype(np.uint8)
+
+
+def host_cache_e4m3(batch: PagedBatch, rng: np.random.Generator, poison: bool = False) -> np.ndarray:
+    """One layer's FP8 E4M3 cache as codes, [pages, 2, P, Hkv, D] uint8: the
+    used pages get ``e4m3_codes`` (in ascending page order), the others zeros,
+    or NaN codes when ``poison`` -- which also fills the unused slots of each
+    request's last page with NaN codes."""
+    shape = batch.cache_shape()
+    cache = np.full(shape, E4M3_NAN if poison else np.uint8(0), dtype=np.uint8)
+    used = np.unique(batch.kv_indices)
+    cache[used] = e4m3_codes(rng, (used.shape[0],) + shape[1:])
+    if poison:
+        last_pages = batch.kv_indices[batch.kv_indptr[1:] - 1]
+        for page, fill in zip(last_pages, batch.kv_last_page_len):
+            cache[page, :, int(fill):] = E4M3_NAN
+    return cache
+
+
+def device_cache_e4m3(batch: PagedBatch, seed: int, device, chunk_pages: int = 8192):
+    """One layer's FP8 E4M3 cache on ``device`` as a torch float8_e4m3fn
+    tensor, every page filled like ``e4m3_codes`` from torch's generator
+    seeded with ``seed`` (for pools too large to fill with numpy)."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    cache = torch.empty(batch.cache_shape(), dtype=torch.uint8, device=device)
+    flat = cache.view(batch.num_pages, -1)
+    for p0 in range(0, batch.num_pages, chunk_pages):
+        p1 = min(batch.num_pages, p0 + chunk_pages)
+        c = torch.randint(0, 256, (p1 - p0, flat.shape[1]), generator=gen, dtype=torch.int32,
+                          device=device)
+        c = torch.where((c & 0x7F) == 0x7F, c - 1, c)
+        flat[p0:p1].copy_(c.to(torch.uint8))
+    return cache.view(torch.float8_e4m3fn)
 
 
 def device_query(batch: PagedBatch, seed: int, device):
