@@ -9,7 +9,8 @@ in [3000, 5000], pages scattered through a 32,768-page pool per layer).
 
 Prints one JSON line.  `value` is the achieved KV-stream rate in GB/s
 (KV bytes the step must read, 4096 B per token per layer, over the measured
-step time).  By default a step is the plan call followed by one replay of a
+step time; 2048 B with --kv-dtype e4m3).  By default a step is the plan
+call followed by one replay of a
 HIP graph that holds the step's runs; --no-graph launches the runs one by
 one, and the eager timing is reported beside the graph one in any case.
 `roofline` gives the decode kernel's own rate from HIP events
@@ -54,36 +55,48 @@ def parse():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--variant", default="auto", choices=["auto", "dot2", "mfma"],
                     help="decode kernel (auto = the matrix-core kernel)")
+    ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "e4m3"],
+                    help="KV cache element type (e4m3: FP8 codes with per-tensor scales)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of this many MiB (5 times), "
                          "to calibrate HBM byte counters against a known size")
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
+# the source files a decode kernel is built from, by kernel
+KERNEL_FILES = {
+    "decode_mfma_kernel": ("decode_mfma.hip", "device_common.h", "plan_layout.h"),
+    "decode_kernel": ("decode.hip", "device_common.h", "plan_layout.h"),
+    "decode_fp8_kernel": ("decode_fp8.hip", "device_common.h", "plan_layout.h"),
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for name in ("decode.hip", "decode_mfma.hip", "merge.hip", "kernels.h", "device_common.h"):
+    for name in KERNEL_FILES[kernel]:
         with open(os.path.join(ROOT, "paged_kv_decode_11_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, launches_bytes: float):
+def measured_traffic(workload: str, kernel: str, kv_dtype: str):
     """HBM bytes per decode launch from committed rocprofv3 counter runs,
     if they were taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    tag = "" if kv_dtype == "bf16" else f"_{kv_dtype}"
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}{tag}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel") != kernel or rec.get("kernel_source_hash") != kernel_source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(batch, q_bits, cache_dev, o_dev, lse_dev, budget_s: float):
+def cpu_baseline(batch, q_bits, cache_dev, o_dev, lse_dev, budget_s: float, fp8_scales=None):
     """Time the oracle on layer 0's requests, in order, until the budget is
-    spent; also report its agreement with the GPU output on those rows."""
+    spent; also report its agreement with the GPU output on those rows.
+    fp8_scales = (k_scale, v_scale) for an E4M3 cache."""
     import numpy as np
     import torch
 
@@ -102,13 +115,21 @@ def cpu_baseline(batch, q_bits, cache_dev, o_dev, lse_dev, budget_s: float):
     for i in range(batch.batch):
         rows = batch.kv_indices[batch.kv_indptr[i]:batch.kv_indptr[i + 1]]
         sel = torch.from_numpy(rows.astype(np.int64)).to(cache_dev.device)
-        host = cache_dev.index_select(0, sel).view(torch.int16).cpu().numpy().view(np.uint16)
         n = rows.shape[0]
         indptr = np.array([0, n], dtype=np.int32)
         idx = np.arange(n, dtype=np.int32)
         last = batch.kv_last_page_len[i:i + 1]
-        t0 = time.perf_counter()
-        o_ref, lse_ref = att.decode(q_bits[i:i + 1], host, indptr, idx, last, batch.num_kv_heads)
+        if fp8_scales is None:
+            host = cache_dev.index_select(0, sel).view(torch.int16).cpu().numpy().view(np.uint16)
+            t0 = time.perf_counter()
+            o_ref, lse_ref = att.decode(q_bits[i:i + 1], host, indptr, idx, last,
+                                        batch.num_kv_heads)
+        else:
+            host = cache_dev.view(torch.uint8).index_select(0, sel).cpu().numpy()
+            t0 = time.perf_counter()
+            o_ref, lse_ref = att.decode_fp8(q_bits[i:i + 1], host, indptr, idx, last,
+                                            batch.num_kv_heads, k_scale=fp8_scales[0],
+                                            v_scale=fp8_scales[1])
         elapsed += time.perf_counter() - t0
         err_o = max(err_o, float(np.max(np.abs(o_gpu[i] - o_ref[0]))))
         err_l = max(err_l, float(np.max(np.abs(lse_gpu[i] - lse_ref[0]))))
@@ -116,7 +137,7 @@ def cpu_baseline(batch, q_bits, cache_dev, o_dev, lse_dev, budget_s: float):
         tokens += int(batch.kv_lens[i])
         if elapsed >= budget_s:
             break
-    kv_bytes = tokens * batch.kv_bytes_per_token()
+    kv_bytes = tokens * batch.kv_bytes_per_token() // (1 if fp8_scales is None else 2)
     gbs = kv_bytes / elapsed / 1e9
     us_layer = elapsed * 1e6 * batch.total_tokens / tokens
     return {
@@ -398,7 +419,12 @@ def main():
     torch.cuda.set_device(dev)
     spec, rng, b = workloads.workload(args.workload)
     batch = b["main"]
-    kv_tok = batch.kv_bytes_per_token()
+    fp8 = args.kv_dtype == "e4m3"
+    if fp8 and (args.variant == "dot2" or args.workload in ("token_sparse", "tiny")):
+        raise SystemExit("an e4m3 cache runs on the matrix-core kernel with page sizes 16-64")
+    kv_tok = batch.kv_bytes_per_token() // (2 if fp8 else 1)
+    kernel = ("decode_fp8_kernel" if fp8 else
+              "decode_mfma_kernel" if args.variant in ("auto", "mfma") else "decode_kernel")
     layer_bytes = batch.total_tokens * kv_tok
     if spec.num_layers > 1:
         n_layers, distinct = spec.num_layers, 2
@@ -412,8 +438,12 @@ def main():
 
     # caches: `distinct` freshly drawn, the rest device copies (distinct addresses)
     used_only = args.workload == "wide_gqa"
-    fresh = [workloads.device_cache(batch, spec.seed * 1000 + j, dev, used_only=used_only)
-             for j in range(distinct)]
+    if fp8:
+        fresh = [workloads.device_cache_e4m3(batch, spec.seed * 1000 + j, dev)
+                 for j in range(distinct)]
+    else:
+        fresh = [workloads.device_cache(batch, spec.seed * 1000 + j, dev, used_only=used_only)
+                 for j in range(distinct)]
     caches = []
     for layer in range(n_layers):
         if layer == 0:
@@ -435,14 +465,23 @@ def main():
                           max_qo_heads=batch.num_qo_heads, num_slots=args.slots, device=0)
     idx = torch.from_numpy(batch.kv_indices.astype(np.int32)).to(dev)
 
+    kv_type = torch.float8_e4m3fn if fp8 else torch.bfloat16
+    # per-tensor scales that bring the uniformly drawn codes (up to 448) to
+    # unit-range keys and values
+    scales = dict(k_scale=1.0 / 64, v_scale=1.0 / 64) if fp8 else {}
+
     def plan():
         r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, batch.num_qo_heads,
-               batch.num_kv_heads, batch.head_dim, batch.page_size, variant=args.variant)
+               batch.num_kv_heads, batch.head_dim, batch.page_size, variant=args.variant,
+               kv_data_type=kv_type)
+
+    def run(layer):
+        r.run(qs[layer], caches[layer], out=outs[layer], lse=lses[layer], **scales)
 
     def step():
         plan()
         for layer in range(n_layers):
-            r.run(qs[layer], caches[layer], out=outs[layer], lse=lses[layer])
+            run(layer)
 
     # plan host cost, on its own
     torch.cuda.synchronize()
@@ -487,7 +526,7 @@ def main():
         torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=s):
             for layer in range(n_layers):
-                r.run(qs[layer], caches[layer], out=outs[layer], lse=lses[layer])
+                run(layer)
         torch.cuda.synchronize()
         for _ in range(args.warmup):
             plan()
@@ -516,9 +555,10 @@ def main():
     spot = None
     if args.cpu_seconds > 0:
         log("cpu baseline (oracle) ...")
-        cpu, spot = cpu_baseline(batch, q_bits, caches[0], outs[0], lses[0], args.cpu_seconds)
+        cpu, spot = cpu_baseline(batch, q_bits, caches[0], outs[0], lses[0], args.cpu_seconds,
+                                 (scales["k_scale"], scales["v_scale"]) if fp8 else None)
 
-    traffic = measured_traffic(args.workload, layer_bytes)
+    traffic = measured_traffic(args.workload, kernel, args.kv_dtype)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -530,15 +570,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 q/K/V, seeded lengths and page placement)",
+        "dtype": "e4m3 kv (bf16/f16 mfma, f32 accumulate)" if fp8 else "bf16",
+        "data": ("synthetic (seeded N(0,1) bf16 q, uniformly drawn E4M3 K/V codes with "
+                 "scales 1/64, seeded lengths and page placement)" if fp8 else
+                 "synthetic (seeded N(0,1) bf16 q/K/V, seeded lengths and page placement)"),
         "config": {
             "workload": args.workload, "batch": batch.batch, "layers": n_layers,
             "num_qo_heads": batch.num_qo_heads, "num_kv_heads": batch.num_kv_heads,
             "head_dim": batch.head_dim, "page_size": batch.page_size,
             "kv_tokens_per_layer": batch.total_tokens, "pages_per_layer": batch.nnz,
-            "pool_pages": batch.num_pages, "slots": r.num_slots,
-            "decode_kernel": "mfma" if args.variant in ("auto", "mfma") else "dot2",
+            "pool_pages": batch.num_pages, "slots": r.num_slots, "kv_dtype": args.kv_dtype,
+            "decode_kernel": kernel,
             "parallelism": "single GPU",
         },
         "us_per_layer_step": round(ms_per_step * 1e3 / n_layers, 2),
@@ -548,7 +590,7 @@ def main():
             "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": "decode_mfma_kernel" if args.variant in ("auto", "mfma") else "decode_kernel",
+            "kernel": kernel,
             "avg_launch_us": round(decode_us, 2),
             "algorithmic_bytes_per_launch": layer_bytes,
             "merge_avg_launch_us": round(merge_us, 2),

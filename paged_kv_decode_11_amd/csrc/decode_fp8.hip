@@ -34,7 +34,7 @@
 //
 // K and V of the next two steps stream into registers while the current one
 // is computed (three steps in a ring), one wave per KV head as in the bf16
-// matrix-core kernel.  Page sizes 16, 32 and 64: each 16-token half of a
+// matrix-core kernel; Q waits in LDS.  Page sizes 16, 32 and 64: each 16-token half of a
 // step lies in one page, addressed through a buffer descriptor over that
 // page.
 
@@ -111,6 +111,7 @@ constexpr int kVRowBytes = 144;
 
 struct FShared {
   uint4 v[kStep * kVRowBytes / 16];  // V rows of the step by slot, kVRowBytes apart
+  uint4 q[4][64];                    // Q^T operand of MFMA j for lane l (see the kernel)
 };
 
 struct FStep {
@@ -159,7 +160,12 @@ __device__ __forceinline__ FRef f_ref(const FCtx& c, const FIds& ids, int s, int
   FRef r;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int64_t pg = safe_page(ids.id[h], c.num_pages, bad);
+    // The id was requested a step earlier.  Passing it through an empty asm
+    // here keeps its range check from being hoisted next to the load, where
+    // it would make the step wait for the scalar load before its prefetch.
+    int32_t id = ids.id[h];
+    asm volatile("" : "+s"(id));
+    const int64_t pg = safe_page(id, c.num_pages, bad);
     // raw buffer over one page (32-bit data format word as raw loads need);
     // offsets past the page read zeros
     r.page[h] = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(c.kv + pg * c.page_bytes), 0,
@@ -199,7 +205,7 @@ struct FState {
 // their V rows to zero (a slot past the sequence may hold any code).
 template <int G, bool kPrefetch, bool kLast>
 __device__ __forceinline__ void f_step(FState<G>& st, const FStep& cur, FStep& nxt,
-                                       const FCtx& c, const FRef& next, const uint4 (&qop)[4],
+                                       const FCtx& c, const FRef& next,
                                        int valid, int lane, float scale_log2, FShared& sh,
                                        uint32_t v_wr, uint32_t v_rd) {
   const int kg = lane >> 4;
@@ -227,15 +233,16 @@ __device__ __forceinline__ void f_step(FState<G>& st, const FStep& cur, FStep& n
 
   // S^T for both halves: A = K rows, B = Q^T; MFMA j takes head dims
   // 64 (j >> 1) + 16 kg + 8 (j & 1) .. + 7 at contraction slots 8 kg ..
-  floatx4_t s[2];
+  floatx4_t s[2] = {floatx4_t{0.f, 0.f, 0.f, 0.f}, floatx4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    s[h] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 4; ++j) {
+    // Q stays in LDS so that it holds no registers across the step
+    const uint4 qj = sh.q[j][lane];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int h = 0; h < 2; ++h) {
       const uint4 kw = cur.k[h][j >> 1];
       const uint4 ka = (j & 1) ? fp8x8_to_bf16(kw.z, kw.w) : fp8x8_to_bf16(kw.x, kw.y);
-      s[h] = mfma_bf16(ka, qop[j], s[h]);
+      s[h] = mfma_bf16(ka, qj, s[h]);
     }
   }
 
@@ -349,7 +356,8 @@ void decode_fp8_kernel(const uint16_t* __restrict__ q_ptr, const uint8_t* __rest
       c.v_lane = uint32_t(lane >> 3) * c.row_bytes + head + 16 * uint32_t(lane & 7);
 
       // Q^T operand: lane (row l & 15, kg) holds head dims
-      // 64 (j >> 1) + 16 kg + 8 (j & 1) .. + 7 for MFMA j; rows >= g are zero
+      // 64 (j >> 1) + 16 kg + 8 (j & 1) .. + 7 for MFMA j; rows >= g are zero.
+      // Loaded first, staged in LDS after the first steps' loads are issued.
       uint4 qop[4];
       {
         const uint16_t* qrow = q_ptr + (int64_t(req) * Hq + kh * G + row16) * kHeadDim + 16 * kg;
@@ -368,31 +376,52 @@ void decode_fp8_kernel(const uint16_t* __restrict__ q_ptr, const uint8_t* __rest
 
       int bad = 0;
       FStep ta, tb, tc;
+      // both loads unconditional (a one-step item reads its step twice): with
+      // the same loads in flight on every path, the wait counts stay exact
       f_load(ta, c, f_ref<P>(c, f_read_ids<P>(idx, len, 0), 0, bad));
-      if (nsteps > 1) f_load(tb, c, f_ref<P>(c, f_read_ids<P>(idx, len, 1), 1, bad));
+      f_load(tb, c, f_ref<P>(c, f_read_ids<P>(idx, len, min(1, nsteps - 1)), min(1, nsteps - 1),
+                             bad));
       FIds ids_next = f_read_ids<P>(idx, len, min(2, nsteps - 1));
       __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sh.q[j][lane] = qop[j];
+      __builtin_amdgcn_wave_barrier();
       const int last_valid = len - kStep * (nsteps - 1);
       const FRef none = {};
       int n = 0;
       auto step = [&](FStep& cur, FStep& nxt) -> bool {
         if (n == nsteps - 1) {
-          f_step<G, false, true>(st, cur, nxt, c, none, qop, last_valid, lane, scale_log2, sh,
+          f_step<G, false, true>(st, cur, nxt, c, none, last_valid, lane, scale_log2, sh,
                                  v_wr, v_rd);
           return true;
         }
         if (n + 2 < nsteps) {
           const FRef ref = f_ref<P>(c, ids_next, n + 2, bad);
           ids_next = f_read_ids<P>(idx, len, min(n + 3, nsteps - 1));
-          f_step<G, true, false>(st, cur, nxt, c, ref, qop, kStep, lane, scale_log2, sh, v_wr,
+          f_step<G, true, false>(st, cur, nxt, c, ref, kStep, lane, scale_log2, sh, v_wr,
                                  v_rd);
         } else {
-          f_step<G, false, false>(st, cur, nxt, c, none, qop, kStep, lane, scale_log2, sh, v_wr,
+          f_step<G, false, false>(st, cur, nxt, c, none, kStep, lane, scale_log2, sh, v_wr,
                                   v_rd);
         }
         ++n;
         return false;
       };
+      // Steady state: three prefetching steps per trip with the ring in
+      // place, straight-line, so no register tile is copied at a branch
+      // merge (a copy of a tile still in flight would wait for every load).
+      while (n + 4 < nsteps) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          FStep& cur = k == 0 ? ta : k == 1 ? tb : tc;
+          FStep& nxt = k == 0 ? tc : k == 1 ? ta : tb;
+          const FRef ref = f_ref<P>(c, ids_next, n + 2, bad);
+          ids_next = f_read_ids<P>(idx, len, min(n + 3, nsteps - 1));
+          f_step<G, true, false>(st, cur, nxt, c, ref, kStep, lane, scale_log2, sh, v_wr, v_rd);
+          ++n;
+        }
+      }
+      // the last one to four steps
       for (;;) {
         if (step(ta, tc)) break;
         if (step(tb, ta)) break;
