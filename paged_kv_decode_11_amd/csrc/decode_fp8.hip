@@ -34,7 +34,8 @@
 //
 // K and V of the next two steps stream into registers while the current one
 // is computed (three steps in a ring), one wave per KV head as in the bf16
-// matrix-core kernel; Q waits in LDS.  Page sizes 16, 32 and 64: each 16-token half of a
+// matrix-core kernel; Q waits in LDS.  The two waves that share a SIMD keep
+// pace through issue priority (see the steady-state loop).  Page sizes 16, 32 and 64: each 16-token half of a
 // step lies in one page, addressed through a buffer descriptor over that
 // page.
 
@@ -305,9 +306,16 @@ void decode_fp8_kernel(const uint16_t* __restrict__ q_ptr, const uint8_t* __rest
   static_assert(G >= 1 && G <= 8, "group size");
   static_assert(P == 16 || P == 32 || P == 64, "page size");
   __shared__ FShared shared[kMaxWavesPerBlock];
+  // steps each wave has completed; see the steady-state loop
+  __shared__ int progress[kMaxWavesPerBlock];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (lane == 0) progress[wave] = 0;
+  __syncthreads();
+  int done_steps = 0;
   const int nwaves = blockDim.x >> 6;
+  // every wave runs the same number of steps when the heads divide evenly
+  const bool lockstep = num_kv_heads % nwaves == 0;
   const int row16 = lane & 15;
   const int kg = lane >> 4;
   FShared& sh = shared[wave];
@@ -411,6 +419,25 @@ void decode_fp8_kernel(const uint16_t* __restrict__ q_ptr, const uint8_t* __rest
       // place, straight-line, so no register tile is copied at a branch
       // merge (a copy of a tile still in flight would wait for every load).
       while (n + 4 < nsteps) {
+        // Waves w and w + 4 share a SIMD, and when both can issue the older
+        // one does: left alone, w + 4 streams its head far slower than w
+        // (measured: waves 0-3 done at ~55% of the kernel's time), and the
+        // heads of one page are read far apart in time.  A workgroup barrier
+        // per trip (LDS-only, so the prefetch stays in flight) keeps the 8
+        // heads of each page within a few steps, and within a trip the wave
+        // of a pair that has done fewer steps takes priority.  Every wave
+        // meets the same number of barriers when the heads divide evenly
+        // over the waves (all waves walk the same items).
+        if (lockstep) lds_barrier();
+        if (nwaves == kMaxWavesPerBlock) {
+          __hip_atomic_store(&progress[wave], done_steps + n, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
+          if (done_steps + n < __hip_atomic_load(&progress[wave ^ 4], __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP))
+            __builtin_amdgcn_s_setprio(1);
+          else
+            __builtin_amdgcn_s_setprio(0);
+        }
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
           FStep& cur = k == 0 ? ta : k == 1 ? tb : tc;
@@ -428,6 +455,8 @@ void decode_fp8_kernel(const uint16_t* __restrict__ q_ptr, const uint8_t* __rest
         if (step(tc, tb)) break;
       }
       if (bad && lane == 0) err[0] = PKD_DEVERR_PAGE_ID;
+      __builtin_amdgcn_s_setprio(0);
+      done_steps += nsteps;
 
       // lane (row l & 15, kg) holds head dims 16 b + 4 kg + v of its row
       const float l_row = rows_sum(st.lp);
