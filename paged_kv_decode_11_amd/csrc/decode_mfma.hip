@@ -294,9 +294,16 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __re
                         int num_qo_heads, int num_kv_heads) {
   static_assert(G >= 1 && G <= 8, "group size");
   __shared__ MShared shared[kMaxWavesPerBlock];
+  // tiles each wave has completed; see the tile loop
+  __shared__ int progress[kMaxWavesPerBlock];
+  if ((threadIdx.x & 63) == 0) progress[threadIdx.x >> 6] = 0;
+  __syncthreads();
+  int done_tiles = 0;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
+  // every wave walks the same tiles when the heads divide evenly
+  const bool lockstep = num_kv_heads % nwaves == 0;
   const int row16 = lane & 15;
   const int kg = lane >> 4;
   MShared& sh = shared[wave];
@@ -398,11 +405,30 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __re
         return false;
       };
       for (;;) {
+        // Waves w and w + 4 share a SIMD, and when both can issue the older
+        // one does, so w + 4 falls behind and the heads of one page are read
+        // far apart in time.  A workgroup barrier every three tiles
+        // (LDS-only, so the prefetch stays in flight) keeps the heads
+        // together, and the wave of a pair with fewer tiles done takes issue
+        // priority.  Every wave meets the same number of barriers when the
+        // heads divide evenly over the waves (all waves walk the same items).
+        if (lockstep) lds_barrier();
+        if (nwaves == kMaxWavesPerBlock) {
+          __hip_atomic_store(&progress[wave], done_tiles + n, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
+          if (done_tiles + n < __hip_atomic_load(&progress[wave ^ 4], __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP))
+            __builtin_amdgcn_s_setprio(1);
+          else
+            __builtin_amdgcn_s_setprio(0);
+        }
         if (step(ta, tc)) break;
         if (step(tb, ta)) break;
         if (step(tc, tb)) break;
       }
       if (bad && lane == 0) err[0] = PKD_DEVERR_PAGE_ID;
+      __builtin_amdgcn_s_setprio(0);
+      done_tiles += ntiles;
 
       // final l per row: sum over the 16 token columns; rows 4 kg + v
       float lt[4];
