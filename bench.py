@@ -108,43 +108,53 @@ def cpu_baseline(batch, q_bits, cache_dev, o_dev, lse_dev, budget_s: float, fp8_
         blas = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         blas = 1
-    done, tokens, elapsed = [], 0, 0.0
+    done, tokens, elapsed, passes = [], 0, 0.0, 0
     o_gpu = o_dev.float().cpu().numpy()
     lse_gpu = lse_dev.cpu().numpy()
     err_o = err_l = 0.0
-    for i in range(batch.batch):
-        rows = batch.kv_indices[batch.kv_indptr[i]:batch.kv_indptr[i + 1]]
-        sel = torch.from_numpy(rows.astype(np.int64)).to(cache_dev.device)
-        n = rows.shape[0]
-        indptr = np.array([0, n], dtype=np.int32)
-        idx = np.arange(n, dtype=np.int32)
-        last = batch.kv_last_page_len[i:i + 1]
-        if fp8_scales is None:
-            host = cache_dev.index_select(0, sel).view(torch.int16).cpu().numpy().view(np.uint16)
+    host_pages = {}
+    # requests in order; when the layer is done inside the budget, it is
+    # decoded again (same inputs), so the timed sample is 10-30 s of work
+    while elapsed < budget_s:
+        passes += 1
+        for i in range(batch.batch):
+            rows = batch.kv_indices[batch.kv_indptr[i]:batch.kv_indptr[i + 1]]
+            n = rows.shape[0]
+            indptr = np.array([0, n], dtype=np.int32)
+            idx = np.arange(n, dtype=np.int32)
+            last = batch.kv_last_page_len[i:i + 1]
+            if i not in host_pages:
+                sel = torch.from_numpy(rows.astype(np.int64)).to(cache_dev.device)
+                if fp8_scales is None:
+                    host_pages[i] = cache_dev.index_select(0, sel).view(
+                        torch.int16).cpu().numpy().view(np.uint16)
+                else:
+                    host_pages[i] = cache_dev.view(torch.uint8).index_select(0, sel).cpu().numpy()
+            host = host_pages[i]
             t0 = time.perf_counter()
-            o_ref, lse_ref = att.decode(q_bits[i:i + 1], host, indptr, idx, last,
-                                        batch.num_kv_heads)
-        else:
-            host = cache_dev.view(torch.uint8).index_select(0, sel).cpu().numpy()
-            t0 = time.perf_counter()
-            o_ref, lse_ref = att.decode_fp8(q_bits[i:i + 1], host, indptr, idx, last,
-                                            batch.num_kv_heads, k_scale=fp8_scales[0],
-                                            v_scale=fp8_scales[1])
-        elapsed += time.perf_counter() - t0
-        err_o = max(err_o, float(np.max(np.abs(o_gpu[i] - o_ref[0]))))
-        err_l = max(err_l, float(np.max(np.abs(lse_gpu[i] - lse_ref[0]))))
-        done.append(i)
-        tokens += int(batch.kv_lens[i])
-        if elapsed >= budget_s:
-            break
+            if fp8_scales is None:
+                o_ref, lse_ref = att.decode(q_bits[i:i + 1], host, indptr, idx, last,
+                                            batch.num_kv_heads)
+            else:
+                o_ref, lse_ref = att.decode_fp8(q_bits[i:i + 1], host, indptr, idx, last,
+                                                batch.num_kv_heads, k_scale=fp8_scales[0],
+                                                v_scale=fp8_scales[1])
+            elapsed += time.perf_counter() - t0
+            if passes == 1:
+                err_o = max(err_o, float(np.max(np.abs(o_gpu[i] - o_ref[0]))))
+                err_l = max(err_l, float(np.max(np.abs(lse_gpu[i] - lse_ref[0]))))
+                done.append(i)
+            tokens += int(batch.kv_lens[i])
+            if elapsed >= budget_s:
+                break
     kv_bytes = tokens * batch.kv_bytes_per_token() // (1 if fp8_scales is None else 2)
     gbs = kv_bytes / elapsed / 1e9
     us_layer = elapsed * 1e6 * batch.total_tokens / tokens
     return {
         "value": round(gbs, 6), "unit": "GB/s", "cores": int(blas),
         "kind": "oracle",
-        "sample": f"layer 0, requests 0..{done[-1]} ({len(done)} of {batch.batch}, {tokens} KV tokens), "
-                  f"numpy fp64, {elapsed:.1f} s",
+        "sample": f"layer 0, requests 0..{done[-1]} ({len(done)} of {batch.batch}), "
+                  f"{passes} pass(es), {tokens} KV tokens decoded, numpy fp64, {elapsed:.1f} s",
         "us_per_layer_step": round(us_layer, 1),
         "affinity_cpus": len(os.sched_getaffinity(0)),
     }, {"max_abs_err_o": err_o, "max_abs_err_lse": err_l, "requests_checked": len(done)}
