@@ -100,13 +100,13 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
   const int num_slots = gridDim.x;
   const int32_t* slot_indptr = ws + plan_off_slots();
   const int32_t* items = ws + plan_off_items(num_slots);
-  const int32_t* kv_idx = ws + hdr[PKD_H_OFF_INDICES];
-  const int32_t* groups = ws + hdr[PKD_H_OFF_GROUPS];
+  const int off_indices = hdr[PKD_H_OFF_INDICES];
+  const int off_groups = hdr[PKD_H_OFF_GROUPS];
   const int rows_per_block = hdr[PKD_H_ROWS_PER_BLOCK];
-  const int64_t n_partials = hdr[PKD_H_PARTIALS];
+  const int partials = hdr[PKD_H_PARTIALS];
+  const int32_t* kv_idx = ws + off_indices;
+  const int32_t* groups = ws + off_groups;
   const int Hq = num_qo_heads;
-  float* o_part = fws;
-  float* lse_part = fws + n_partials * Hq * kHeadDim;
 
   const uint32_t row_bytes = uint32_t(num_kv_heads) * kHeadDim * 2;
   const uint64_t v_bytes = uint64_t(P) * row_bytes;
@@ -114,42 +114,34 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
   const char* kv = reinterpret_cast<const char*>(kv_ptr);
   int bad = 0;
 
+  // The slot's bounds and its first item sit at offsets fixed by the slot
+  // count, so they are read together with the header: the first tile loads
+  // wait for two round trips (item, then page ids), not four.
+  const int32_t* first = ws + plan_off_first(num_slots) + 8 * int64_t(blockIdx.x);
+  const int it_begin = slot_indptr[blockIdx.x];
   const int it_end = slot_indptr[blockIdx.x + 1];
-  for (int it = slot_indptr[blockIdx.x]; it < it_end; ++it) {
-    const int32_t* item = items + 8 * it;
-    const int grp = item[0];
-    const int32_t* idx = kv_idx + item[1];
-    const int out = item[4];
-    const int len = item[5];
-    const int block = item[6];
-    const int kh = item[7];
-    const int row0 = groups[4 * grp + 0];
-    const int rows = groups[4 * grp + 1];
-    const int kchunks = groups[4 * grp + 2];
+  int32_t fi[8];
+#pragma unroll
+  for (int f = 0; f < 8; ++f) fi[f] = first[f];
+  // keep the loads next to the bounds' (not sunk past the empty-slot test)
+  asm volatile("" ::"s"(fi[0]), "s"(fi[1]), "s"(fi[2]), "s"(fi[3]), "s"(fi[4]), "s"(fi[5]),
+               "s"(fi[6]), "s"(fi[7]), "s"(off_indices), "s"(off_groups), "s"(rows_per_block),
+               "s"(partials));
+  float* o_part = fws;
+  float* lse_part = fws + int64_t(partials) * Hq * kHeadDim;
+  for (int it = it_begin; it < it_end; ++it) {
+    int32_t itm[8];
+#pragma unroll
+    for (int f = 0; f < 8; ++f) itm[f] = it == it_begin ? fi[f] : items[8 * it + f];
+    const int grp = itm[0];
+    const int32_t* idx = kv_idx + itm[1];
+    const int out = itm[4];
+    const int len = itm[5];
+    const int block = itm[6];
+    const int kh = itm[7];
     const int ntiles = (len + kTile - 1) / kTile;
     const int last_valid = len - kTile * (ntiles - 1);
     const int last_token = len - 1;
-
-    // this wave's requests: first row (group-relative) and count
-    const int wrow = block * rows_per_block + wave * kReqPerWave;
-    const int nreq = min(kReqPerWave, rows - wrow);  // <= 0: the wave only loads
-    const bool compute = nreq > 0;
-
-    // q as the B operand: lane l holds query row l & 15 (request (l & 15) / g,
-    // head kh g + (l & 15) % g), head_dim elements 32 j + 8 kg .. + 8
-    uint4 qv[4];
-    {
-      const int i = row16 / G;
-      const bool have = compute && i < nreq;
-      const uint16_t* qrow =
-          q_ptr + ((int64_t(row0) + wrow + (have ? i : 0)) * Hq + kh * G + row16 % G) * kHeadDim +
-          kg * 8;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        qv[j] = have ? *reinterpret_cast<const uint4*>(qrow + 32 * j) : make_uint4(0u, 0u, 0u, 0u);
-    }
-
-    float m = kNegInf, lsum = 0.f;
     floatx4_t acc[8];
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) acc[cb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
@@ -176,6 +168,18 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
     int32_t pid[kDepth];
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) pid[d] = page_of(min(d, ntiles - 1));
+    // the group's rows are needed only for q, which is loaded after the
+    // first tile
+    const int row0 = groups[4 * grp + 0];
+    const int rows = groups[4 * grp + 1];
+    const int kchunks = groups[4 * grp + 2];
+    // this wave's requests: first row (group-relative) and count
+    const int wrow = block * rows_per_block + wave * kReqPerWave;
+    int nreq = 0;
+    bool compute = false;
+    // q as the B operand: lane l holds query row l & 15 (request (l & 15) / g,
+    // head kh g + (l & 15) % g), head_dim elements 32 j + 8 kg .. + 8
+    uint4 qv[4];
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
       const uint4* a = piece_addr(min(d, ntiles - 1), pid[d]);
@@ -183,8 +187,24 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
       rv[d] = load_stream16(reinterpret_cast<const char*>(a) + v_bytes);
       pid[d] = page_of(min(d + kDepth, ntiles - 1));
       __builtin_amdgcn_sched_barrier(0);
+      if (d == 0) {
+        nreq = min(kReqPerWave, rows - wrow);  // <= 0: the wave only loads
+        compute = nreq > 0;
+        const int i = row16 / G;
+        const bool have = compute && i < nreq;
+        const uint16_t* qrow = q_ptr +
+                               ((int64_t(row0) + wrow + (have ? i : 0)) * Hq + kh * G + row16 % G) *
+                                   kHeadDim +
+                               kg * 8;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          qv[j] =
+              have ? *reinterpret_cast<const uint4*>(qrow + 32 * j) : make_uint4(0u, 0u, 0u, 0u);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 
+    float m = kNegInf, lsum = 0.f;
     auto step = [&](uint4& sk, uint4& sv, int32_t& next_page, int n, bool reload) {
       const int stage = n & 1;
       const bool last = n == ntiles - 1;
