@@ -24,13 +24,14 @@
 //   * the online softmax per query row: a max over those 8 tokens and over
 //     the 4 lanes holding the same row (permlane swaps), exponentials in base
 //     2;
-//   * O += P V on the matrix cores (v_mfma_f32_16x16x32_bf16, 32 tokens per
-//     instruction, 8 column blocks of 16 elements of head_dim): P as bf16
-//     straight from the softmax registers is the A operand, and the
-//     transposing LDS read (ds_read_b64_tr_b16) gives each lane the B operand
-//     of its column: 4 consecutive tokens of each half.
-// The rescale factors and the final max and sum move from "row l & 15" to the
-// accumulator's "rows 4 (l >> 4) + v" layout through a per-wave LDS row.
+//   * O^T += V^T P^T on the matrix cores (v_mfma_f32_16x16x32_bf16, 32 tokens
+//     per instruction, 8 blocks of 16 elements of head_dim): the transposing
+//     LDS read (ds_read_b64_tr_b16) gives each lane the A operand of its head
+//     dim, 4 consecutive tokens of each half, and P as bf16 straight from the
+//     softmax registers is the B operand.  The product leaves lane l with
+//     query row l & 15 (head dims 16 b + 4 (l >> 4) + v), the row the
+//     softmax keeps in that lane, so rescale factors and the final max and
+//     sum never move between lanes.
 
 #include <hip/hip_runtime.h>
 
@@ -56,8 +57,6 @@ constexpr int kDepth = 8;   // tiles in flight per workgroup
 struct PShared {
   uint4 k[2][kTile][16];  // K tile, row r's 16-byte piece c at [r][c ^ (r & 15)]
   uint4 v[2][kTile][16];  // V tile, same layout
-  float xa[kWaves][16];   // per wave, per query row: rescale factor, then max
-  float xl[kWaves][16];   // per wave, per query row: final sum
 };
 
 __device__ __forceinline__ floatx4_t mfma32(uint4 a, uint4 b, floatx4_t c) {
@@ -251,18 +250,13 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
       }
       lsum = fmaf(lsum, alpha, ps);
       m = mn;
-      // rescale factors to the accumulator's row layout (rows 4 kg + v)
-      if (kg == 0) sh.xa[wave][row16] = alpha;
-      __builtin_amdgcn_wave_barrier();
-      const float4 a4 = *reinterpret_cast<const float4*>(&sh.xa[wave][4 * kg]);
-      __builtin_amdgcn_wave_barrier();
-      // P as the A operand: k = 8 kg + j <-> token 4 kg + j (j < 4) of the
+      // P^T as the B operand: k = 8 kg + j <-> token 4 kg + j (j < 4) of the
       // first half and 16 + 4 kg + j - 4 of the second
-      const uint4 pa = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+      const uint4 pb = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                   pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
-      // B operand of column block cb: lane (kg, i = 4 r + q) points the
-      // transposing read at row 4 kg + r, elements cb 16 + 4 q .. + 3 of each
-      // half
+      // V^T as the A operand of head-dim block cb: lane (kg, i = 4 r + q)
+      // points the transposing read at row 4 kg + r, elements cb 16 + 4 q ..
+      // + 3 of each half
       const int tr_row = 4 * kg + (row16 >> 2);
       const int tr_q = row16 & 3;
 #pragma unroll
@@ -275,11 +269,8 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
             8 * (tr_q & 1);
         const uint2 b0 = lds_read_tr(r0);
         const uint2 b1 = lds_read_tr(r1);
-        acc[cb][0] *= a4.x;
-        acc[cb][1] *= a4.y;
-        acc[cb][2] *= a4.z;
-        acc[cb][3] *= a4.w;
-        acc[cb] = mfma32(pa, make_uint4(b0.x, b0.y, b1.x, b1.y), acc[cb]);
+        acc[cb] *= alpha;
+        acc[cb] = mfma32(make_uint4(b0.x, b0.y, b1.x, b1.y), pb, acc[cb]);
       }
     };
 
@@ -296,39 +287,32 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
       if (full * kDepth + d < ntiles) step(rk[d], rv[d], pid[d], full * kDepth + d, false);
 
     if (compute) {
-      // final per-row max and sum, to the accumulator's row layout
+      // lane l: query row l & 15, head dims 16 cb + 4 kg + v
       const float lt = rows_sum(lsum);
-      if (kg == 0) {
-        sh.xa[wave][row16] = m;
-        sh.xl[wave][row16] = lt;
-      }
-      __builtin_amdgcn_wave_barrier();
-      const float4 m4 = *reinterpret_cast<const float4*>(&sh.xa[wave][4 * kg]);
-      const float4 l4 = *reinterpret_cast<const float4*>(&sh.xl[wave][4 * kg]);
-      __builtin_amdgcn_wave_barrier();
-      const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = 4 * kg + v;  // query row of the wave
-        const int i = r / G;
-        if (i >= nreq) continue;
+      const int i = row16 / G;
+      if (i < nreq) {
         const int req_in_group = wrow + i;
-        const int64_t qh = int64_t(kh) * G + r % G;
-        const float inv = 1.f / lv[v];
-        const float lse_nat = (mv[v] + __log2f(lv[v])) * kLn2;
+        const int64_t qh = int64_t(kh) * G + row16 % G;
+        const float inv = 1.f / lt;
+        const float lse_nat = (m + __log2f(lt)) * kLn2;
         if (out < 0) {
-          uint16_t* orow = o_ptr + ((int64_t(row0) + req_in_group) * Hq + qh) * kHeadDim + row16;
+          uint16_t* orow =
+              o_ptr + ((int64_t(row0) + req_in_group) * Hq + qh) * kHeadDim + 4 * kg;
 #pragma unroll
           for (int cb = 0; cb < 8; ++cb)
-            orow[cb * 16] = uint16_t(pack_bf16x2(acc[cb][v] * inv, 0.f) & 0xffffu);
-          if (lse_ptr && row16 == 0) lse_ptr[(int64_t(row0) + req_in_group) * Hq + qh] = lse_nat;
+            *reinterpret_cast<uint2*>(orow + 16 * cb) =
+                make_uint2(pack_bf16x2(acc[cb][0] * inv, acc[cb][1] * inv),
+                           pack_bf16x2(acc[cb][2] * inv, acc[cb][3] * inv));
+          if (lse_ptr && kg == 0) lse_ptr[(int64_t(row0) + req_in_group) * Hq + qh] = lse_nat;
         } else {
           const int64_t pid_out = int64_t(out) + int64_t(req_in_group) * kchunks;
-          float* prow = o_part + (pid_out * Hq + qh) * kHeadDim + row16;
+          float* prow = o_part + (pid_out * Hq + qh) * kHeadDim + 4 * kg;
 #pragma unroll
-          for (int cb = 0; cb < 8; ++cb) prow[cb * 16] = acc[cb][v] * inv;
-          if (row16 == 0) lse_part[pid_out * Hq + qh] = lse_nat;
+          for (int cb = 0; cb < 8; ++cb)
+            *reinterpret_cast<float4*>(prow + 16 * cb) =
+                make_float4(acc[cb][0] * inv, acc[cb][1] * inv, acc[cb][2] * inv,
+                            acc[cb][3] * inv);
+          if (kg == 0) lse_part[pid_out * Hq + qh] = lse_nat;
         }
       }
     }
