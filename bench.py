@@ -53,8 +53,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="oracle time budget for cpu_baseline (0 disables)")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--variant", default="auto", choices=["auto", "dot2", "mfma"],
-                    help="decode kernel (auto = the matrix-core kernel)")
+    ap.add_argument("--variant", default="auto", choices=["auto", "dot2", "mfma", "mfma_pv"],
+                    help="decode kernel (auto = the library's default for the shape)")
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "e4m3"],
                     help="KV cache element type (e4m3: FP8 codes with per-tensor scales)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -68,6 +68,7 @@ KERNEL_FILES = {
     "decode_mfma_kernel": ("decode_mfma.hip", "device_common.h", "plan_layout.h"),
     "decode_kernel": ("decode.hip", "device_common.h", "plan_layout.h"),
     "decode_fp8_kernel": ("decode_fp8.hip", "device_common.h", "plan_layout.h"),
+    "decode_pv_kernel": ("decode_pv.hip", "device_common.h", "plan_layout.h"),
 }
 
 
@@ -433,8 +434,7 @@ def main():
     if fp8 and (args.variant == "dot2" or args.workload in ("token_sparse", "tiny")):
         raise SystemExit("an e4m3 cache runs on the matrix-core kernel with page sizes 16-64")
     kv_tok = batch.kv_bytes_per_token() // (2 if fp8 else 1)
-    kernel = ("decode_fp8_kernel" if fp8 else
-              "decode_mfma_kernel" if args.variant in ("auto", "mfma") else "decode_kernel")
+    kernel = None  # set from the library's plan below
     layer_bytes = batch.total_tokens * kv_tok
     if spec.num_layers > 1:
         n_layers, distinct = spec.num_layers, 2
@@ -493,6 +493,11 @@ def main():
         for layer in range(n_layers):
             run(layer)
 
+    plan()
+    kernel = ("decode_fp8_kernel" if fp8 else
+              {"mfma": "decode_mfma_kernel", "mfma_pv": "decode_pv_kernel",
+               "dot2": "decode_kernel"}[r.planned_variant])
+    log(f"decode kernel: {kernel}")
     # plan host cost, on its own
     torch.cuda.synchronize()
     plan_us = []

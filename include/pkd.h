@@ -88,9 +88,12 @@ typedef struct pkd_plan_opts {
 /* Decode kernels.  Both compute the same result (to rounding); they differ
  * in where q.k is evaluated. */
 enum {
-  PKD_VARIANT_AUTO = 0, /* the matrix-core kernel */
-  PKD_VARIANT_DOT2 = 1, /* q.k with packed bf16 dot products on the vector ALUs */
-  PKD_VARIANT_MFMA = 2  /* q.k as a 16 x 16 tile on the matrix cores (GQA group as rows) */
+  PKD_VARIANT_AUTO = 0,    /* PKD_VARIANT_MFMA_PV for group size 8 with pages of 16-64 tokens
+                              (measured faster there), PKD_VARIANT_MFMA otherwise */
+  PKD_VARIANT_DOT2 = 1,    /* q.k with packed bf16 dot products on the vector ALUs */
+  PKD_VARIANT_MFMA = 2,    /* q.k as a 16 x 16 tile on the matrix cores (GQA group as rows),
+                              p.v on the vector ALUs */
+  PKD_VARIANT_MFMA_PV = 3  /* both q.k and p.v on the matrix cores (page sizes 16, 32, 64) */
 };
 
 /* ---------------------------------------------------------------------
@@ -174,6 +177,11 @@ enum {
 int pkd_create(pkd_handle** out, int32_t device, int32_t num_slots);
 int pkd_destroy(pkd_handle* h);
 int32_t pkd_num_slots(const pkd_handle* h);
+
+/* The decode kernel runs of the handle's current plan launch (PKD_VARIANT_DOT2,
+ * _MFMA or _MFMA_PV: PKD_VARIANT_AUTO resolved for the plan's shape); 0
+ * before any plan. */
+int32_t pkd_planned_variant(const pkd_handle* h);
 /* Id of the last successful plan on this handle (0 before any); lets an
  * engine assert that the plan matches its batch (aicassindra, "What to do
  * next", item 3). */

@@ -27,7 +27,9 @@ PKD_DEVERR_PAGE_ID = 1
 PKD_VARIANT_AUTO = 0
 PKD_VARIANT_DOT2 = 1
 PKD_VARIANT_MFMA = 2
-VARIANTS = {"auto": PKD_VARIANT_AUTO, "dot2": PKD_VARIANT_DOT2, "mfma": PKD_VARIANT_MFMA}
+PKD_VARIANT_MFMA_PV = 3
+VARIANTS = {"auto": PKD_VARIANT_AUTO, "dot2": PKD_VARIANT_DOT2, "mfma": PKD_VARIANT_MFMA,
+            "mfma_pv": PKD_VARIANT_MFMA_PV}
 
 HEADER_BASE = 32
 PKD_PLAN_DECODE, PKD_PLAN_SHARED = 0, 1
@@ -63,6 +65,7 @@ SIGNATURES = {
     "pkd_destroy": (ctypes.c_int, [_vp]),
     "pkd_num_slots": (_i32, [_vp]),
     "pkd_plan_id": (_i64, [_vp]),
+    "pkd_planned_variant": (_i32, [_vp]),
     "pkd_last_error": (ctypes.c_char_p, []),
     "pkd_int_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "pkd_float_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),

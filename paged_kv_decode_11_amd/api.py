@@ -145,6 +145,13 @@ class DecodePlanRun:
     def plan_id(self) -> int:
         return int(self._L.pkd_plan_id(self._h))
 
+    @property
+    def planned_variant(self) -> str:
+        """The decode kernel runs of the current plan launch ('dot2', 'mfma',
+        'mfma_pv'; '' before any plan)."""
+        v = int(self._L.pkd_planned_variant(self._h))
+        return {code: name for name, code in _lib.VARIANTS.items() if name != "auto"}.get(v, "")
+
     def plan(self, kv_indptr, kv_indices, kv_last_page_len, num_qo_heads: int, num_kv_heads: int,
              head_dim: int, page_size: int, q_data_type=None, kv_data_type=None,
              kv_layout: str = "NHD", stream=None, **opts):

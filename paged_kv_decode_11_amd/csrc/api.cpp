@@ -202,6 +202,8 @@ int pkd_destroy(pkd_handle* h) {
 
 int32_t pkd_num_slots(const pkd_handle* h) { return h ? h->num_slots : 0; }
 
+int32_t pkd_planned_variant(const pkd_handle* h) { return h && h->planned ? h->variant : 0; }
+
 int64_t pkd_plan_id(const pkd_handle* h) { return h && h->planned ? h->plan_counter : 0; }
 
 size_t pkd_int_workspace_bytes(int32_t max_batch, int32_t max_nnz, int32_t num_slots) {
@@ -300,8 +302,14 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
     return fail(PKD_ERR_INVALID_ARG, "workspaces must be 256-byte aligned");
 
   const int32_t variant = opts ? opts->variant : PKD_VARIANT_AUTO;
-  if (variant != PKD_VARIANT_AUTO && variant != PKD_VARIANT_DOT2 && variant != PKD_VARIANT_MFMA)
+  if (variant != PKD_VARIANT_AUTO && variant != PKD_VARIANT_DOT2 && variant != PKD_VARIANT_MFMA &&
+      variant != PKD_VARIANT_MFMA_PV)
     return fail(PKD_ERR_INVALID_ARG, "unknown decode kernel variant");
+  if (variant == PKD_VARIANT_MFMA_PV &&
+      (kv_dtype != PKD_DTYPE_BF16 || !pkd::pv_variant_built(num_qo_heads / num_kv_heads, page_size)))
+    return fail(PKD_ERR_UNSUPPORTED,
+                "the PKD_VARIANT_MFMA_PV kernel is built for a bf16 cache, group size 1, 2, 4 or 8 "
+                "and page_size 16, 32 or 64");
   if (variant == PKD_VARIANT_DOT2 && kv_dtype == PKD_DTYPE_FP8_E4M3)
     return fail(PKD_ERR_UNSUPPORTED, "an fp8 e4m3 cache has only the matrix-core kernel");
 
@@ -379,7 +387,15 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
   h->P = page_size;
   h->q_dtype = q_dtype;
   h->kv_dtype = kv_dtype;
-  h->variant = variant == PKD_VARIANT_DOT2 ? PKD_VARIANT_DOT2 : PKD_VARIANT_MFMA;
+  // group size 8 streams faster with p.v on the matrix cores; smaller groups
+  // keep it on the vector ALUs (measured on the benchmark workloads)
+  if (variant == PKD_VARIANT_AUTO)
+    h->variant = kv_dtype == PKD_DTYPE_BF16 && num_qo_heads / num_kv_heads == 8 &&
+                         pkd::pv_variant_built(8, page_size)
+                     ? PKD_VARIANT_MFMA_PV
+                     : PKD_VARIANT_MFMA;
+  else
+    h->variant = variant;
   h->layout = layout;
   h->int_ws = int_workspace;
   h->int_bytes = int_workspace_bytes;
@@ -503,6 +519,8 @@ int pkd_run_scaled(pkd_handle* h, const void* q, int32_t batch, const void* kv_c
     e = pkd::launch_prefix_mfma(dp, h->Hq / h->Hkv, h->P, h->num_slots, s);
   else if (h->kv_dtype == PKD_DTYPE_FP8_E4M3)
     e = pkd::launch_decode_fp8(dp, h->Hq / h->Hkv, h->P, h->num_slots, s);
+  else if (h->variant == PKD_VARIANT_MFMA_PV)
+    e = pkd::launch_decode_pv(dp, h->Hq / h->Hkv, h->P, h->num_slots, s);
   else if (h->variant == PKD_VARIANT_DOT2)
     e = pkd::launch_decode(dp, h->Hq / h->Hkv, h->P, h->num_slots, s);
   else

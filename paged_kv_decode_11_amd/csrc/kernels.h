@@ -50,6 +50,10 @@ hipError_t launch_decode(const DecodeParams& p, int g, int page_size, int num_sl
 hipError_t launch_decode_mfma(const DecodeParams& p, int g, int page_size, int num_slots,
                               hipStream_t stream);
 bool decode_variant_built(int g, int page_size);
+// ... or with both products on the matrix cores (decode_pv.hip; pages of 16-64).
+hipError_t launch_decode_pv(const DecodeParams& p, int g, int page_size, int num_slots,
+                            hipStream_t stream);
+bool pv_variant_built(int g, int page_size);
 // Decode over an E4M3 cache (decode_fp8.hip): both products on the matrix
 // cores, V transposed through LDS.
 hipError_t launch_decode_fp8(const DecodeParams& p, int g, int page_size, int num_slots,

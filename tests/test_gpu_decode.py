@@ -11,7 +11,7 @@ from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = ["dot2", "mfma"]
+VARIANTS = ["dot2", "mfma", "mfma_pv"]
 
 
 def _small(seed, lens, P, Hq, Hkv, poison=True, spare=9):
@@ -66,6 +66,8 @@ def test_tiny_forced_splits(fixed, variant):
 @pytest.mark.parametrize("P", [1, 2, 4, 8, 16, 32, 64])
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
 def test_page_sizes_and_groups(P, G, variant):
+    if variant == "mfma_pv" and P < 16:
+        pytest.skip("the both-products-on-matrix-cores kernel is built for pages of 16-64 tokens")
     Hkv = 8 if G <= 4 else 4
     lens = sorted(set(workloads.edge_lengths(P) + [3 * P + 5, 77, 300]))
     batch, q, cache = _small(10 * P + G, lens, P, Hkv * G, Hkv)
@@ -131,12 +133,33 @@ def test_outputs_are_deterministic(variant):
 
 
 def test_variants_agree():
-    """The two kernels compute the same states; they may differ only in
-    rounding of the fp32 arithmetic."""
+    """The kernels compute the same states; they may differ only in rounding
+    (fp32 arithmetic, and the probabilities' high-and-low bf16 split in the
+    mfma_pv kernel)."""
     batch, q, cache = _small(13, [1, 17, 300, 2000, 4999], 16, 32, 8)
     qd, cd = gu.bits_to_dev(q), gu.bits_to_dev(cache)
     o1, l1 = gu.decode(batch, qd, cd, variant="dot2")
-    o2, l2 = gu.decode(batch, qd, cd, variant="mfma")
-    gu.check_o(gu.dev_to_f64(o2), gu.dev_to_f64(o1), "mfma-vs-dot2")
-    gu.check_lse(l2.cpu().numpy().astype(np.float64), l1.cpu().numpy().astype(np.float64),
-                 "mfma-vs-dot2")
+    for other in ("mfma", "mfma_pv"):
+        o2, l2 = gu.decode(batch, qd, cd, variant=other)
+        gu.check_o(gu.dev_to_f64(o2), gu.dev_to_f64(o1), f"{other}-vs-dot2")
+        gu.check_lse(l2.cpu().numpy().astype(np.float64), l1.cpu().numpy().astype(np.float64),
+                     f"{other}-vs-dot2")
+
+
+def test_auto_variant_by_shape():
+    """The default kernel: both products on the matrix cores for group size 8
+    with pages of 16-64 tokens, p.v on the vector ALUs otherwise; explicit
+    variants are kept."""
+    import torch
+
+    r = gu.runner(max_batch=64, max_nnz=1 << 12)
+    for P, Hq, Hkv, want in ((16, 64, 8, "mfma_pv"), (64, 8, 1, "mfma_pv"), (8, 64, 8, "mfma"),
+                             (16, 32, 8, "mfma"), (16, 8, 8, "mfma")):
+        batch, q, cache = _small(3, [40, 7], P, Hq, Hkv)
+        idx = torch.from_numpy(batch.kv_indices).cuda()
+        r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, Hq, Hkv, 128, P)
+        assert r.planned_variant == want, (P, Hq, Hkv, r.planned_variant)
+    r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, 8, 8, 128, 16, variant="mfma_pv")
+    assert r.planned_variant == "mfma_pv"
+    r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, 8, 8, 128, 16, variant="dot2")
+    assert r.planned_variant == "dot2"

@@ -49,6 +49,20 @@ def test_llama8b_layer_full_size():
     _sampled_check("llama8b_step", [int(np.argmax(lens)), int(np.argmin(lens)), 17])
 
 
+def test_wide_gqa_full_size_pv_kernel():
+    _, _, b = workloads.workload("wide_gqa")
+    lens = b["main"].kv_lens
+    order = np.argsort(lens)
+    _sampled_check("wide_gqa", [int(order[-1]), int(order[0]), int(order[128])], used_only=True,
+                   variant="mfma_pv")
+
+
+def test_llama8b_layer_full_size_pv_kernel():
+    _, _, b = workloads.workload("llama8b_step")
+    lens = b["main"].kv_lens
+    _sampled_check("llama8b_step", [int(np.argmax(lens)), 5], variant="mfma_pv")
+
+
 def test_wide_gqa_full_size():
     _, _, b = workloads.workload("wide_gqa")
     lens = b["main"].kv_lens
