@@ -387,15 +387,22 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
   h->P = page_size;
   h->q_dtype = q_dtype;
   h->kv_dtype = kv_dtype;
-  // group size 8 streams faster with p.v on the matrix cores; smaller groups
-  // keep it on the vector ALUs (measured on the benchmark workloads)
-  if (variant == PKD_VARIANT_AUTO)
-    h->variant = kv_dtype == PKD_DTYPE_BF16 && num_qo_heads / num_kv_heads == 8 &&
-                         pkd::pv_variant_built(8, page_size)
-                     ? PKD_VARIANT_MFMA_PV
-                     : PKD_VARIANT_MFMA;
-  else
+  // The default kernel, by measurement on 64 requests of 3-5k tokens: pages
+  // below 16 tokens stream faster through the dot-product kernel (its
+  // per-token rows suit them; 1.2-1.5x); group size 8 with larger pages
+  // faster with p.v on the matrix cores (1.3x); otherwise the matrix-core
+  // q.k kernel leads.  An FP8 cache has its own kernel.
+  if (variant == PKD_VARIANT_AUTO) {
+    const int g = num_qo_heads / num_kv_heads;
+    if (kv_dtype == PKD_DTYPE_BF16 && page_size < 16)
+      h->variant = PKD_VARIANT_DOT2;
+    else if (kv_dtype == PKD_DTYPE_BF16 && g == 8 && pkd::pv_variant_built(g, page_size))
+      h->variant = PKD_VARIANT_MFMA_PV;
+    else
+      h->variant = PKD_VARIANT_MFMA;
+  } else {
     h->variant = variant;
+  }
   h->layout = layout;
   h->int_ws = int_workspace;
   h->int_bytes = int_workspace_bytes;
