@@ -419,25 +419,9 @@ void decode_fp8_kernel(const uint16_t* __restrict__ q_ptr, const uint8_t* __rest
       // place, straight-line, so no register tile is copied at a branch
       // merge (a copy of a tile still in flight would wait for every load).
       while (n + 4 < nsteps) {
-        // Waves w and w + 4 share a SIMD, and when both can issue the older
-        // one does: left alone, w + 4 streams its head far slower than w
-        // (measured: waves 0-3 done at ~55% of the kernel's time), and the
-        // heads of one page are read far apart in time.  A workgroup barrier
-        // per trip (LDS-only, so the prefetch stays in flight) keeps the 8
-        // heads of each page within a few steps, and within a trip the wave
-        // of a pair that has done fewer steps takes priority.  Every wave
-        // meets the same number of barriers when the heads divide evenly
-        // over the waves (all waves walk the same items).
-        if (lockstep) lds_barrier();
-        if (nwaves == kMaxWavesPerBlock) {
-          __hip_atomic_store(&progress[wave], done_steps + n, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_WORKGROUP);
-          if (done_steps + n < __hip_atomic_load(&progress[wave ^ 4], __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_WORKGROUP))
-            __builtin_amdgcn_s_setprio(1);
-          else
-            __builtin_amdgcn_s_setprio(0);
-        }
+        // keep the waves of the workgroup together, once per trip (left alone,
+        // waves 4-7 finished their heads at ~1.75x the time of waves 0-3)
+        keep_pace<kMaxWavesPerBlock>(progress, wave, nwaves, lockstep, done_steps + n);
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
           FStep& cur = k == 0 ? ta : k == 1 ? tb : tc;

@@ -405,23 +405,9 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __re
         return false;
       };
       for (;;) {
-        // Waves w and w + 4 share a SIMD, and when both can issue the older
-        // one does, so w + 4 falls behind and the heads of one page are read
-        // far apart in time.  A workgroup barrier every three tiles
-        // (LDS-only, so the prefetch stays in flight) keeps the heads
-        // together, and the wave of a pair with fewer tiles done takes issue
-        // priority.  Every wave meets the same number of barriers when the
-        // heads divide evenly over the waves (all waves walk the same items).
-        if (lockstep) lds_barrier();
-        if (nwaves == kMaxWavesPerBlock) {
-          __hip_atomic_store(&progress[wave], done_tiles + n, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_WORKGROUP);
-          if (done_tiles + n < __hip_atomic_load(&progress[wave ^ 4], __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_WORKGROUP))
-            __builtin_amdgcn_s_setprio(1);
-          else
-            __builtin_amdgcn_s_setprio(0);
-        }
+        // keep the waves of the workgroup together, every three tiles (all
+        // waves walk the same items, so they meet the same barriers)
+        keep_pace<kMaxWavesPerBlock>(progress, wave, nwaves, lockstep, done_tiles + n);
         if (step(ta, tc)) break;
         if (step(tb, ta)) break;
         if (step(tc, tb)) break;

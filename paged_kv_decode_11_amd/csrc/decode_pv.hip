@@ -322,22 +322,8 @@ void decode_pv_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __rest
       // place, straight-line, so no register tile is copied at a branch
       // merge (a copy of a tile still in flight would wait for every load).
       while (n + 4 < ntiles) {
-        // Waves w and w + 4 share a SIMD, and when both can issue the older
-        // one does.  A workgroup barrier per trip (LDS-only, so the prefetch
-        // stays in flight) keeps the heads of a page together in time, and
-        // the wave of a pair with fewer tiles done takes issue priority.
-        // Every wave meets the same number of barriers when the heads divide
-        // evenly over the waves (all waves walk the same items).
-        if (lockstep) lds_barrier();
-        if (nwaves == kMaxWavesPerBlock) {
-          __hip_atomic_store(&progress[wave], done_tiles + n, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_WORKGROUP);
-          if (done_tiles + n < __hip_atomic_load(&progress[wave ^ 4], __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_WORKGROUP))
-            __builtin_amdgcn_s_setprio(1);
-          else
-            __builtin_amdgcn_s_setprio(0);
-        }
+        // keep the waves of the workgroup together, once per trip
+        keep_pace<kMaxWavesPerBlock>(progress, wave, nwaves, lockstep, done_tiles + n);
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
           VTile& cur = k == 0 ? ta : k == 1 ? tb : tc;

@@ -120,6 +120,29 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Keeping the waves of a workgroup together.  Waves w and w + 4 of an
+// 8-wave workgroup share a SIMD, and when both can issue, the older one does,
+// so w + 4 falls behind and the heads of one page get read far apart in time.
+// Called once per few tiles by every wave: a workgroup barrier with LDS-only
+// fences (the wave's prefetch stays in flight), taken only when `lockstep`
+// (every wave then meets the same number of calls), and issue priority for
+// the wave of its pair that has done fewer tiles.  `progress` is a
+// workgroup-shared array of one counter per wave (LDS); `done` counts this
+// wave's tiles so far.
+template <int kWaves>
+__device__ __forceinline__ void keep_pace(int* progress, int wave, int nwaves, bool lockstep,
+                                          int done) {
+  if (lockstep) lds_barrier();
+  if (nwaves == kWaves) {
+    __hip_atomic_store(&progress[wave], done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (done < __hip_atomic_load(&progress[wave ^ (kWaves / 2)], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP))
+      __builtin_amdgcn_s_setprio(1);
+    else
+      __builtin_amdgcn_s_setprio(0);
+  }
+}
+
 // A page id outside [0, num_pages) is replaced by page 0 and remembered.
 __device__ __forceinline__ int64_t safe_page(int32_t id, int64_t num_pages, int& bad) {
   const bool ok = id >= 0 && id < num_pages;
