@@ -114,7 +114,13 @@ enum {
  *                                 Items, 8 ints each: request, page_begin
  *                                 (index into kv_indices), num_pages,
  *                                 last_len, out (partial id, -1 = write the
- *                                 final output directly), length, 0, 0
+ *                                 final output directly), length, id0, id1.
+ *                                 id0, id1 are 0 in the image pkd_plan_host
+ *                                 returns; in pkd_plan's device copy (items
+ *                                 and first-item rows of decode plans) they
+ *                                 are the page ids kv_indices[page_begin]
+ *                                 and kv_indices[page_begin + 1] (the first
+ *                                 twice for a one-page item)
  *   [off_merge, +4*n_split)       split requests in ascending order: request,
  *                                 first partial id, number of partials, 0
  *   [off_groups, +4*num_groups)   shared-prefix plans only: per group, its

@@ -369,9 +369,15 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
     h->host_view_for = host_workspace;
   }
   int32_t* dev = static_cast<int32_t*>(int_workspace);
+  // the item rows of a decode plan (the first-item table and the items,
+  // contiguous) get their items' first two page ids on the device, in words 6
+  // and 7; a shared-prefix plan keeps row block and head there
+  const int64_t item_rows =
+      layout.kind == PKD_PLAN_DECODE ? int64_t(h->num_slots) + layout.num_items : 0;
   e = pkd::launch_plan_upload(h->host_view + half * half_ints + PKD_HEADER_BASE,
                               dev + PKD_HEADER_BASE, layout.off_indices - PKD_HEADER_BASE,
-                              kv_indices, dev + layout.off_indices, layout.nnz, s);
+                              kv_indices, dev + layout.off_indices, layout.nnz,
+                              layout.off_first - PKD_HEADER_BASE, item_rows, s);
   if (e != hipSuccess) return hip_fail(e, "plan upload kernel");
   e = hipEventRecord(h->staging_done[half], s);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");

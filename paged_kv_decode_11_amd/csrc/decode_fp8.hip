@@ -308,6 +308,25 @@ void decode_fp8_kernel(const uint16_t* __restrict__ q_ptr, const uint8_t* __rest
   __shared__ FShared shared[kMaxWavesPerBlock];
   // steps each wave has completed; see the steady-state loop
   __shared__ int progress[kMaxWavesPerBlock];
+
+  // The slot's bounds, its first item (with the ids of that item's first two
+  // pages) and the header fields sit at offsets fixed by the slot count (the
+  // grid size): requested together, waited for at once (the empty asm), one
+  // round trip to memory before the first loads of K and V.
+  const int32_t* hdr = ws + PKD_HEADER_BASE;
+  const int num_slots = gridDim.x;
+  const int32_t* slot_indptr = ws + plan_off_slots();
+  const int32_t* first = ws + plan_off_first(num_slots) + 8 * int64_t(blockIdx.x);
+  const int32_t* items = ws + plan_off_items(num_slots);
+  const int it_begin = slot_indptr[blockIdx.x];
+  const int it_end = slot_indptr[blockIdx.x + 1];
+  const int first_req = first[0], first_page = first[1], first_out = first[4],
+            first_len = first[5], first_id0 = first[6], first_id1 = first[7];
+  const int off_indices = hdr[PKD_H_OFF_INDICES];
+  const int partials = hdr[PKD_H_PARTIALS];
+  asm volatile("" ::"s"(it_begin), "s"(it_end), "s"(first_req), "s"(first_page), "s"(first_out),
+               "s"(first_len), "s"(first_id0), "s"(first_id1), "s"(off_indices), "s"(partials));
+
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (lane == 0) progress[wave] = 0;
@@ -324,13 +343,8 @@ void decode_fp8_kernel(const uint16_t* __restrict__ q_ptr, const uint8_t* __rest
   const uint32_t v_wr = uint32_t(v_slot(lane >> 3)) * kVRowBytes + 16 * uint32_t(lane & 7);
   const uint32_t v_rd = uint32_t(8 * kg + (row16 >> 1)) * kVRowBytes + 8 * uint32_t(lane & 1);
 
-  const int32_t* hdr = ws + PKD_HEADER_BASE;
-  const int num_slots = gridDim.x;
-  const int32_t* slot_indptr = ws + plan_off_slots();
-  const int32_t* first = ws + plan_off_first(num_slots) + 8 * int64_t(blockIdx.x);
-  const int32_t* items = ws + plan_off_items(num_slots);
-  const int32_t* kv_idx = ws + hdr[PKD_H_OFF_INDICES];
-  const int64_t n_partials = hdr[PKD_H_PARTIALS];
+  const int32_t* kv_idx = ws + off_indices;
+  const int64_t n_partials = partials;
   const int Hq = num_qo_heads;
   float* o_part = fws;
   float* lse_part = fws + n_partials * Hq * kHeadDim;
@@ -342,18 +356,18 @@ void decode_fp8_kernel(const uint16_t* __restrict__ q_ptr, const uint8_t* __rest
   c.v_bytes = uint32_t(P) * c.row_bytes;
   c.page_bytes = 2 * c.v_bytes;
 
-  const int it_begin = slot_indptr[blockIdx.x];
-  const int it_end = slot_indptr[blockIdx.x + 1];
-  const int first_req = first[0], first_page = first[1], first_out = first[4],
-            first_len = first[5];
   for (int it = it_begin; it < it_end; ++it) {
-    int req = first_req, page_begin = first_page, out = first_out, len = first_len;
+    // an item row carries the ids of the item's first two pages
+    int req = first_req, page_begin = first_page, out = first_out, len = first_len,
+        id0 = first_id0, id1 = first_id1;
     if (it != it_begin) {
       const int32_t* item = items + 8 * it;
       req = item[0];
       page_begin = item[1];
       out = item[4];
       len = item[5];
+      id0 = item[6];
+      id1 = item[7];
     }
     const int32_t* idx = kv_idx + page_begin;
     const int nsteps = (len + kStep - 1) / kStep;
@@ -386,9 +400,21 @@ void decode_fp8_kernel(const uint16_t* __restrict__ q_ptr, const uint8_t* __rest
       FStep ta, tb, tc;
       // both loads unconditional (a one-step item reads its step twice): with
       // the same loads in flight on every path, the wait counts stay exact
-      f_load(ta, c, f_ref<P>(c, f_read_ids<P>(idx, len, 0), 0, bad));
-      f_load(tb, c, f_ref<P>(c, f_read_ids<P>(idx, len, min(1, nsteps - 1)), min(1, nsteps - 1),
-                             bad));
+      // Step 0 lies in the item's first two pages (one, for P >= 32), whose
+      // ids the item row holds; so does step 1 for P >= 32 (page 1 for
+      // P = 32: the first page again when the item has one page, as then it
+      // has one step).  For P = 16 step 1 needs the page table.
+      FIds ids0, ids1;
+      ids0.id[0] = id0;
+      ids0.id[1] = P == 16 ? id1 : id0;
+      f_load(ta, c, f_ref<P>(c, ids0, 0, bad));
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (P == 16) {
+        ids1 = f_read_ids<P>(idx, len, min(1, nsteps - 1));
+      } else {
+        ids1.id[0] = ids1.id[1] = P == 32 ? id1 : id0;
+      }
+      f_load(tb, c, f_ref<P>(c, ids1, min(1, nsteps - 1), bad));
       FIds ids_next = f_read_ids<P>(idx, len, min(2, nsteps - 1));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll

@@ -121,6 +121,22 @@ __device__ __forceinline__ MIds<P> m_read_ids(const int32_t* idx, int len, int t
   return ids;
 }
 
+// Ids of tile t (0 or 1) of an item.  With pages of 16 tokens or more both
+// tiles lie in the item's first two pages, whose ids the item row carries
+// (`id`): no read of the page table stands between an item's row and its
+// first loads.
+template <int P>
+__device__ __forceinline__ MIds<P> m_start_ids(int32_t id, const int32_t* idx, int len, int t,
+                                               int row16) {
+  if constexpr (P % 16 == 0) {
+    MIds<P> ids;
+    ids.id = id;
+    return ids;
+  } else {
+    return m_read_ids<P>(idx, len, t, row16);
+  }
+}
+
 template <int P>
 __device__ __forceinline__ MRef<P> m_tile_ref(const MCtx& c, const MIds<P>& ids, int len, int t,
                                               int row16, int kg, int& bad) {
@@ -296,6 +312,26 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __re
   __shared__ MShared shared[kMaxWavesPerBlock];
   // tiles each wave has completed; see the tile loop
   __shared__ int progress[kMaxWavesPerBlock];
+
+  // The slot's bounds, its first item (with the ids of that item's first two
+  // pages) and the header fields sit at offsets fixed by the slot count (the
+  // grid size).  They are requested together, and the empty asm below makes
+  // the kernel wait for them all at once: one round trip to memory before the
+  // first K and V loads are issued.
+  const int32_t* hdr = ws + PKD_HEADER_BASE;
+  const int num_slots = gridDim.x;
+  const int32_t* slot_indptr = ws + plan_off_slots();
+  const int32_t* first = ws + plan_off_first(num_slots) + 8 * int64_t(blockIdx.x);
+  const int32_t* items = ws + plan_off_items(num_slots);
+  const int it_begin = slot_indptr[blockIdx.x];
+  const int it_end = slot_indptr[blockIdx.x + 1];
+  const int first_req = first[0], first_page = first[1], first_out = first[4],
+            first_len = first[5], first_id0 = first[6], first_id1 = first[7];
+  const int off_indices = hdr[PKD_H_OFF_INDICES];
+  const int partials = hdr[PKD_H_PARTIALS];
+
+  asm volatile("" ::"s"(it_begin), "s"(it_end), "s"(first_req), "s"(first_page), "s"(first_out),
+               "s"(first_len), "s"(first_id0), "s"(first_id1), "s"(off_indices), "s"(partials));
   if ((threadIdx.x & 63) == 0) progress[threadIdx.x >> 6] = 0;
   __syncthreads();
   int done_tiles = 0;
@@ -308,15 +344,8 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __re
   const int kg = lane >> 4;
   MShared& sh = shared[wave];
 
-  // The slot's bounds and its first item sit at offsets fixed by the slot
-  // count (the grid size), so they are read together with the header.
-  const int32_t* hdr = ws + PKD_HEADER_BASE;
-  const int num_slots = gridDim.x;
-  const int32_t* slot_indptr = ws + plan_off_slots();
-  const int32_t* first = ws + plan_off_first(num_slots) + 8 * int64_t(blockIdx.x);
-  const int32_t* items = ws + plan_off_items(num_slots);
-  const int32_t* kv_idx = ws + hdr[PKD_H_OFF_INDICES];
-  const int64_t n_partials = hdr[PKD_H_PARTIALS];
+  const int32_t* kv_idx = ws + off_indices;
+  const int64_t n_partials = partials;
   const int Hq = num_qo_heads;
   float* o_part = fws;
   float* lse_part = fws + n_partials * Hq * kHeadDim;
@@ -328,18 +357,17 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __re
   c.v_bytes = uint64_t(P) * c.row_bytes;
   c.page_bytes = 2 * c.v_bytes;
 
-  const int it_begin = slot_indptr[blockIdx.x];
-  const int it_end = slot_indptr[blockIdx.x + 1];
-  const int first_req = first[0], first_page = first[1], first_out = first[4],
-            first_len = first[5];
   for (int it = it_begin; it < it_end; ++it) {
-    int req = first_req, page_begin = first_page, out = first_out, len = first_len;
+    int req = first_req, page_begin = first_page, out = first_out, len = first_len,
+        id0 = first_id0, id1 = first_id1;
     if (it != it_begin) {
       const int32_t* item = items + 8 * it;
       req = item[0];
       page_begin = item[1];
       out = item[4];
       len = item[5];
+      id0 = item[6];
+      id1 = item[7];
     }
     const int32_t* idx = kv_idx + page_begin;
     const int ntiles = (len + 15) >> 4;
@@ -372,10 +400,12 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __re
       // Three register tiles used in a ring: while tile n is computed, tiles
       // n + 1 and n + 2 stream in.  Page ids run one tile further ahead.
       MTile ta, tb, tc;
-      m_load<P>(ta, m_tile_ref<P>(c, m_read_ids<P>(idx, len, 0, row16), len, 0, row16, kg, bad),
+      m_load<P>(ta, m_tile_ref<P>(c, m_start_ids<P>(id0, idx, len, 0, row16), len, 0, row16, kg, bad),
                 lane, c.head_bytes);
       if (ntiles > 1)
-        m_load<P>(tb, m_tile_ref<P>(c, m_read_ids<P>(idx, len, 1, row16), len, 1, row16, kg, bad),
+        m_load<P>(tb,
+                  m_tile_ref<P>(c, m_start_ids<P>(P == 16 ? id1 : id0, idx, len, 1, row16), len,
+                                1, row16, kg, bad),
                   lane, c.head_bytes);
       MIds<P> ids_next = m_read_ids<P>(idx, len, min(2, ntiles - 1), row16);
       __builtin_amdgcn_sched_barrier(0);

@@ -222,6 +222,25 @@ void decode_pv_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __rest
   __shared__ VShared shared[kMaxWavesPerBlock];
   // tiles each wave has completed; see the steady-state loop
   __shared__ int progress[kMaxWavesPerBlock];
+
+  // The slot's bounds, its first item (with the ids of that item's first two
+  // pages) and the header fields sit at offsets fixed by the slot count (the
+  // grid size): requested together, waited for at once (the empty asm), one
+  // round trip to memory before the first K and V loads.
+  const int32_t* hdr = ws + PKD_HEADER_BASE;
+  const int num_slots = gridDim.x;
+  const int32_t* slot_indptr = ws + plan_off_slots();
+  const int32_t* first = ws + plan_off_first(num_slots) + 8 * int64_t(blockIdx.x);
+  const int32_t* items = ws + plan_off_items(num_slots);
+  const int it_begin = slot_indptr[blockIdx.x];
+  const int it_end = slot_indptr[blockIdx.x + 1];
+  const int first_req = first[0], first_page = first[1], first_out = first[4],
+            first_len = first[5], first_id0 = first[6], first_id1 = first[7];
+  const int off_indices = hdr[PKD_H_OFF_INDICES];
+  const int partials = hdr[PKD_H_PARTIALS];
+  asm volatile("" ::"s"(it_begin), "s"(it_end), "s"(first_req), "s"(first_page), "s"(first_out),
+               "s"(first_len), "s"(first_id0), "s"(first_id1), "s"(off_indices), "s"(partials));
+
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
@@ -234,13 +253,8 @@ void decode_pv_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __rest
   const int kg = lane >> 4;
   VShared& sh = shared[wave];
 
-  const int32_t* hdr = ws + PKD_HEADER_BASE;
-  const int num_slots = gridDim.x;
-  const int32_t* slot_indptr = ws + plan_off_slots();
-  const int32_t* first = ws + plan_off_first(num_slots) + 8 * int64_t(blockIdx.x);
-  const int32_t* items = ws + plan_off_items(num_slots);
-  const int32_t* kv_idx = ws + hdr[PKD_H_OFF_INDICES];
-  const int64_t n_partials = hdr[PKD_H_PARTIALS];
+  const int32_t* kv_idx = ws + off_indices;
+  const int64_t n_partials = partials;
   const int Hq = num_qo_heads;
   float* o_part = fws;
   float* lse_part = fws + n_partials * Hq * kHeadDim;
@@ -252,18 +266,19 @@ void decode_pv_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __rest
   c.v_bytes = uint32_t(P) * c.row_bytes;
   c.page_bytes = 2 * c.v_bytes;
 
-  const int it_begin = slot_indptr[blockIdx.x];
-  const int it_end = slot_indptr[blockIdx.x + 1];
-  const int first_req = first[0], first_page = first[1], first_out = first[4],
-            first_len = first[5];
   for (int it = it_begin; it < it_end; ++it) {
-    int req = first_req, page_begin = first_page, out = first_out, len = first_len;
+    // an item row carries the ids of the item's first two pages, which hold
+    // its first two tiles
+    int req = first_req, page_begin = first_page, out = first_out, len = first_len,
+        id0 = first_id0, id1 = first_id1;
     if (it != it_begin) {
       const int32_t* item = items + 8 * it;
       req = item[0];
       page_begin = item[1];
       out = item[4];
       len = item[5];
+      id0 = item[6];
+      id1 = item[7];
     }
     const int32_t* idx = kv_idx + page_begin;
     const int ntiles = (len + 15) >> 4;
@@ -293,8 +308,8 @@ void decode_pv_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __rest
       VTile ta, tb, tc;
       // both loads unconditional (a one-tile item reads its tile twice), so
       // the same loads are in flight on every path and the waits stay exact
-      v_load(ta, c, v_ref<P>(c, v_read_id<P>(idx, 0), 0, bad));
-      v_load(tb, c, v_ref<P>(c, v_read_id<P>(idx, min(1, ntiles - 1)), min(1, ntiles - 1), bad));
+      v_load(ta, c, v_ref<P>(c, id0, 0, bad));
+      v_load(tb, c, v_ref<P>(c, P == 16 ? id1 : id0, min(1, ntiles - 1), bad));
       int32_t id_next = v_read_id<P>(idx, min(2, ntiles - 1));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll

@@ -71,10 +71,13 @@ int decode_blocks_per_cu_dot2(int waves_per_block);
 
 // Copy `image_ints` ints (a multiple of 4, 16-byte aligned ends) of a plan
 // image from pinned host memory (device-visible pointer) to the workspace,
-// and `nnz` page ids from `indices` to `dst_indices`, in one kernel.
+// and `nnz` page ids from `indices` to `dst_indices`, in one kernel.  Words
+// 6 and 7 of each of the `item_rows` 8-int item rows starting at image int
+// `rows_off` receive the page ids of that item's first two pages (its first
+// twice for a one-page item; a row with no pages is left as it is).
 hipError_t launch_plan_upload(const int32_t* image, int32_t* dst, int64_t image_ints,
                               const int32_t* indices, int32_t* dst_indices, int64_t nnz,
-                              hipStream_t stream);
+                              int64_t rows_off, int64_t item_rows, hipStream_t stream);
 
 // New tokens' requests and positions, and their K/V rows into the paged
 // cache (append.hip).

@@ -3,6 +3,9 @@
 // kv_indices snapshot into the int workspace.  Keeping the upload on the
 // compute queue, rather than handing it to a copy engine, leaves no
 // cross-engine wait between the plan and the first decode launch behind it.
+// On the way it writes into each item row of a decode plan the ids of the
+// item's first two pages, which only the device holds; the decode kernels
+// then start an item's loads as soon as its row has arrived.
 
 #include <hip/hip_runtime.h>
 
@@ -17,10 +20,24 @@ constexpr int kUploadThreads = 256;
 
 __global__ __launch_bounds__(kUploadThreads) void plan_upload_kernel(
     const int4* __restrict__ image, int4* __restrict__ dst, int64_t image_vec4,
-    const int32_t* __restrict__ indices, int32_t* __restrict__ dst_indices, int64_t nnz) {
+    const int32_t* __restrict__ indices, int32_t* __restrict__ dst_indices, int64_t nnz,
+    int64_t rows_vec4, int64_t item_rows) {
   const int64_t stride = int64_t(gridDim.x) * kUploadThreads;
   const int64_t tid = int64_t(blockIdx.x) * kUploadThreads + threadIdx.x;
-  for (int64_t i = tid; i < image_vec4; i += stride) dst[i] = image[i];
+  for (int64_t i = tid; i < image_vec4; i += stride) {
+    int4 v = image[i];
+    // words 6 and 7 of an item row, written by the thread that copies the
+    // row's second half
+    const int64_t r = i - rows_vec4;
+    if (r >= 0 && r < 2 * item_rows && (r & 1)) {
+      const int4 head = image[i - 1];  // request, page_begin, num_pages, last_len
+      if (head.z > 0) {
+        v.z = indices[head.y];
+        v.w = indices[head.y + (head.z > 1 ? 1 : 0)];
+      }
+    }
+    dst[i] = v;
+  }
   for (int64_t i = tid; i < nnz; i += stride) dst_indices[i] = indices[i];
 }
 
@@ -28,9 +45,10 @@ __global__ __launch_bounds__(kUploadThreads) void plan_upload_kernel(
 
 hipError_t launch_plan_upload(const int32_t* image, int32_t* dst, int64_t image_ints,
                               const int32_t* indices, int32_t* dst_indices, int64_t nnz,
-                              hipStream_t stream) {
+                              int64_t rows_off, int64_t item_rows, hipStream_t stream) {
   if ((reinterpret_cast<uintptr_t>(image) | reinterpret_cast<uintptr_t>(dst)) & 15 ||
-      image_ints % 4 != 0)
+      image_ints % 4 != 0 || rows_off % 4 != 0 || rows_off < 0 ||
+      rows_off + 8 * item_rows > image_ints)
     return hipErrorInvalidValue;
   const int64_t work = image_ints / 4 > nnz ? image_ints / 4 : nnz;
   int64_t grid = (work + kUploadThreads - 1) / kUploadThreads;
@@ -38,7 +56,7 @@ hipError_t launch_plan_upload(const int32_t* image, int32_t* dst, int64_t image_
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(plan_upload_kernel, dim3(unsigned(grid)), dim3(kUploadThreads), 0, stream,
                      reinterpret_cast<const int4*>(image), reinterpret_cast<int4*>(dst),
-                     image_ints / 4, indices, dst_indices, nnz);
+                     image_ints / 4, indices, dst_indices, nnz, rows_off / 4, item_rows);
   return hipGetLastError();
 }
 

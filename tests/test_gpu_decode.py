@@ -33,6 +33,48 @@ def _check(batch, q, cache, label, sm_scale=None, return_lse=True, r=None, **opt
     return gu.assert_close(o, lse, o_ref, lse_ref, label=label)
 
 
+def test_device_plan_image():
+    """The uploaded plan is the host planner's image, except that the item
+    rows (first-item rows and items) of a decode plan also carry the ids of
+    each item's first two pages, read on the device from kv_indices."""
+    import torch
+
+    import paged_kv_decode_11_amd as pkd
+    from paged_kv_decode_11_amd import _lib
+
+    rng = np.random.default_rng(71)
+    lens = [int(x) for x in rng.integers(1, 900, size=23)] + [16, 17, 1, 2000]
+    need = sum(-(-n // 16) for n in lens)
+    batch = workloads.make_batch(lens, 16, need + 40, 32, 8, 128, rng)
+    r = gu.runner()
+    gu.decode(batch, gu.bits_to_dev(workloads.host_query(batch, rng)),
+              gu.bits_to_dev(workloads.host_cache(batch, rng)), r=r, fixed_chunk_pages=7)
+    host = pkd.plan_host(batch.kv_indptr, batch.kv_last_page_len, 32, 8, 128, 16, r.num_slots,
+                         fixed_chunk_pages=7)
+    img = host["image"]
+    dev = r.int_workspace.view(torch.int32)[: img.size].cpu().numpy()
+    h = host["header"]
+    gu.say("plan image", "ints", img.size, "items", h["ITEMS"], "slots", h["SLOTS"])
+    lo, hi = h["OFF_FIRST"], h["OFF_MERGE"]
+    assert hi - lo == 8 * (h["SLOTS"] + h["ITEMS"])
+    plan_id = _lib.HEADER_BASE + _lib.H["PLAN_ID"]
+    same = np.ones(img.size, dtype=bool)
+    same[: _lib.HEADER_BASE] = False  # device-only words
+    same[plan_id] = False
+    rows = np.arange(lo, hi).reshape(-1, 8)
+    same[rows[:, 6:].ravel()] = False
+    assert np.array_equal(dev[same], img[same])
+    assert dev[plan_id] == r.plan_id
+    fields = dev[lo:hi].reshape(-1, 8)
+    kv = batch.kv_indices.astype(np.int64)
+    for row, f in enumerate(fields):
+        if f[2] == 0:  # a slot without items
+            assert f[6] == 0 and f[7] == 0, row
+            continue
+        assert f[6] == kv[f[1]], row
+        assert f[7] == kv[f[1] + (1 if f[2] > 1 else 0)], row
+
+
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_tiny_workload_writethrough(variant):
     spec, rng, b = workloads.workload("tiny")
