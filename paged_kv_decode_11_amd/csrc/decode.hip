@@ -263,7 +263,7 @@ __device__ __forceinline__ void tile_step(State<G>& st, TileRegs& t, const TileR
 // plan and kv_indices are not written by this kernel and reads them through
 // the scalar cache.
 template <int G, int P>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2, 8)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void decode_kernel(
     const uint16_t* __restrict__ q_ptr, const uint16_t* __restrict__ kv_ptr,
     uint16_t* __restrict__ o_ptr, float* __restrict__ lse_ptr, const int32_t* __restrict__ ws,
@@ -321,22 +321,69 @@ void decode_kernel(
       }
 
       int bad = 0;
-      TileRegs t;
-      {
-        const TileRef<P> t0 = tile_ref<P>(p, read_ids<P>(idx, len, 0, R), len, 0, R, col, bad);
-        load_k<P>(t.k, t0);
-        load_v<P>(t.v, t0);
-      }
-      // page ids run one tile ahead of the loads that use them
-      TileIds<P> ids_next = read_ids<P>(idx, len, ntiles > 1 ? 1 : 0, R);
-      for (int n = 0; n + 1 < ntiles; ++n) {
-        const TileRef<P> ref = tile_ref<P>(p, ids_next, len, n + 1, R, col, bad);
-        ids_next = read_ids<P>(idx, len, min(n + 2, ntiles - 1), R);
-        tile_step<G, P, true>(st, t, ref, 16, R, p.scale_log2, p.v_bytes);
-      }
-      {
+      if constexpr (G > 4) {
+        // g = 8 holds twice the query rows and accumulators; a second tile
+        // in registers would spill, so one tile is in flight.  Page ids run
+        // one tile ahead of the loads that use them.
+        TileRegs t;
+        {
+          const TileRef<P> t0 = tile_ref<P>(p, read_ids<P>(idx, len, 0, R), len, 0, R, col, bad);
+          load_k<P>(t.k, t0);
+          load_v<P>(t.v, t0);
+        }
+        TileIds<P> ids_next = read_ids<P>(idx, len, ntiles > 1 ? 1 : 0, R);
+        for (int n = 0; n + 1 < ntiles; ++n) {
+          const TileRef<P> ref = tile_ref<P>(p, ids_next, len, n + 1, R, col, bad);
+          ids_next = read_ids<P>(idx, len, min(n + 2, ntiles - 1), R);
+          tile_step<G, P, true>(st, t, ref, 16, R, p.scale_log2, p.v_bytes);
+        }
         const TileRef<P> none = {};
         tile_step<G, P, false>(st, t, none, len - 16 * (ntiles - 1), R, p.scale_log2, p.v_bytes);
+      } else {
+        // Two tiles in a register ring: while tile n is computed, tile n + 1
+        // is in flight and tile n + 2 is requested into n's registers as they
+        // free up.  Page ids run one tile ahead of the loads that use them.
+        TileRegs ta, tb;
+        {
+          const TileRef<P> r0 = tile_ref<P>(p, read_ids<P>(idx, len, 0, R), len, 0, R, col, bad);
+          load_k<P>(ta.k, r0);
+          load_v<P>(ta.v, r0);
+        }
+        if (ntiles > 1) {
+          const TileRef<P> r1 = tile_ref<P>(p, read_ids<P>(idx, len, 1, R), len, 1, R, col, bad);
+          load_k<P>(tb.k, r1);
+          load_v<P>(tb.v, r1);
+        }
+        TileIds<P> ids_next = read_ids<P>(idx, len, min(2, ntiles - 1), R);
+        int n = 0;
+        for (; n + 3 < ntiles; n += 2) {
+          {
+            const TileRef<P> ref = tile_ref<P>(p, ids_next, len, n + 2, R, col, bad);
+            ids_next = read_ids<P>(idx, len, n + 3, R);
+            tile_step<G, P, true>(st, ta, ref, 16, R, p.scale_log2, p.v_bytes);
+          }
+          {
+            const TileRef<P> ref = tile_ref<P>(p, ids_next, len, n + 3, R, col, bad);
+            ids_next = read_ids<P>(idx, len, min(n + 4, ntiles - 1), R);
+            tile_step<G, P, true>(st, tb, ref, 16, R, p.scale_log2, p.v_bytes);
+          }
+        }
+        // 1, 2 or 3 tiles remain; only the last one masks
+        {
+          const TileRef<P> none = {};
+          const int last_valid = len - 16 * (ntiles - 1);
+          if (ntiles - n == 3) {
+            const TileRef<P> ref = tile_ref<P>(p, ids_next, len, n + 2, R, col, bad);
+            tile_step<G, P, true>(st, ta, ref, 16, R, p.scale_log2, p.v_bytes);
+            tile_step<G, P, false>(st, tb, none, 16, R, p.scale_log2, p.v_bytes);
+            tile_step<G, P, false>(st, ta, none, last_valid, R, p.scale_log2, p.v_bytes);
+          } else if (ntiles - n == 2) {
+            tile_step<G, P, false>(st, ta, none, 16, R, p.scale_log2, p.v_bytes);
+            tile_step<G, P, false>(st, tb, none, last_valid, R, p.scale_log2, p.v_bytes);
+          } else {
+            tile_step<G, P, false>(st, ta, none, last_valid, R, p.scale_log2, p.v_bytes);
+          }
+        }
       }
       if (bad && lane == 0) err[0] = PKD_DEVERR_PAGE_ID;
 
