@@ -94,7 +94,7 @@ enum {
   PKD_VARIANT_DOT2 = 1,    /* q.k with packed bf16 dot products on the vector ALUs */
   PKD_VARIANT_MFMA = 2,    /* q.k as a 16 x 16 tile on the matrix cores (GQA group as rows),
                               p.v on the vector ALUs */
-  PKD_VARIANT_MFMA_PV = 3  /* both q.k and p.v on the matrix cores (page sizes 16, 32, 64) */
+  PKD_VARIANT_MFMA_PV = 3  /* both q.k and p.v on the matrix cores */
 };
 
 /* ---------------------------------------------------------------------

@@ -308,8 +308,8 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
   if (variant == PKD_VARIANT_MFMA_PV &&
       (kv_dtype != PKD_DTYPE_BF16 || !pkd::pv_variant_built(num_qo_heads / num_kv_heads, page_size)))
     return fail(PKD_ERR_UNSUPPORTED,
-                "the PKD_VARIANT_MFMA_PV kernel is built for a bf16 cache, group size 1, 2, 4 or 8 "
-                "and page_size 16, 32 or 64");
+                "the PKD_VARIANT_MFMA_PV kernel is built for a bf16 cache and group size 1, 2, 4 "
+                "or 8");
   if (variant == PKD_VARIANT_DOT2 && kv_dtype == PKD_DTYPE_FP8_E4M3)
     return fail(PKD_ERR_UNSUPPORTED, "an fp8 e4m3 cache has only the matrix-core kernel");
 

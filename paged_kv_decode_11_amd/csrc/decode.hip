@@ -35,6 +35,7 @@
 #include "device_common.h"
 #include "kernels.h"
 #include "pkd.h"
+#include "plan_layout.h"
 
 namespace pkd {
 namespace {
@@ -277,11 +278,24 @@ void decode_kernel(
   const int R = lane >> 4;
   const int c = lane & 15;
 
+  // The slot's bounds, its first item and the header fields sit at offsets
+  // fixed by the slot count (the grid size): requested together and waited
+  // for at once (the empty asm), one round trip before the page ids.
   const int32_t* hdr = ws + PKD_HEADER_BASE;
-  const int32_t* slot_indptr = ws + hdr[PKD_H_OFF_SLOTS];
-  const int32_t* items = ws + hdr[PKD_H_OFF_ITEMS];
-  const int32_t* kv_idx = ws + hdr[PKD_H_OFF_INDICES];
-  const int64_t n_partials = hdr[PKD_H_PARTIALS];
+  const int num_slots = gridDim.x;
+  const int32_t* slot_indptr = ws + plan_off_slots();
+  const int32_t* first = ws + plan_off_first(num_slots) + 8 * int64_t(blockIdx.x);
+  const int32_t* items = ws + plan_off_items(num_slots);
+  const int it_begin = slot_indptr[blockIdx.x];
+  const int it_end = slot_indptr[blockIdx.x + 1];
+  const int first_req = first[0], first_page = first[1], first_out = first[4],
+            first_len = first[5];
+  const int off_indices = hdr[PKD_H_OFF_INDICES];
+  const int partials = hdr[PKD_H_PARTIALS];
+  asm volatile("" ::"s"(it_begin), "s"(it_end), "s"(first_req), "s"(first_page), "s"(first_out),
+               "s"(first_len), "s"(off_indices), "s"(partials));
+  const int32_t* kv_idx = ws + off_indices;
+  const int64_t n_partials = partials;
 
   Ctx p;
   p.q = q_ptr;
@@ -298,13 +312,16 @@ void decode_kernel(
   p.v_bytes = uint64_t(P) * p.row_bytes;
   p.page_bytes = 2 * p.v_bytes;
 
-  const int it_end = slot_indptr[blockIdx.x + 1];
-  for (int it = slot_indptr[blockIdx.x]; it < it_end; ++it) {
-    const int32_t* item = items + 8 * it;
-    const int req = item[0];
-    const int out = item[4];
-    const int len = item[5];
-    const int32_t* idx = kv_idx + item[1];
+  for (int it = it_begin; it < it_end; ++it) {
+    int req = first_req, page_begin = first_page, out = first_out, len = first_len;
+    if (it != it_begin) {
+      const int32_t* item = items + 8 * it;
+      req = item[0];
+      page_begin = item[1];
+      out = item[4];
+      len = item[5];
+    }
+    const int32_t* idx = kv_idx + page_begin;
     const int ntiles = (len + 15) >> 4;
 
     for (int kh = wave; kh < p.Hkv; kh += nwaves) {

@@ -26,8 +26,9 @@
 // Streaming as in the FP8 kernel: three tiles in a register ring (two in
 // flight), a straight-line steady state of three prefetching tiles per trip,
 // and a workgroup barrier plus issue priority per trip keeping the two waves
-// of each SIMD together.  Page sizes that are multiples of 16 (each tile in
-// one page, addressed through a buffer descriptor over the page).
+// of each SIMD together.  Page sizes that are multiples of 16 keep each tile
+// in one page, addressed through a buffer descriptor over the page; smaller
+// pages (1, 2, 4, 8 tokens) give each lane the address of each of its rows.
 
 #include <hip/hip_runtime.h>
 
@@ -75,9 +76,37 @@ struct VTile {
   uint4 v[4];  // load j: V row 4 j + (l >> 4), 16-byte piece l & 15
 };
 
-struct VRef {
+// Where this lane's rows of one tile are.  Page sizes that are multiples of
+// 16 keep a tile in one page: a buffer over that page and the tile's offset
+// in it.  Smaller pages spread a tile over 16 / P pages: the lane carries the
+// address of each of its 4 K rows (V rows sit v_bytes further).
+template <int P, bool kWhole = (P % 16 == 0)>
+struct VRef;
+
+template <int P>
+struct VRef<P, true> {
   __amdgpu_buffer_rsrc_t page;  // buffer over the tile's page
   uint32_t tile_off;            // byte offset of the tile's first K row in the page
+};
+
+template <int P>
+struct VRef<P, false> {
+  const char* row[4];  // K row 4 j + (l >> 4) of the tile, this lane's 16-byte piece
+};
+
+// Page ids of one tile, read a tile ahead of their use: one wave-uniform id
+// for whole-tile pages, else the id of each of this lane's 4 rows.
+template <int P, bool kWhole = (P % 16 == 0)>
+struct VIds;
+
+template <int P>
+struct VIds<P, true> {
+  int32_t id;
+};
+
+template <int P>
+struct VIds<P, false> {
+  int32_t id[4];
 };
 
 struct VCtx {
@@ -87,40 +116,74 @@ struct VCtx {
   uint32_t v_bytes;    // K half of a page
   uint32_t page_bytes;
   uint32_t lane_off;   // (l >> 4) rows + this wave's head + 16 (l & 15)
+  uint32_t col_off;    // this wave's head + 16 (l & 15)
 };
 
-template <int P>
-__device__ __forceinline__ int32_t v_read_id(const int32_t* idx, int t) {
-  return idx[(16 * t) / P];
+// Row 4 j + kg of tile t, clamped into the chunk: rows past its end re-read
+// its last token (their logits are masked and their V zeroed), so no slot
+// past last_page_len and no page past the chunk's is touched.
+__device__ __forceinline__ int v_row(int j, int kg, int len, int t) {
+  return 16 * t + min(4 * j + kg, len - 16 * t - 1);
 }
 
 template <int P>
-__device__ __forceinline__ VRef v_ref(const VCtx& c, int32_t id, int t, int& bad) {
-  // The id was requested a tile earlier; the empty asm keeps its range
-  // check here instead of next to the load.
-  asm volatile("" : "+s"(id));
-  const int64_t pg = safe_page(id, c.num_pages, bad);
-  VRef r;
-  // raw buffer over one page (32-bit data format word as raw loads need)
-  r.page = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(c.kv + pg * c.page_bytes), 0,
-                                             int(c.page_bytes), 0x00020000);
-  r.tile_off = uint32_t((16 * t) % P) * c.row_bytes;
+__device__ __forceinline__ VIds<P> v_read_ids(const int32_t* idx, int len, int t, int kg) {
+  VIds<P> ids;
+  if constexpr (P % 16 == 0) {
+    ids.id = idx[(16 * t) / P];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ids.id[j] = idx[v_row(j, kg, len, t) / P];
+  }
+  return ids;
+}
+
+template <int P>
+__device__ __forceinline__ VRef<P> v_ref(const VCtx& c, VIds<P> ids, int len, int t, int kg,
+                                         int& bad) {
+  VRef<P> r;
+  if constexpr (P % 16 == 0) {
+    // The id was requested a tile earlier; the empty asm keeps its range
+    // check here instead of next to the load.
+    asm volatile("" : "+s"(ids.id));
+    const int64_t pg = safe_page(ids.id, c.num_pages, bad);
+    // raw buffer over one page (32-bit data format word as raw loads need)
+    r.page = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(c.kv + pg * c.page_bytes), 0,
+                                               int(c.page_bytes), 0x00020000);
+    r.tile_off = uint32_t((16 * t) % P) * c.row_bytes;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      asm volatile("" : "+v"(ids.id[j]));
+      const int64_t pg = safe_page(ids.id[j], c.num_pages, bad);
+      const uint32_t slot = uint32_t(v_row(j, kg, len, t) % P);
+      r.row[j] = c.kv + pg * c.page_bytes + slot * c.row_bytes + c.col_off;
+    }
+  }
   return r;
 }
 
-__device__ __forceinline__ void v_load(VTile& d, const VCtx& c, const VRef& r) {
+template <int P>
+__device__ __forceinline__ void v_load(VTile& d, const VCtx& c, const VRef<P>& r) {
+  if constexpr (P % 16 == 0) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const auto w = __builtin_amdgcn_raw_buffer_load_b128(
-        r.page, c.lane_off, r.tile_off + uint32_t(4 * j) * c.row_bytes, kBufferNontemporal);
-    d.k[j] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
+    for (int j = 0; j < 4; ++j) {
+      const auto w = __builtin_amdgcn_raw_buffer_load_b128(
+          r.page, c.lane_off, r.tile_off + uint32_t(4 * j) * c.row_bytes, kBufferNontemporal);
+      d.k[j] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const auto w = __builtin_amdgcn_raw_buffer_load_b128(
-        r.page, c.lane_off, r.tile_off + c.v_bytes + uint32_t(4 * j) * c.row_bytes,
-        kBufferNontemporal);
-    d.v[j] = make_uint4(w[0], w[1], w[2], w[3]);
+    for (int j = 0; j < 4; ++j) {
+      const auto w = __builtin_amdgcn_raw_buffer_load_b128(
+          r.page, c.lane_off, r.tile_off + c.v_bytes + uint32_t(4 * j) * c.row_bytes,
+          kBufferNontemporal);
+      d.v[j] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d.k[j] = load_stream16(r.row[j]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d.v[j] = load_stream16(r.row[j] + c.v_bytes);
   }
 }
 
@@ -133,9 +196,9 @@ struct VState {
 // One tile.  With kPrefetch a later tile's loads are issued first; the last
 // tile (kLast) masks tokens >= valid: logits to -inf, V rows to zero (a slot
 // past the sequence may hold any value).
-template <bool kPrefetch, bool kLast>
+template <bool kPrefetch, bool kLast, int P>
 __device__ __forceinline__ void v_step(VState& st, const VTile& cur, VTile& nxt, const VCtx& c,
-                                       const VRef& next, int valid, int lane, float scale_log2,
+                                       const VRef<P>& next, int valid, int lane, float scale_log2,
                                        VShared& sh) {
   const int row16 = lane & 15;
   const int kg = lane >> 4;
@@ -218,7 +281,6 @@ void decode_pv_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __rest
                       int32_t* __restrict__ err, int64_t num_pages, float scale_log2,
                       int num_qo_heads, int num_kv_heads) {
   static_assert(G >= 1 && G <= 8, "group size");
-  static_assert(P % 16 == 0, "a 16-token tile must lie in one page");
   __shared__ VShared shared[kMaxWavesPerBlock];
   // tiles each wave has completed; see the steady-state loop
   __shared__ int progress[kMaxWavesPerBlock];
@@ -285,7 +347,8 @@ void decode_pv_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __rest
 
     for (int kh = wave; kh < num_kv_heads; kh += nwaves) {
       const uint32_t head_bytes = uint32_t(kh) * kHeadDim * 2;
-      c.lane_off = uint32_t(kg) * c.row_bytes + head_bytes + 16 * uint32_t(row16);
+      c.col_off = head_bytes + 16 * uint32_t(row16);
+      c.lane_off = uint32_t(kg) * c.row_bytes + c.col_off;
       // Q^T operand: lane (row l & 15, kg) holds head dims 32 j + 8 kg .. + 7
       // for MFMA j; rows >= g are zero.  Loaded first, staged in LDS after
       // the first tiles' loads are issued.
@@ -308,15 +371,24 @@ void decode_pv_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __rest
       VTile ta, tb, tc;
       // both loads unconditional (a one-tile item reads its tile twice), so
       // the same loads are in flight on every path and the waits stay exact
-      v_load(ta, c, v_ref<P>(c, id0, 0, bad));
-      v_load(tb, c, v_ref<P>(c, P == 16 ? id1 : id0, min(1, ntiles - 1), bad));
-      int32_t id_next = v_read_id<P>(idx, min(2, ntiles - 1));
+      VIds<P> ids0, ids1;
+      if constexpr (P % 16 == 0) {
+        ids0.id = id0;
+        ids1.id = P == 16 ? id1 : id0;
+      } else {
+        // the item row's two ids cover 2 P tokens here; read the tiles' own
+        ids0 = v_read_ids<P>(idx, len, 0, kg);
+        ids1 = v_read_ids<P>(idx, len, min(1, ntiles - 1), kg);
+      }
+      v_load(ta, c, v_ref<P>(c, ids0, len, 0, kg, bad));
+      v_load(tb, c, v_ref<P>(c, ids1, len, min(1, ntiles - 1), kg, bad));
+      VIds<P> id_next = v_read_ids<P>(idx, len, min(2, ntiles - 1), kg);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) sh.qa[j][lane] = qv[j];
       __builtin_amdgcn_wave_barrier();
       const int last_valid = len - 16 * (ntiles - 1);
-      const VRef none = {};
+      const VRef<P> none = {};
       int n = 0;
       auto step = [&](VTile& cur, VTile& nxt) -> bool {
         if (n == ntiles - 1) {
@@ -324,8 +396,8 @@ void decode_pv_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __rest
           return true;
         }
         if (n + 2 < ntiles) {
-          const VRef ref = v_ref<P>(c, id_next, n + 2, bad);
-          id_next = v_read_id<P>(idx, min(n + 3, ntiles - 1));
+          const VRef<P> ref = v_ref<P>(c, id_next, len, n + 2, kg, bad);
+          id_next = v_read_ids<P>(idx, len, min(n + 3, ntiles - 1), kg);
           v_step<true, false>(st, cur, nxt, c, ref, 16, lane, scale_log2, sh);
         } else {
           v_step<false, false>(st, cur, nxt, c, none, 16, lane, scale_log2, sh);
@@ -343,8 +415,8 @@ void decode_pv_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __rest
         for (int k = 0; k < 3; ++k) {
           VTile& cur = k == 0 ? ta : k == 1 ? tb : tc;
           VTile& nxt = k == 0 ? tc : k == 1 ? ta : tb;
-          const VRef ref = v_ref<P>(c, id_next, n + 2, bad);
-          id_next = v_read_id<P>(idx, min(n + 3, ntiles - 1));
+          const VRef<P> ref = v_ref<P>(c, id_next, len, n + 2, kg, bad);
+          id_next = v_read_ids<P>(idx, len, min(n + 3, ntiles - 1), kg);
           v_step<true, false>(st, cur, nxt, c, ref, 16, lane, scale_log2, sh);
           ++n;
         }
@@ -400,6 +472,10 @@ hipError_t launch_v(const DecodeParams& p, int num_slots, hipStream_t stream) {
 template <int G>
 hipError_t launch_vg(const DecodeParams& p, int page_size, int num_slots, hipStream_t stream) {
   switch (page_size) {
+    case 1: return launch_v<G, 1>(p, num_slots, stream);
+    case 2: return launch_v<G, 2>(p, num_slots, stream);
+    case 4: return launch_v<G, 4>(p, num_slots, stream);
+    case 8: return launch_v<G, 8>(p, num_slots, stream);
     case 16: return launch_v<G, 16>(p, num_slots, stream);
     case 32: return launch_v<G, 32>(p, num_slots, stream);
     case 64: return launch_v<G, 64>(p, num_slots, stream);
@@ -411,7 +487,8 @@ hipError_t launch_vg(const DecodeParams& p, int page_size, int num_slots, hipStr
 
 bool pv_variant_built(int g, int page_size) {
   return (g == 1 || g == 2 || g == 4 || g == 8) &&
-         (page_size == 16 || page_size == 32 || page_size == 64);
+         (page_size == 1 || page_size == 2 || page_size == 4 || page_size == 8 ||
+          page_size == 16 || page_size == 32 || page_size == 64);
 }
 
 hipError_t launch_decode_pv(const DecodeParams& p, int g, int page_size, int num_slots,

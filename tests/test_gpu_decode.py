@@ -108,8 +108,6 @@ def test_tiny_forced_splits(fixed, variant):
 @pytest.mark.parametrize("P", [1, 2, 4, 8, 16, 32, 64])
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
 def test_page_sizes_and_groups(P, G, variant):
-    if variant == "mfma_pv" and P < 16:
-        pytest.skip("the both-products-on-matrix-cores kernel is built for pages of 16-64 tokens")
     Hkv = 8 if G <= 4 else 4
     lens = sorted(set(workloads.edge_lengths(P) + [3 * P + 5, 77, 300]))
     batch, q, cache = _small(10 * P + G, lens, P, Hkv * G, Hkv)
