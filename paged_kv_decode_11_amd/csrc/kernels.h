@@ -50,7 +50,7 @@ hipError_t launch_decode(const DecodeParams& p, int g, int page_size, int num_sl
 hipError_t launch_decode_mfma(const DecodeParams& p, int g, int page_size, int num_slots,
                               hipStream_t stream);
 bool decode_variant_built(int g, int page_size);
-// ... or with both products on the matrix cores (decode_pv.hip; pages of 16-64).
+// ... or with both products on the matrix cores (decode_pv.hip).
 hipError_t launch_decode_pv(const DecodeParams& p, int g, int page_size, int num_slots,
                             hipStream_t stream);
 bool pv_variant_built(int g, int page_size);
