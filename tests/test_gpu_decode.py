@@ -127,6 +127,19 @@ def test_kv_head_counts(Hkv, variant):
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("P", [1, 4])
+@pytest.mark.parametrize("G", [2, 8])
+@pytest.mark.parametrize("Hkv", [3, 12])
+def test_kv_head_counts_small_pages(Hkv, G, P, variant):
+    """Pages below 16 tokens (each lane addresses its own rows) with fewer
+    waves than 8 (Hkv = 3) and with heads looped over waves (Hkv = 12)."""
+    batch, q, cache = _small(60 + Hkv + G + P, [1, 15, 17, 70, 300], P, G * Hkv, Hkv)
+    _check(batch, q, cache, f"P{P}-G{G}-Hkv{Hkv}-{variant}", variant=variant)
+    _check(batch, q, cache, f"P{P}-G{G}-Hkv{Hkv}-{variant}-split", min_chunk_tokens=16,
+           variant=variant)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
 def test_no_lse_and_custom_scale(variant):
     batch, q, cache = _small(7, [100, 33, 1], 16, 32, 8)
     _check(batch, q, cache, "no-lse", return_lse=False, variant=variant)
