@@ -161,6 +161,47 @@ def cpu_baseline(batch, q_bits, cache_dev, o_dev, lse_dev, budget_s: float, fp8_
     }, {"max_abs_err_o": err_o, "max_abs_err_lse": err_l, "requests_checked": len(done)}
 
 
+def read_ceilings(caches, batch, reps: int = 6) -> dict:
+    """Context for the decode kernel's rate: what this GPU reads with the
+    library's read-only kernels (no compute) over the same caches, rotated
+    like the decode runs.  `stream_gbs`: each cache (first 4 GiB at most) read
+    front to back.  `page_gather_gbs`: the pages the batch uses, whole, in a
+    seeded random order.  Each the best of 256 and 512 workgroups (larger
+    grids read slower)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_decode_11_amd as pkd
+
+    def timed(fn, nbytes):
+        for i in range(2):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+
+    flat = [c.view(-1).view(torch.uint8) for c in caches]
+    span = min(flat[0].numel(), 4 << 30) // 16 * 16
+    sink = torch.empty(512 * 512, dtype=torch.int32, device=caches[0].device)
+    stream = max(timed(lambda i: pkd.read_stream(flat[i % len(flat)][:span], grid=g, sink=sink),
+                       span) for g in (256, 512))
+    page_bytes = flat[0].numel() // batch.num_pages
+    pages = np.unique(batch.kv_indices)
+    ids = np.random.Generator(np.random.PCG64(12345)).permutation(pages).astype(np.int32)
+    ids_dev = torch.from_numpy(ids).to(caches[0].device)
+    gather = max(timed(lambda i: pkd.read_pages(flat[i % len(flat)], batch.num_pages, page_bytes,
+                                                ids_dev, grid=g, sink=sink), ids.size * page_bytes)
+                 for g in (256, 512))
+    return {"stream_gbs": round(stream, 1), "page_gather_gbs": round(gather, 1),
+            "page_bytes": int(page_bytes), "pages": int(ids.size),
+            "kernels": "read_stream_kernel, read_pages_kernel (read_ceiling.hip)"}
+
+
 def calibrate_copy(mib: int) -> None:
     """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give
     the scale between counter units and bytes moved."""
@@ -573,6 +614,10 @@ def main():
         cpu, spot = cpu_baseline(batch, q_bits, caches[0], outs[0], lses[0], args.cpu_seconds,
                                  (scales["k_scale"], scales["v_scale"]) if fp8 else None)
 
+    ceiling = read_ceilings(caches, batch)
+    ceiling["decode_kernel_frac_of_page_gather"] = round(achieved / ceiling["page_gather_gbs"], 4)
+    log(f"read ceilings: {ceiling}")
+
     traffic = measured_traffic(args.workload, kernel, args.kv_dtype)
     line = {
         "metric": METRIC,
@@ -613,6 +658,7 @@ def main():
         "mode": "graph" if graph else "eager",
         "graph": graph,
         "eager": eager,
+        "read_ceiling": ceiling,
         "cpu_baseline": cpu,
         "parity_spot_check": spot,
     }

@@ -407,6 +407,32 @@ int pkd_merge_states(const void* o, const float* lse, int32_t n, int32_t k, int3
 int pkd_profile_enable(pkd_handle* h, int32_t enable);
 int pkd_profile_read(pkd_handle* h, double* decode_ms, double* merge_ms, int64_t* runs);
 
+/* ------------------------- read-ceiling kernels ----------------------- */
+
+/* Measurement aids, not part of the decode path.  Decode reads every cached
+ * key and value once per step, so HBM bandwidth bounds it (aicassindra, "Why
+ * serving attention is a different problem"); these kernels only read, and
+ * tell how fast this GPU reads with a plain stream and with a page gather,
+ * as context for the decode kernels' rate.  Each lane XORs the 32-bit words
+ * it reads and writes the result to `sink` (device memory, caller-owned,
+ * pkd_read_sink_words(grid) words): the XOR over the sink is the XOR of
+ * every word read.  Asynchronous on `stream`; nothing is allocated.
+ *
+ * pkd_read_stream: `bytes` (a positive multiple of 16) from `buf` (device,
+ * 16-byte aligned), each byte once.
+ * pkd_read_pages: for each of the n_ids device page ids in order, the whole
+ * page of page_bytes (a power of two, at least 16) at base + id * page_bytes;
+ * ids outside [0, num_pages) are skipped.  Each workgroup reads a contiguous
+ * run of the id list.
+ * Both return PKD_ERR_INVALID_ARG on null pointers, bad sizes or alignment,
+ * or a grid outside [1, 2^20]. */
+int32_t pkd_read_sink_words(int32_t grid);
+int pkd_read_stream(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid,
+                    pkd_stream_t stream);
+int pkd_read_pages(const void* base, int64_t num_pages, int64_t page_bytes,
+                   const int32_t* page_ids, int64_t n_ids, uint32_t* sink, int32_t grid,
+                   pkd_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,4 +22,6 @@ from .api import (  # noqa: F401
     merge_states,
     plan_host,
     plan_shared_host,
+    read_pages,
+    read_stream,
 )

@@ -98,6 +98,9 @@ SIGNATURES = {
     "pkd_merge_state": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "pkd_merge_states": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "pkd_profile_enable": (ctypes.c_int, [_vp, _i32]),
+    "pkd_read_sink_words": (_i32, [_i32]),
+    "pkd_read_stream": (ctypes.c_int, [_vp, _i64, _vp, _i32, _vp]),
+    "pkd_read_pages": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i32, _vp]),
     "pkd_profile_read": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
 }

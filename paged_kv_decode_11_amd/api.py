@@ -257,6 +257,44 @@ def merge_states(o, lse, out=None, lse_out=None, stream=None):
     return out, lse_out
 
 
+def read_stream(buf, grid: int = 1024, sink=None, stream=None):
+    """Read-ceiling kernel: read every byte of the contiguous GPU tensor `buf`
+    once (16-byte nontemporal loads).  Returns the uint32 sink whose XOR is
+    the XOR of every 32-bit word of `buf` (a measurement aid, not part of the
+    decode path)."""
+    import torch
+
+    L = _lib.load()
+    if not (buf.is_cuda and buf.is_contiguous()):
+        raise ValueError("buf must be a contiguous GPU tensor")
+    if sink is None:
+        sink = torch.empty(int(L.pkd_read_sink_words(grid)), dtype=torch.int32, device=buf.device)
+    check(L.pkd_read_stream(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                            grid, _stream_ptr(stream)))
+    return sink
+
+
+def read_pages(base, num_pages: int, page_bytes: int, page_ids, grid: int = 1024, sink=None,
+               stream=None):
+    """Read-ceiling kernel: read the whole page of `page_bytes` at
+    base + id * page_bytes for each id of the int32 GPU tensor `page_ids`, in
+    order (ids outside [0, num_pages) skipped).  Returns the uint32 sink whose
+    XOR is the XOR of every 32-bit word read."""
+    import torch
+
+    L = _lib.load()
+    if not (base.is_cuda and base.is_contiguous() and page_ids.is_cuda
+            and page_ids.is_contiguous() and page_ids.dtype == torch.int32):
+        raise ValueError("base and page_ids (int32) must be contiguous GPU tensors")
+    if num_pages * page_bytes > base.numel() * base.element_size():
+        raise ValueError("num_pages * page_bytes exceeds the buffer")
+    if sink is None:
+        sink = torch.empty(int(L.pkd_read_sink_words(grid)), dtype=torch.int32, device=base.device)
+    check(L.pkd_read_pages(base.data_ptr(), int(num_pages), int(page_bytes), page_ids.data_ptr(),
+                           page_ids.numel(), sink.data_ptr(), grid, _stream_ptr(stream)))
+    return sink
+
+
 def plan_shared_host(qo_indptr, kv_indptr, kv_last_page_len, num_qo_heads, num_kv_heads, head_dim,
                      page_size, num_slots, **opts) -> dict:
     """The schedule pkd_plan_shared would upload (pkd_plan_shared_host),

@@ -670,6 +670,35 @@ int pkd_merge_states(const void* o, const float* lse, int32_t n, int32_t k, int3
   return PKD_OK;
 }
 
+int32_t pkd_read_sink_words(int32_t grid) {
+  return grid < 1 ? 0 : grid * pkd::read_ceiling_threads();
+}
+
+int pkd_read_stream(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid,
+                    pkd_stream_t stream) {
+  if (!buf || !sink) return fail(PKD_ERR_INVALID_ARG, "null pointer");
+  if (bytes <= 0 || bytes % 16 || reinterpret_cast<uintptr_t>(buf) % 16)
+    return fail(PKD_ERR_INVALID_ARG, "bytes must be a positive multiple of 16, buf 16-byte aligned");
+  if (grid < 1 || grid > (1 << 20)) return fail(PKD_ERR_INVALID_ARG, "grid must be in [1, 2^20]");
+  hipError_t e = pkd::launch_read_stream(buf, bytes / 16, sink, grid,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKD_OK : hip_fail(e, "read_stream launch");
+}
+
+int pkd_read_pages(const void* base, int64_t num_pages, int64_t page_bytes,
+                   const int32_t* page_ids, int64_t n_ids, uint32_t* sink, int32_t grid,
+                   pkd_stream_t stream) {
+  if (!base || !page_ids || !sink) return fail(PKD_ERR_INVALID_ARG, "null pointer");
+  if (num_pages < 1 || n_ids < 1) return fail(PKD_ERR_INVALID_ARG, "num_pages and n_ids must be >= 1");
+  if (page_bytes < 16 || (page_bytes & (page_bytes - 1)) || reinterpret_cast<uintptr_t>(base) % 16)
+    return fail(PKD_ERR_INVALID_ARG,
+                "page_bytes must be a power of two of at least 16, base 16-byte aligned");
+  if (grid < 1 || grid > (1 << 20)) return fail(PKD_ERR_INVALID_ARG, "grid must be in [1, 2^20]");
+  hipError_t e = pkd::launch_read_pages(base, page_ids, n_ids, num_pages, page_bytes, sink, grid,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKD_OK : hip_fail(e, "read_pages launch");
+}
+
 int pkd_profile_enable(pkd_handle* h, int32_t enable) {
   if (!h) return fail(PKD_ERR_INVALID_ARG, "null handle");
   h->profile = enable != 0;

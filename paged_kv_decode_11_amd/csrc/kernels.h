@@ -107,4 +107,13 @@ hipError_t launch_merge_two_bf16(const uint16_t* o_a, const float* lse_a, const 
                                  const float* lse_b, int64_t rows, uint16_t* o_out,
                                  float* lse_out, hipStream_t stream);
 
+// Read-ceiling kernels (read_ceiling.hip): `grid` workgroups of
+// read_ceiling_threads() lanes, one 32-bit XOR per lane into `sink`.
+int read_ceiling_threads();
+hipError_t launch_read_stream(const void* buf, int64_t n16, uint32_t* sink, int grid,
+                              hipStream_t stream);
+hipError_t launch_read_pages(const void* base, const int32_t* ids, int64_t n_ids,
+                             int64_t num_pages, int64_t page_bytes, uint32_t* sink, int grid,
+                             hipStream_t stream);
+
 }  // namespace pkd

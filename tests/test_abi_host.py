@@ -200,3 +200,25 @@ def test_plan_shared_host_rejects_bad_groups():
     with pytest.raises(pkd.PkdError) as e:
         pkd.plan_shared_host([0, 0], indptr, last, 32, 8, 128, 16, 16)
     assert e.value.code == _lib.PKD_ERR_INVALID_ARG
+
+
+def test_read_ceiling_argument_checks():
+    """The read-ceiling entry points reject bad sizes, alignment, grids and
+    null pointers before any launch (the pointers here are never touched)."""
+    L = _lib.load()
+    inv = _lib.PKD_ERR_INVALID_ARG
+    buf, sink, ids = 0x10000, 0x20000, 0x30000
+    assert L.pkd_read_sink_words(3) == 3 * 512 and L.pkd_read_sink_words(0) == 0
+    assert L.pkd_read_stream(buf, 24, sink, 1, None) == inv          # not a multiple of 16
+    assert L.pkd_read_stream(buf, 0, sink, 1, None) == inv
+    assert L.pkd_read_stream(buf + 8, 4096, sink, 1, None) == inv    # misaligned
+    assert L.pkd_read_stream(buf, 4096, sink, 0, None) == inv        # grid
+    assert L.pkd_read_stream(buf, 4096, sink, (1 << 20) + 1, None) == inv
+    assert L.pkd_read_stream(None, 4096, sink, 1, None) == inv
+    assert L.pkd_read_stream(buf, 4096, None, 1, None) == inv
+    assert L.pkd_read_pages(buf, 4, 1000, ids, 4, sink, 1, None) == inv   # not a power of two
+    assert L.pkd_read_pages(buf, 4, 8, ids, 4, sink, 1, None) == inv      # below 16
+    assert L.pkd_read_pages(buf, 0, 1024, ids, 4, sink, 1, None) == inv   # no pages
+    assert L.pkd_read_pages(buf, 4, 1024, ids, 0, sink, 1, None) == inv   # no ids
+    assert L.pkd_read_pages(buf, 4, 1024, None, 4, sink, 1, None) == inv
+    assert L.pkd_read_pages(buf, 4, 1024, ids, 4, sink, 0, None) == inv
