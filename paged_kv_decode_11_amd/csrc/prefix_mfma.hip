@@ -13,22 +13,23 @@
 // One workgroup (8 waves) takes one item: one KV head of one (group, row
 // block, chunk).  Wave w owns 16 query rows, 16 / g requests times the g
 // query heads of the KV head, so the workgroup covers 128 / g requests.
-// Per 32-token tile (two 16-token halves, each within one page):
-//   * every lane loads one 16-byte piece of one K row and of one V row of
-//     the head (32 rows x 256 bytes each), kDepth tiles ahead, and stages
+// Per 64-token tile (four 16-token quarters, each within one page):
+//   * every lane loads one 16-byte piece of two K rows and of two V rows of
+//     the head (64 rows x 256 bytes each), kDepth tiles ahead, and stages
 //     them in LDS row-major, the 16-byte pieces of row r rotated by XOR r;
-//   * S^T = K Q^T on the matrix cores (v_mfma_f32_16x16x32_bf16 per half, K
-//     from LDS as the A operand, the wave's q rows as B), which leaves lane l
-//     with the logits of query row l & 15 for tokens 4 (l >> 4) .. +3 of each
-//     half;
-//   * the online softmax per query row: a max over those 8 tokens and over
+//   * S^T = K Q^T on the matrix cores (v_mfma_f32_16x16x32_bf16 per quarter,
+//     K from LDS as the A operand, the wave's q rows as B), which leaves lane
+//     l with the logits of query row l & 15 for tokens 4 (l >> 4) .. +3 of
+//     each quarter;
+//   * the online softmax per query row: a max over those 16 tokens and over
 //     the 4 lanes holding the same row (permlane swaps), exponentials in base
 //     2;
 //   * O^T += V^T P^T on the matrix cores (v_mfma_f32_16x16x32_bf16, 32 tokens
-//     per instruction, 8 blocks of 16 elements of head_dim): the transposing
-//     LDS read (ds_read_b64_tr_b16) gives each lane the A operand of its head
-//     dim, 4 consecutive tokens of each half, and P as bf16 straight from the
-//     softmax registers is the B operand.  The product leaves lane l with
+//     -- two quarters -- per instruction, 8 blocks of 16 elements of
+//     head_dim): the transposing LDS read (ds_read_b64_tr_b16) gives each
+//     lane the A operand of its head dim, 4 consecutive tokens of each
+//     quarter, and P as bf16 straight from the softmax registers is the B
+//     operand.  The product leaves lane l with
 //     query row l & 15 (head dims 16 b + 4 (l >> 4) + v), the row the
 //     softmax keeps in that lane, so rescale factors and the final max and
 //     sum never move between lanes.
@@ -51,8 +52,9 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTile = 32;   // tokens per tile (two halves of 16)
-constexpr int kDepth = 8;   // tiles in flight per workgroup
+constexpr int kTile = 64;   // tokens per tile (four quarters of 16)
+constexpr int kDepth = 4;   // tiles in flight per workgroup
+constexpr int kLdRows = kTile / 32;  // tile rows each lane loads (32 rows per pass)
 
 struct PShared {
   uint4 k[2][kTile][16];  // K tile, row r's 16-byte piece c at [r][c ^ (r & 15)]
@@ -89,9 +91,8 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row16 = lane & 15;
   const int kg = lane >> 4;
-  // load role: tile row tid >> 4 (0..31, half tid >> 8), 16-byte piece tid & 15
+  // load role: tile rows (tid >> 4) + 32 i, 16-byte piece tid & 15
   const int ld_row = tid >> 4;
-  const int ld_half = tid >> 8;
   const int ld_piece = tid & 15;
   const int ld_slot = ld_piece ^ (ld_row & 15);
 
@@ -145,28 +146,33 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) acc[cb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    // This lane's token of tile t (clamped to the chunk: rows past its end
-    // repeat the last token; they are masked, and V of those rows is zeroed
-    // when staged) and the page id of that token.
-    auto token_of = [&](int t) { return min(kTile * t + ld_row, last_token); };
+    // This lane's token of row ld_row + 32 i of tile t (clamped to the
+    // chunk: rows past its end repeat the last token; they are masked, and V
+    // of those rows is zeroed when staged) and the page id of that token.
+    auto token_of = [&](int t, int i) { return min(kTile * t + 32 * i + ld_row, last_token); };
     // (threadIdx.y is 0 in this one-dimensional launch; adding it makes the
     // page-id load a per-lane one, so its wait sits where the id is used)
-    auto page_of = [&](int t) -> int32_t { return idx[token_of(t) / P + int(threadIdx.y)]; };
-    auto piece_addr = [&](int t, int32_t id) -> const uint4* {
+    auto page_of = [&](int t, int i) -> int32_t {
+      return idx[token_of(t, i) / P + int(threadIdx.y)];
+    };
+    auto piece_addr = [&](int t, int i, int32_t id) -> const uint4* {
       const int64_t pg = safe_page(id, num_pages, bad);
-      const uint64_t off = uint64_t(pg) * page_bytes + uint64_t(token_of(t) % P) * row_bytes +
+      const uint64_t off = uint64_t(pg) * page_bytes + uint64_t(token_of(t, i) % P) * row_bytes +
                            uint64_t(kh) * kHeadDim * 2 + uint64_t(ld_piece) * 16;
       return reinterpret_cast<const uint4*>(kv + off);
     };
 
-    // Ring of kDepth tiles in registers (K and V piece per lane) and the page
-    // ids of the tiles each slot loads next.  Loads are issued
-    // unconditionally and in the same order in the prologue and the loop
-    // (tile, then a page id), so every wait is for one specific older load.
-    uint4 rk[kDepth], rv[kDepth];
-    int32_t pid[kDepth];
+    // Ring of kDepth tiles in registers (K and V pieces of kLdRows rows per
+    // lane) and the page ids of the tiles each slot loads next.  Loads are
+    // issued unconditionally and in the same order in the prologue and the
+    // loop (tile, then its page ids), so every wait is for one specific
+    // older load.
+    uint4 rk[kDepth][kLdRows], rv[kDepth][kLdRows];
+    int32_t pid[kDepth][kLdRows];
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) pid[d] = page_of(min(d, ntiles - 1));
+    for (int d = 0; d < kDepth; ++d)
+#pragma unroll
+      for (int i = 0; i < kLdRows; ++i) pid[d][i] = page_of(min(d, ntiles - 1), i);
     // the group's rows are needed only for q, which is loaded after the
     // first tile
     const int row0 = groups[4 * grp + 0];
@@ -181,10 +187,14 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
     uint4 qv[4];
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
-      const uint4* a = piece_addr(min(d, ntiles - 1), pid[d]);
-      rk[d] = load_stream16(a);
-      rv[d] = load_stream16(reinterpret_cast<const char*>(a) + v_bytes);
-      pid[d] = page_of(min(d + kDepth, ntiles - 1));
+#pragma unroll
+      for (int i = 0; i < kLdRows; ++i) {
+        const uint4* a = piece_addr(min(d, ntiles - 1), i, pid[d][i]);
+        rk[d][i] = load_stream16(a);
+        rv[d][i] = load_stream16(reinterpret_cast<const char*>(a) + v_bytes);
+      }
+#pragma unroll
+      for (int i = 0; i < kLdRows; ++i) pid[d][i] = page_of(min(d + kDepth, ntiles - 1), i);
       __builtin_amdgcn_sched_barrier(0);
       if (d == 0) {
         nreq = min(kReqPerWave, rows - wrow);  // <= 0: the wave only loads
@@ -204,73 +214,90 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
     }
 
     float m = kNegInf, lsum = 0.f;
-    auto step = [&](uint4& sk, uint4& sv, int32_t& next_page, int n, bool reload) {
+    auto step = [&](uint4 (&sk)[kLdRows], uint4 (&sv)[kLdRows], int32_t (&next_page)[kLdRows],
+                    int n, bool reload) {
       const int stage = n & 1;
       const bool last = n == ntiles - 1;
       const int valid = last ? last_valid : kTile;
       // stage tile n; V rows past the valid ones are zero (a zero probability
       // must not meet a repeated or NaN value)
-      sh.k[stage][ld_row][ld_slot] = sk;
-      sh.v[stage][ld_row][ld_slot] = ld_row < valid ? sv : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int i = 0; i < kLdRows; ++i) {
+        const int r = 32 * i + ld_row;
+        sh.k[stage][r][ld_slot] = sk[i];
+        sh.v[stage][r][ld_slot] = r < valid ? sv[i] : make_uint4(0u, 0u, 0u, 0u);
+      }
       lds_barrier();
       if (reload) {
-        const int32_t page = next_page;
-        const uint4* a = piece_addr(min(n + kDepth, ntiles - 1), page);
-        sk = load_stream16(a);
-        sv = load_stream16(reinterpret_cast<const char*>(a) + v_bytes);
-        next_page = page_of(min(n + 2 * kDepth, ntiles - 1));
+#pragma unroll
+        for (int i = 0; i < kLdRows; ++i) {
+          const uint4* a = piece_addr(min(n + kDepth, ntiles - 1), i, next_page[i]);
+          sk[i] = load_stream16(a);
+          sv[i] = load_stream16(reinterpret_cast<const char*>(a) + v_bytes);
+        }
+#pragma unroll
+        for (int i = 0; i < kLdRows; ++i)
+          next_page[i] = page_of(min(n + 2 * kDepth, ntiles - 1), i);
       }
       if (!compute) return;
 
-      // S^T = K Q^T per half: lane l gets query row l & 15, tokens
+      // S^T = K Q^T per quarter h: lane l gets query row l & 15, tokens
       // 16 h + 4 kg + v
-      floatx4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      floatx4_t sq[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        s0 = mfma32(sh.k[stage][row16][(4 * j + kg) ^ row16], qv[j], s0);
-        s1 = mfma32(sh.k[stage][16 + row16][(4 * j + kg) ^ row16], qv[j], s1);
-      }
-      float sc[8];
+      for (int h = 0; h < 4; ++h) sq[h] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          sq[h] = mfma32(sh.k[stage][16 * h + row16][(4 * j + kg) ^ row16], qv[j], sq[h]);
+      float sc[16];
       float mx = kNegInf;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        sc[v] = (4 * kg + v < valid) ? s0[v] * scale_log2 : kNegInf;
-        sc[4 + v] = (16 + 4 * kg + v < valid) ? s1[v] * scale_log2 : kNegInf;
-      }
+      for (int h = 0; h < 4; ++h)
 #pragma unroll
-      for (int v = 0; v < 8; ++v) mx = fmaxf(mx, sc[v]);
+        for (int v = 0; v < 4; ++v)
+          sc[4 * h + v] = (16 * h + 4 * kg + v < valid) ? sq[h][v] * scale_log2 : kNegInf;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[v]);
       const float mn = fmaxf(m, rows_max(mx));
       const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 while m = -inf
-      float p[8];
+      float p[16];
       float ps = 0.f;
 #pragma unroll
-      for (int v = 0; v < 8; ++v) {
+      for (int v = 0; v < 16; ++v) {
         p[v] = __builtin_amdgcn_exp2f(sc[v] - mn);
         ps += p[v];
       }
       lsum = fmaf(lsum, alpha, ps);
       m = mn;
-      // P^T as the B operand: k = 8 kg + j <-> token 4 kg + j (j < 4) of the
-      // first half and 16 + 4 kg + j - 4 of the second
-      const uint4 pb = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                  pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+      // P^T as the B operand of the product over quarters 2 e and 2 e + 1:
+      // k = 8 kg + j <-> token 4 kg + j (j < 4) of the first quarter and
+      // 16 + 4 kg + j - 4 of the second
+      uint4 pb[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        pb[e] = make_uint4(pack_bf16x2(p[8 * e + 0], p[8 * e + 1]),
+                           pack_bf16x2(p[8 * e + 2], p[8 * e + 3]),
+                           pack_bf16x2(p[8 * e + 4], p[8 * e + 5]),
+                           pack_bf16x2(p[8 * e + 6], p[8 * e + 7]));
       // V^T as the A operand of head-dim block cb: lane (kg, i = 4 r + q)
-      // points the transposing read at row 4 kg + r, elements cb 16 + 4 q ..
-      // + 3 of each half
+      // points the transposing read at row 4 kg + r of each quarter,
+      // elements cb 16 + 4 q .. + 3
       const int tr_row = 4 * kg + (row16 >> 2);
       const int tr_q = row16 & 3;
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb) {
         const int piece = 2 * cb + (tr_q >> 1);
-        const char* r0 = reinterpret_cast<const char*>(&sh.v[stage][tr_row][piece ^ tr_row]) +
-                         8 * (tr_q & 1);
-        const char* r1 =
-            reinterpret_cast<const char*>(&sh.v[stage][16 + tr_row][piece ^ tr_row]) +
-            8 * (tr_q & 1);
-        const uint2 b0 = lds_read_tr(r0);
-        const uint2 b1 = lds_read_tr(r1);
+        uint2 b[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          b[h] = lds_read_tr(
+              reinterpret_cast<const char*>(&sh.v[stage][16 * h + tr_row][piece ^ tr_row]) +
+              8 * (tr_q & 1));
         acc[cb] *= alpha;
-        acc[cb] = mfma32(make_uint4(b0.x, b0.y, b1.x, b1.y), pb, acc[cb]);
+        acc[cb] = mfma32(make_uint4(b[0].x, b[0].y, b[1].x, b[1].y), pb[0], acc[cb]);
+        acc[cb] = mfma32(make_uint4(b[2].x, b[2].y, b[3].x, b[3].y), pb[1], acc[cb]);
       }
     };
 
