@@ -44,7 +44,7 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_step",
                     choices=["llama8b_step", "skewed", "wide_gqa", "token_sparse", "tiny",
@@ -595,9 +595,23 @@ def main():
         torch.cuda.synchronize()
         tg1 = time.perf_counter()
         g_ms = (tg1 - tg0) * 1e3 / args.steps
+        # per-step spread: events around each plan + replay, steps back to
+        # back (each sample runs from the previous step's end to this one's)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for e0, e1 in evs:
+            e0.record()
+            plan()
+            g.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        per = sorted(e0.elapsed_time(e1) * 1e3 / n_layers for e0, e1 in evs)
+        pct = lambda f: round(per[min(len(per) - 1, int(f * len(per)))], 2)
         graph = {"ms_per_step": round(g_ms, 4), "us_per_layer_step": round(g_ms * 1e3 / n_layers, 2),
-                 "kv_gbs": round(step_bytes / (g_ms / 1e3) / 1e9, 1)}
-        log(f"graph: {g_ms:.3f} ms/step, {graph['kv_gbs']} GB/s")
+                 "kv_gbs": round(step_bytes / (g_ms / 1e3) / 1e9, 1),
+                 "us_per_layer_step_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)]}
+        log(f"graph: {g_ms:.3f} ms/step, {graph['kv_gbs']} GB/s, per-step spread "
+            f"{graph['us_per_layer_step_p10_p50_p90']} us/layer")
         del g
 
     # the headline is the graph-replayed step when graphs are on (the serving
