@@ -69,6 +69,7 @@ KERNEL_FILES = {
     "decode_kernel": ("decode.hip", "device_common.h", "plan_layout.h"),
     "decode_fp8_kernel": ("decode_fp8.hip", "device_common.h", "plan_layout.h"),
     "decode_pv_kernel": ("decode_pv.hip", "device_common.h", "plan_layout.h"),
+    "prefix_mfma_kernel": ("prefix_mfma.hip", "device_common.h", "plan_layout.h"),
 }
 
 
@@ -363,7 +364,8 @@ def bench_shared_prefix(args):
         "single_format_kv_bytes_per_layer": single_bytes,
         "single_format_kv_gbs": round(single_bytes * R / (ms1 / 1e3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic("shared_prefix", "prefix_mfma_kernel", "bf16"),
                      "kernel": "prefix_mfma_kernel", "avg_launch_us": round(prefix_us, 2),
                      "algorithmic_bytes_per_launch": prefix_bytes,
                      "merge_avg_launch_us": round(prefix_merge_us, 2)},
