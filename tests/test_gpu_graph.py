@@ -14,7 +14,8 @@ from tests import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replay_across_plans():
+@pytest.mark.parametrize("variant", ["auto", "dot2", "mfma_pv"])
+def test_graph_replay_across_plans(variant):
     import torch
     import paged_kv_decode_11_amd as pkd
 
@@ -40,7 +41,7 @@ def test_graph_replay_across_plans():
     # dummy plan at the maximum batch, then capture run on it
     b0, q0, _ = make_step(MAXB, 1)
     r.plan(b0.kv_indptr, torch.from_numpy(b0.kv_indices).cuda(), b0.kv_last_page_len, Hq, Hkv,
-           128, P)
+           128, P, variant=variant)
     q_buf.copy_(gu.bits_to_dev(q0))
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -57,9 +58,10 @@ def test_graph_replay_across_plans():
     steps = [(MAXB, 2, 0), (17, 3, 2), (5, 4, 1), (MAXB, 5, 0)]
     for B, seed, fixed in steps:
         b, q, fixed = make_step(B, seed, fixed)
-        gu.say("graph step", B, seed, fixed)
+        gu.say("graph step", variant, B, seed, fixed)
         idx = torch.from_numpy(b.kv_indices).cuda()
-        r.plan(b.kv_indptr, idx, b.kv_last_page_len, Hq, Hkv, 128, P, fixed_chunk_pages=fixed)
+        r.plan(b.kv_indptr, idx, b.kv_last_page_len, Hq, Hkv, 128, P, fixed_chunk_pages=fixed,
+               variant=variant)
         q_buf[:B].copy_(gu.bits_to_dev(q))
         g.replay()
         torch.cuda.synchronize()
@@ -67,4 +69,4 @@ def test_graph_replay_across_plans():
         torch.cuda.synchronize()
         assert torch.isfinite(junk)
         o_ref, lse_ref = att.decode(q, cache, b.kv_indptr, b.kv_indices, b.kv_last_page_len, Hkv)
-        gu.assert_close(o_buf[:B], lse_buf[:B], o_ref, lse_ref, label=f"replay-{seed}")
+        gu.assert_close(o_buf[:B], lse_buf[:B], o_ref, lse_ref, label=f"replay-{variant}-{seed}")
