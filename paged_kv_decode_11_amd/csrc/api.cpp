@@ -393,17 +393,18 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
   h->P = page_size;
   h->q_dtype = q_dtype;
   h->kv_dtype = kv_dtype;
-  // The default kernel, by measurement on 64 requests of 3-5k tokens: pages
-  // below 16 tokens stream faster through the dot-product kernel (its
-  // per-token rows suit them; 1.2-1.5x); group size 8 with larger pages
-  // faster with p.v on the matrix cores (1.3x); otherwise the matrix-core
-  // q.k kernel leads.  An FP8 cache has its own kernel.
+  // The default kernel, by measurement on 64 requests of 3-5k tokens: group
+  // size 8 runs faster with both products on the matrix cores (1.3x with
+  // pages of 16-64 tokens, 1.4x below); smaller groups with pages below 16
+  // tokens stream faster through the dot-product kernel (its per-token rows
+  // suit them; 1.2-1.5x); otherwise the matrix-core q.k kernel leads.  An
+  // FP8 cache has its own kernel.
   if (variant == PKD_VARIANT_AUTO) {
     const int g = num_qo_heads / num_kv_heads;
-    if (kv_dtype == PKD_DTYPE_BF16 && page_size < 16)
-      h->variant = PKD_VARIANT_DOT2;
-    else if (kv_dtype == PKD_DTYPE_BF16 && g == 8 && pkd::pv_variant_built(g, page_size))
+    if (kv_dtype == PKD_DTYPE_BF16 && g == 8 && pkd::pv_variant_built(g, page_size))
       h->variant = PKD_VARIANT_MFMA_PV;
+    else if (kv_dtype == PKD_DTYPE_BF16 && page_size < 16)
+      h->variant = PKD_VARIANT_DOT2;
     else
       h->variant = PKD_VARIANT_MFMA;
   } else {

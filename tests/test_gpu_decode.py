@@ -200,15 +200,15 @@ def test_variants_agree():
 
 
 def test_auto_variant_by_shape():
-    """The default kernel: the dot-product kernel for pages below 16 tokens,
-    both products on the matrix cores for group size 8 with pages of 16-64
-    tokens, q.k on the matrix cores otherwise; explicit variants are kept."""
+    """The default kernel: both products on the matrix cores for group size
+    8, the dot-product kernel for smaller groups with pages below 16 tokens,
+    q.k on the matrix cores otherwise; explicit variants are kept."""
     import torch
 
     r = gu.runner(max_batch=64, max_nnz=1 << 12)
-    for P, Hq, Hkv, want in ((16, 64, 8, "mfma_pv"), (64, 8, 1, "mfma_pv"), (8, 64, 8, "dot2"),
-                             (1, 32, 8, "dot2"), (16, 32, 8, "mfma"), (16, 8, 8, "mfma"),
-                             (32, 16, 8, "mfma")):
+    for P, Hq, Hkv, want in ((16, 64, 8, "mfma_pv"), (64, 8, 1, "mfma_pv"), (8, 64, 8, "mfma_pv"),
+                             (1, 64, 8, "mfma_pv"), (1, 32, 8, "dot2"), (4, 16, 8, "dot2"),
+                             (16, 32, 8, "mfma"), (16, 8, 8, "mfma"), (32, 16, 8, "mfma")):
         batch, q, cache = _small(3, [40, 7], P, Hq, Hkv)
         idx = torch.from_numpy(batch.kv_indices).cuda()
         r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, Hq, Hkv, 128, P)
