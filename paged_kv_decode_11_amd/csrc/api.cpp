@@ -393,18 +393,16 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
   h->P = page_size;
   h->q_dtype = q_dtype;
   h->kv_dtype = kv_dtype;
-  // The default kernel, by measurement on 64 requests of 3-5k tokens: group
-  // size 8 runs faster with both products on the matrix cores (1.3x with
-  // pages of 16-64 tokens, 1.4x below); smaller groups with pages below 16
-  // tokens stream faster through the dot-product kernel (its per-token rows
-  // suit them; 1.2-1.5x); otherwise the matrix-core q.k kernel leads.  An
-  // FP8 cache has its own kernel.
+  // The default kernel, by measurement on 64 requests of 3-5k tokens: both
+  // products on the matrix cores for pages below 16 tokens (1.0-1.7x faster
+  // than the dot-product kernel, 1.3x on the token-sparse batch) and for
+  // group size 8 (1.3x with pages of 16-64 tokens); otherwise the matrix-core
+  // q.k kernel leads.  An FP8 cache has its own kernel.
   if (variant == PKD_VARIANT_AUTO) {
     const int g = num_qo_heads / num_kv_heads;
-    if (kv_dtype == PKD_DTYPE_BF16 && g == 8 && pkd::pv_variant_built(g, page_size))
+    if (kv_dtype == PKD_DTYPE_BF16 && (page_size < 16 || g == 8) &&
+        pkd::pv_variant_built(g, page_size))
       h->variant = PKD_VARIANT_MFMA_PV;
-    else if (kv_dtype == PKD_DTYPE_BF16 && page_size < 16)
-      h->variant = PKD_VARIANT_DOT2;
     else
       h->variant = PKD_VARIANT_MFMA;
   } else {

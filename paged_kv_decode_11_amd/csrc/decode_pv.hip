@@ -196,13 +196,15 @@ struct VState {
 // One tile.  With kPrefetch a later tile's loads are issued first; the last
 // tile (kLast) masks tokens >= valid: logits to -inf, V rows to zero (a slot
 // past the sequence may hold any value).
-template <bool kPrefetch, bool kLast, int P>
+// With kAfterStage (the two-tile ring) the later tile is requested into
+// `nxt` only once this tile has been staged in LDS, so `nxt` may be `cur`.
+template <bool kPrefetch, bool kLast, int P, bool kAfterStage = false>
 __device__ __forceinline__ void v_step(VState& st, const VTile& cur, VTile& nxt, const VCtx& c,
                                        const VRef<P>& next, int valid, int lane, float scale_log2,
                                        VShared& sh) {
   const int row16 = lane & 15;
   const int kg = lane >> 4;
-  if constexpr (kPrefetch) {
+  if constexpr (kPrefetch && !kAfterStage) {
     __builtin_amdgcn_sched_barrier(0);
     v_load(nxt, c, next);
     __builtin_amdgcn_sched_barrier(0);
@@ -218,6 +220,11 @@ __device__ __forceinline__ void v_step(VState& st, const VTile& cur, VTile& nxt,
       if (r >= valid) w = make_uint4(0u, 0u, 0u, 0u);
     }
     sh.vt[r][row16 ^ r] = w;
+  }
+  if constexpr (kPrefetch && kAfterStage) {
+    __builtin_amdgcn_sched_barrier(0);
+    v_load(nxt, c, next);
+    __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_wave_barrier();
 
@@ -390,6 +397,41 @@ void decode_pv_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __rest
       const int last_valid = len - 16 * (ntiles - 1);
       const VRef<P> none = {};
       int n = 0;
+      if constexpr (P % 16 != 0) {
+        // Pages below 16 tokens: each lane also carries its rows' addresses,
+        // and a third tile in registers would spill, so two tiles form the
+        // ring and each is refilled as soon as it is staged in LDS.
+        auto step2 = [&](VTile& cur) -> bool {
+          if (n == ntiles - 1) {
+            v_step<false, true, P, true>(st, cur, cur, c, none, last_valid, lane, scale_log2, sh);
+            return true;
+          }
+          if (n + 2 < ntiles) {
+            const VRef<P> ref = v_ref<P>(c, id_next, len, n + 2, kg, bad);
+            id_next = v_read_ids<P>(idx, len, min(n + 3, ntiles - 1), kg);
+            v_step<true, false, P, true>(st, cur, cur, c, ref, 16, lane, scale_log2, sh);
+          } else {
+            v_step<false, false, P, true>(st, cur, cur, c, none, 16, lane, scale_log2, sh);
+          }
+          ++n;
+          return false;
+        };
+        while (n + 3 < ntiles) {
+          keep_pace<kMaxWavesPerBlock>(progress, wave, nwaves, lockstep, done_tiles + n);
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            VTile& cur = k == 0 ? ta : tb;
+            const VRef<P> ref = v_ref<P>(c, id_next, len, n + 2, kg, bad);
+            id_next = v_read_ids<P>(idx, len, min(n + 3, ntiles - 1), kg);
+            v_step<true, false, P, true>(st, cur, cur, c, ref, 16, lane, scale_log2, sh);
+            ++n;
+          }
+        }
+        for (;;) {
+          if (step2(ta)) break;
+          if (step2(tb)) break;
+        }
+      } else {
       auto step = [&](VTile& cur, VTile& nxt) -> bool {
         if (n == ntiles - 1) {
           v_step<false, true>(st, cur, nxt, c, none, last_valid, lane, scale_log2, sh);
@@ -426,6 +468,7 @@ void decode_pv_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __rest
         if (step(ta, tc)) break;
         if (step(tb, ta)) break;
         if (step(tc, tb)) break;
+      }
       }
       if (bad && lane == 0) err[0] = PKD_DEVERR_PAGE_ID;
       __builtin_amdgcn_s_setprio(0);

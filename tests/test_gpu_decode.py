@@ -200,14 +200,14 @@ def test_variants_agree():
 
 
 def test_auto_variant_by_shape():
-    """The default kernel: both products on the matrix cores for group size
-    8, the dot-product kernel for smaller groups with pages below 16 tokens,
-    q.k on the matrix cores otherwise; explicit variants are kept."""
+    """The default kernel: both products on the matrix cores for pages below
+    16 tokens and for group size 8, q.k on the matrix cores otherwise;
+    explicit variants are kept."""
     import torch
 
     r = gu.runner(max_batch=64, max_nnz=1 << 12)
     for P, Hq, Hkv, want in ((16, 64, 8, "mfma_pv"), (64, 8, 1, "mfma_pv"), (8, 64, 8, "mfma_pv"),
-                             (1, 64, 8, "mfma_pv"), (1, 32, 8, "dot2"), (4, 16, 8, "dot2"),
+                             (1, 64, 8, "mfma_pv"), (1, 32, 8, "mfma_pv"), (4, 16, 8, "mfma_pv"),
                              (16, 32, 8, "mfma"), (16, 8, 8, "mfma"), (32, 16, 8, "mfma")):
         batch, q, cache = _small(3, [40, 7], P, Hq, Hkv)
         idx = torch.from_numpy(batch.kv_indices).cuda()
