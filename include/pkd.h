@@ -88,8 +88,9 @@ typedef struct pkd_plan_opts {
 /* Decode kernels.  Both compute the same result (to rounding); they differ
  * in where q.k is evaluated. */
 enum {
-  PKD_VARIANT_AUTO = 0,    /* by measurement: PKD_VARIANT_MFMA_PV for pages below 16
-                              tokens and for group size 8, PKD_VARIANT_MFMA otherwise */
+  PKD_VARIANT_AUTO = 0,    /* by measurement: PKD_VARIANT_MFMA_PV for group size 8, pages
+                              below 16 tokens or fewer than 768 KV tokens per slot,
+                              PKD_VARIANT_MFMA otherwise */
   PKD_VARIANT_DOT2 = 1,    /* q.k with packed bf16 dot products on the vector ALUs */
   PKD_VARIANT_MFMA = 2,    /* q.k as a 16 x 16 tile on the matrix cores (GQA group as rows),
                               p.v on the vector ALUs */

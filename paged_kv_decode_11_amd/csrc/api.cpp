@@ -150,6 +150,10 @@ int check_shared_shapes(int32_t Hq, int32_t Hkv, int32_t P) {
 
 }  // namespace
 
+// Below this many KV tokens per persistent slot the default bf16 kernel is
+// the one with both products on the matrix cores (see pkd_plan).
+constexpr int64_t kPvMaxTokensPerSlot = 768;
+
 extern "C" {
 
 const char* pkd_last_error(void) { return g_last_error.c_str(); }
@@ -393,18 +397,20 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
   h->P = page_size;
   h->q_dtype = q_dtype;
   h->kv_dtype = kv_dtype;
-  // The default kernel, by measurement on 64 requests of 3-5k tokens: both
-  // products on the matrix cores for pages below 16 tokens (1.0-1.7x faster
-  // than the dot-product kernel, 1.3x on the token-sparse batch) and for
-  // group size 8 (1.3x with pages of 16-64 tokens); otherwise the matrix-core
-  // q.k kernel leads.  An FP8 cache has its own kernel.
+  // The default kernel, by measurement in the benchmark (caches streamed from
+  // HBM, alternating runs on one box): both products on the matrix cores for
+  // group size 8 (1.3-1.4x), for pages below 16 tokens (1.0-1.7x over the
+  // dot-product kernel) and where each slot has little work (skewed batch,
+  // about 520 tokens per slot: 87.8 vs 92.1 us); with about 1,000 tokens per
+  // slot and smaller groups the q.k-only matrix-core kernel streams faster
+  // (Llama-3-8B-like layer: 156.1 vs 160.8 us).  An FP8 cache has its own
+  // kernel.
   if (variant == PKD_VARIANT_AUTO) {
     const int g = num_qo_heads / num_kv_heads;
-    if (kv_dtype == PKD_DTYPE_BF16 && (page_size < 16 || g == 8) &&
-        pkd::pv_variant_built(g, page_size))
-      h->variant = PKD_VARIANT_MFMA_PV;
-    else
-      h->variant = PKD_VARIANT_MFMA;
+    const int64_t tokens_per_slot = layout.total_tokens / h->num_slots;
+    const bool pv = kv_dtype == PKD_DTYPE_BF16 && pkd::pv_variant_built(g, page_size) &&
+                    (g == 8 || page_size < 16 || tokens_per_slot < kPvMaxTokensPerSlot);
+    h->variant = pv ? PKD_VARIANT_MFMA_PV : PKD_VARIANT_MFMA;
   } else {
     h->variant = variant;
   }

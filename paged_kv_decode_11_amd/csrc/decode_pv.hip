@@ -23,10 +23,11 @@
 //   accumulate.  Lane l ends with query row l & 15, so rescale factors and
 //   the final max and sum never cross lanes.
 //
-// Streaming as in the FP8 kernel: three tiles in a register ring (two in
-// flight), a straight-line steady state of three prefetching tiles per trip,
-// and a workgroup barrier plus issue priority per trip keeping the two waves
-// of each SIMD together.  Page sizes that are multiples of 16 keep each tile
+// Streaming: two tiles in a register ring, each refilled with the tile two
+// ahead as soon as it has been staged in LDS, so while one tile is computed
+// the next two are in flight; a straight-line steady state of two tiles per
+// trip, and a workgroup barrier plus issue priority per trip keeping the two
+// waves of each SIMD together.  Page sizes that are multiples of 16 keep each tile
 // in one page, addressed through a buffer descriptor over the page; smaller
 // pages (1, 2, 4, 8 tokens) give each lane the address of each of its rows.
 
@@ -196,19 +197,14 @@ struct VState {
 // One tile.  With kPrefetch a later tile's loads are issued first; the last
 // tile (kLast) masks tokens >= valid: logits to -inf, V rows to zero (a slot
 // past the sequence may hold any value).
-// With kAfterStage (the two-tile ring) the later tile is requested into
-// `nxt` only once this tile has been staged in LDS, so `nxt` may be `cur`.
-template <bool kPrefetch, bool kLast, int P, bool kAfterStage = false>
+// With kPrefetch the later tile is requested into `nxt` once this tile has
+// been staged in LDS, so `nxt` may be `cur` (the two-tile ring).
+template <bool kPrefetch, bool kLast, int P>
 __device__ __forceinline__ void v_step(VState& st, const VTile& cur, VTile& nxt, const VCtx& c,
                                        const VRef<P>& next, int valid, int lane, float scale_log2,
                                        VShared& sh) {
   const int row16 = lane & 15;
   const int kg = lane >> 4;
-  if constexpr (kPrefetch && !kAfterStage) {
-    __builtin_amdgcn_sched_barrier(0);
-    v_load(nxt, c, next);
-    __builtin_amdgcn_sched_barrier(0);
-  }
   // stage the tile (the previous tile's reads come first in program order,
   // and one wave's LDS accesses complete in order)
 #pragma unroll
@@ -221,7 +217,7 @@ __device__ __forceinline__ void v_step(VState& st, const VTile& cur, VTile& nxt,
     }
     sh.vt[r][row16 ^ r] = w;
   }
-  if constexpr (kPrefetch && kAfterStage) {
+  if constexpr (kPrefetch) {
     __builtin_amdgcn_sched_barrier(0);
     v_load(nxt, c, next);
     __builtin_amdgcn_sched_barrier(0);
@@ -375,7 +371,7 @@ void decode_pv_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __rest
       for (int b = 0; b < 8; ++b) st.o[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
       int bad = 0;
-      VTile ta, tb, tc;
+      VTile ta, tb;
       // both loads unconditional (a one-tile item reads its tile twice), so
       // the same loads are in flight on every path and the waits stay exact
       VIds<P> ids0, ids1;
@@ -397,78 +393,39 @@ void decode_pv_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __rest
       const int last_valid = len - 16 * (ntiles - 1);
       const VRef<P> none = {};
       int n = 0;
-      if constexpr (P % 16 != 0) {
-        // Pages below 16 tokens: each lane also carries its rows' addresses,
-        // and a third tile in registers would spill, so two tiles form the
-        // ring and each is refilled as soon as it is staged in LDS.
-        auto step2 = [&](VTile& cur) -> bool {
-          if (n == ntiles - 1) {
-            v_step<false, true, P, true>(st, cur, cur, c, none, last_valid, lane, scale_log2, sh);
-            return true;
-          }
-          if (n + 2 < ntiles) {
-            const VRef<P> ref = v_ref<P>(c, id_next, len, n + 2, kg, bad);
-            id_next = v_read_ids<P>(idx, len, min(n + 3, ntiles - 1), kg);
-            v_step<true, false, P, true>(st, cur, cur, c, ref, 16, lane, scale_log2, sh);
-          } else {
-            v_step<false, false, P, true>(st, cur, cur, c, none, 16, lane, scale_log2, sh);
-          }
-          ++n;
-          return false;
-        };
-        while (n + 3 < ntiles) {
-          keep_pace<kMaxWavesPerBlock>(progress, wave, nwaves, lockstep, done_tiles + n);
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            VTile& cur = k == 0 ? ta : tb;
-            const VRef<P> ref = v_ref<P>(c, id_next, len, n + 2, kg, bad);
-            id_next = v_read_ids<P>(idx, len, min(n + 3, ntiles - 1), kg);
-            v_step<true, false, P, true>(st, cur, cur, c, ref, 16, lane, scale_log2, sh);
-            ++n;
-          }
-        }
-        for (;;) {
-          if (step2(ta)) break;
-          if (step2(tb)) break;
-        }
-      } else {
-      auto step = [&](VTile& cur, VTile& nxt) -> bool {
+      // Two tiles form the ring; each is refilled as soon as it is staged in
+      // LDS (its registers are free from then on), so while a tile is
+      // computed the next one and the one after it are in flight.  Two tiles
+      // per straight-line trip.
+      auto step2 = [&](VTile& cur) -> bool {
         if (n == ntiles - 1) {
-          v_step<false, true>(st, cur, nxt, c, none, last_valid, lane, scale_log2, sh);
+          v_step<false, true, P>(st, cur, cur, c, none, last_valid, lane, scale_log2, sh);
           return true;
         }
         if (n + 2 < ntiles) {
           const VRef<P> ref = v_ref<P>(c, id_next, len, n + 2, kg, bad);
           id_next = v_read_ids<P>(idx, len, min(n + 3, ntiles - 1), kg);
-          v_step<true, false>(st, cur, nxt, c, ref, 16, lane, scale_log2, sh);
+          v_step<true, false, P>(st, cur, cur, c, ref, 16, lane, scale_log2, sh);
         } else {
-          v_step<false, false>(st, cur, nxt, c, none, 16, lane, scale_log2, sh);
+          v_step<false, false, P>(st, cur, cur, c, none, 16, lane, scale_log2, sh);
         }
         ++n;
         return false;
       };
-      // Steady state: three prefetching tiles per trip with the ring in
-      // place, straight-line, so no register tile is copied at a branch
-      // merge (a copy of a tile still in flight would wait for every load).
-      while (n + 4 < ntiles) {
-        // keep the waves of the workgroup together, once per trip
+      while (n + 3 < ntiles) {
         keep_pace<kMaxWavesPerBlock>(progress, wave, nwaves, lockstep, done_tiles + n);
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-          VTile& cur = k == 0 ? ta : k == 1 ? tb : tc;
-          VTile& nxt = k == 0 ? tc : k == 1 ? ta : tb;
+        for (int k = 0; k < 2; ++k) {
+          VTile& cur = k == 0 ? ta : tb;
           const VRef<P> ref = v_ref<P>(c, id_next, len, n + 2, kg, bad);
           id_next = v_read_ids<P>(idx, len, min(n + 3, ntiles - 1), kg);
-          v_step<true, false>(st, cur, nxt, c, ref, 16, lane, scale_log2, sh);
+          v_step<true, false, P>(st, cur, cur, c, ref, 16, lane, scale_log2, sh);
           ++n;
         }
       }
-      // the last one to four tiles
       for (;;) {
-        if (step(ta, tc)) break;
-        if (step(tb, ta)) break;
-        if (step(tc, tb)) break;
-      }
+        if (step2(ta)) break;
+        if (step2(tb)) break;
       }
       if (bad && lane == 0) err[0] = PKD_DEVERR_PAGE_ID;
       __builtin_amdgcn_s_setprio(0);

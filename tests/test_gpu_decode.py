@@ -200,20 +200,33 @@ def test_variants_agree():
 
 
 def test_auto_variant_by_shape():
-    """The default kernel: both products on the matrix cores for pages below
-    16 tokens and for group size 8, q.k on the matrix cores otherwise;
-    explicit variants are kept."""
+    """The default kernel for a bf16 cache: both products on the matrix
+    cores for group size 8, pages below 16 tokens, or fewer than 768 KV
+    tokens per slot; q.k on the matrix cores otherwise; explicit variants are
+    kept."""
     import torch
 
     r = gu.runner(max_batch=64, max_nnz=1 << 12)
     for P, Hq, Hkv, want in ((16, 64, 8, "mfma_pv"), (64, 8, 1, "mfma_pv"), (8, 64, 8, "mfma_pv"),
                              (1, 64, 8, "mfma_pv"), (1, 32, 8, "mfma_pv"), (4, 16, 8, "mfma_pv"),
-                             (16, 32, 8, "mfma"), (16, 8, 8, "mfma"), (32, 16, 8, "mfma")):
+                             (16, 32, 8, "mfma_pv"), (16, 8, 8, "mfma_pv"),
+                             (32, 16, 8, "mfma_pv")):
         batch, q, cache = _small(3, [40, 7], P, Hq, Hkv)
         idx = torch.from_numpy(batch.kv_indices).cuda()
         r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, Hq, Hkv, 128, P)
         assert r.planned_variant == want, (P, Hq, Hkv, r.planned_variant)
-    r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, 8, 8, 128, 16, variant="mfma_pv")
-    assert r.planned_variant == "mfma_pv"
+    r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, 8, 8, 128, 16, variant="mfma")
+    assert r.planned_variant == "mfma"
+    # about 1,000 tokens per slot (a Llama-3-8B-like layer) against about 520
+    # (the skewed batch), planned only
+    big = gu.runner(max_batch=64, max_nnz=1 << 15)
+    rng = np.random.default_rng(5)
+    for lens, Hq, want in (([4000] * 64, 32, "mfma"), ([512] * 63 + [100000], 32, "mfma_pv"),
+                           ([4000] * 64, 64, "mfma_pv")):
+        b = workloads.make_batch(lens, 16, sum(-(-n // 16) for n in lens) + 8, Hq, 8, 128, rng)
+        big.plan(b.kv_indptr, torch.from_numpy(b.kv_indices).cuda(), b.kv_last_page_len, Hq, 8,
+                 128, 16)
+        per_slot = sum(lens) // big.num_slots
+        assert big.planned_variant == want, (per_slot, Hq, big.planned_variant)
     r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, 8, 8, 128, 16, variant="dot2")
     assert r.planned_variant == "dot2"
