@@ -33,7 +33,8 @@
 //   / l.
 //
 // K and V of the next two steps stream into registers while the current one
-// is computed (three steps in a ring), one wave per KV head as in the bf16
+// is computed (two steps in a ring, each refilled with the step two ahead
+// once its V is in LDS and its K consumed), one wave per KV head as in the bf16
 // matrix-core kernel; Q waits in LDS.  The two waves that share a SIMD keep
 // pace through issue priority (see the steady-state loop).  Page sizes 16, 32 and 64: each 16-token half of a
 // step lies in one page, addressed through a buffer descriptor over that
@@ -164,7 +165,9 @@ __device__ __forceinline__ FRef f_ref(const FCtx& c, const FIds& ids, int s, int
     // The id was requested a step earlier.  Passing it through an empty asm
     // here keeps its range check from being hoisted next to the load, where
     // it would make the step wait for the scalar load before its prefetch.
-    int32_t id = ids.id[h];
+    // (wave-uniform by construction; readfirstlane keeps it in a scalar
+    // register whatever the loop structure)
+    int32_t id = __builtin_amdgcn_readfirstlane(ids.id[h]);
     asm volatile("" : "+s"(id));
     const int64_t pg = safe_page(id, c.num_pages, bad);
     // raw buffer over one page (32-bit data format word as raw loads need);
@@ -201,20 +204,17 @@ struct FState {
   floatx4_t o[8];   // O^T block b: dims 16 b + 4 (l >> 4) + v of row l & 15, scaled by 2^15
 };
 
-// One 32-token step.  With kPrefetch a later step's loads are issued first;
-// the last step (kLast) masks tokens >= valid: their logits to -inf and
-// their V rows to zero (a slot past the sequence may hold any code).
+// One 32-token step.  With kPrefetch a later step's loads are issued into
+// `nxt` once this step's V is in LDS and its K has gone through the matrix
+// cores, so `nxt` may be `cur` (the two-step ring); the last step (kLast)
+// masks tokens >= valid: their logits to -inf and their V rows to zero (a
+// slot past the sequence may hold any code).
 template <int G, bool kPrefetch, bool kLast>
 __device__ __forceinline__ void f_step(FState<G>& st, const FStep& cur, FStep& nxt,
                                        const FCtx& c, const FRef& next,
                                        int valid, int lane, float scale_log2, FShared& sh,
                                        uint32_t v_wr, uint32_t v_rd) {
   const int kg = lane >> 4;
-  if constexpr (kPrefetch) {
-    __builtin_amdgcn_sched_barrier(0);
-    f_load(nxt, c, next);
-    __builtin_amdgcn_sched_barrier(0);
-  }
 
   // V rows to LDS in slot order (the previous step's transposed reads come
   // first in program order, and one wave's LDS accesses complete in order).
@@ -245,6 +245,11 @@ __device__ __forceinline__ void f_step(FState<G>& st, const FStep& cur, FStep& n
       const uint4 ka = (j & 1) ? fp8x8_to_bf16(kw.z, kw.w) : fp8x8_to_bf16(kw.x, kw.y);
       s[h] = mfma_bf16(ka, qj, s[h]);
     }
+  }
+  if constexpr (kPrefetch) {
+    __builtin_amdgcn_sched_barrier(0);
+    f_load(nxt, c, next);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // online softmax on row l & 15, tokens 16 h + 4 kg + v
@@ -397,7 +402,7 @@ void decode_fp8_kernel(const uint16_t* __restrict__ q_ptr, const uint8_t* __rest
       for (int b = 0; b < 8; ++b) st.o[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
       int bad = 0;
-      FStep ta, tb, tc;
+      FStep ta, tb;
       // both loads unconditional (a one-step item reads its step twice): with
       // the same loads in flight on every path, the wait counts stay exact
       // Step 0 lies in the item's first two pages (one, for P >= 32), whose
@@ -423,46 +428,44 @@ void decode_fp8_kernel(const uint16_t* __restrict__ q_ptr, const uint8_t* __rest
       const int last_valid = len - kStep * (nsteps - 1);
       const FRef none = {};
       int n = 0;
-      auto step = [&](FStep& cur, FStep& nxt) -> bool {
+      // Two steps form the ring; each is refilled with the step two ahead as
+      // soon as its V is in LDS and its K consumed, so while a step is
+      // computed the next two are in flight.  Two steps per straight-line
+      // trip.
+      auto step2 = [&](FStep& cur) -> bool {
         if (n == nsteps - 1) {
-          f_step<G, false, true>(st, cur, nxt, c, none, last_valid, lane, scale_log2, sh,
+          f_step<G, false, true>(st, cur, cur, c, none, last_valid, lane, scale_log2, sh,
                                  v_wr, v_rd);
           return true;
         }
         if (n + 2 < nsteps) {
           const FRef ref = f_ref<P>(c, ids_next, n + 2, bad);
           ids_next = f_read_ids<P>(idx, len, min(n + 3, nsteps - 1));
-          f_step<G, true, false>(st, cur, nxt, c, ref, kStep, lane, scale_log2, sh, v_wr,
+          f_step<G, true, false>(st, cur, cur, c, ref, kStep, lane, scale_log2, sh, v_wr,
                                  v_rd);
         } else {
-          f_step<G, false, false>(st, cur, nxt, c, none, kStep, lane, scale_log2, sh, v_wr,
+          f_step<G, false, false>(st, cur, cur, c, none, kStep, lane, scale_log2, sh, v_wr,
                                   v_rd);
         }
         ++n;
         return false;
       };
-      // Steady state: three prefetching steps per trip with the ring in
-      // place, straight-line, so no register tile is copied at a branch
-      // merge (a copy of a tile still in flight would wait for every load).
-      while (n + 4 < nsteps) {
+      while (n + 3 < nsteps) {
         // keep the waves of the workgroup together, once per trip (left alone,
         // waves 4-7 finished their heads at ~1.75x the time of waves 0-3)
         keep_pace<kMaxWavesPerBlock>(progress, wave, nwaves, lockstep, done_steps + n);
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-          FStep& cur = k == 0 ? ta : k == 1 ? tb : tc;
-          FStep& nxt = k == 0 ? tc : k == 1 ? ta : tb;
+        for (int k = 0; k < 2; ++k) {
+          FStep& cur = k == 0 ? ta : tb;
           const FRef ref = f_ref<P>(c, ids_next, n + 2, bad);
           ids_next = f_read_ids<P>(idx, len, min(n + 3, nsteps - 1));
-          f_step<G, true, false>(st, cur, nxt, c, ref, kStep, lane, scale_log2, sh, v_wr, v_rd);
+          f_step<G, true, false>(st, cur, cur, c, ref, kStep, lane, scale_log2, sh, v_wr, v_rd);
           ++n;
         }
       }
-      // the last one to four steps
       for (;;) {
-        if (step(ta, tc)) break;
-        if (step(tb, ta)) break;
-        if (step(tc, tb)) break;
+        if (step2(ta)) break;
+        if (step2(tb)) break;
       }
       if (bad && lane == 0) err[0] = PKD_DEVERR_PAGE_ID;
       __builtin_amdgcn_s_setprio(0);
