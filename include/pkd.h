@@ -193,6 +193,14 @@ int32_t pkd_planned_variant(const pkd_handle* h);
  * engine assert that the plan matches its batch (aicassindra, "What to do
  * next", item 3). */
 int64_t pkd_plan_id(const pkd_handle* h);
+/* The shape the handle's current plan was made for, so a caller can refuse
+ * a run whose buffers do not match it before anything is launched (a stale
+ * plan ranges from wrong output to out-of-bounds accesses: aicassindra,
+ * "Failure modes in production").  Writes 8 ints to shape: requests (rows
+ * of q, o and lse), num_qo_heads, num_kv_heads, head_dim, page_size,
+ * q_dtype, kv_dtype and the plan kind (PKD_PLAN_*).  PKD_ERR_STALE_PLAN
+ * before any plan, PKD_ERR_INVALID_ARG on null pointers. */
+int pkd_plan_shape(const pkd_handle* h, int32_t* shape);
 const char* pkd_last_error(void);
 
 /* ----------------------------- workspaces ----------------------------- */
@@ -305,7 +313,14 @@ int pkd_plan_shared_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
  * workgroups; the shared-prefix kernel for a plan from pkd_plan_shared) and
  * the merge kernel.  `batch` must equal the planned batch
  * and the dtypes the planned ones (else PKD_ERR_STALE_PLAN /
- * PKD_ERR_DTYPE_MISMATCH).  sm_scale <= 0 means 1/sqrt(head_dim).  A page id
+ * PKD_ERR_DTYPE_MISMATCH).  The buffers must have the planned shape, which
+ * this call cannot see through plain pointers and so does not check: q and
+ * o [batch, num_qo_heads, head_dim], lse [batch, num_qo_heads] and the
+ * cache [num_pages, 2, page_size, num_kv_heads, head_dim] with the plan's
+ * num_qo_heads, num_kv_heads, head_dim and page_size (pkd_plan_shape
+ * returns them; the Python binding compares every tensor with them and
+ * raises before calling here).  Any other shape reads and writes past the
+ * buffers.  sm_scale <= 0 means 1/sqrt(head_dim).  A page id
  * outside [0, num_pages) is not read: the kernel uses page 0 instead and
  * raises PKD_DEVERR_PAGE_ID (see pkd_read_device_error). */
 int pkd_run(pkd_handle* h, const void* q, int32_t batch, const void* kv_cache,

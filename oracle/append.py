@@ -69,12 +69,13 @@ def append_quantized(cache_codes, k_new_bits, v_new_bits, batch_indices, positio
 
     The code is a rounding decision, so it is taken in the precision the
     library computes x / scale in: float32, as x times the float32 value of
-    1 / scale."""
+    1 / scale.  The scale itself is the float32 the C interface receives, so
+    it is rounded to float32 first."""
     from . import fp8
     from .attention import bf16_to_f64
 
     def scaled(bits, scale):
-        inv = np.float32(1.0 / float(scale))
+        inv = np.float32(1.0 / float(np.float32(scale)))
         with np.errstate(over="ignore"):  # a product past float32's range is inf, then saturates
             return (bf16_to_f64(bits).astype(np.float32) * inv).astype(np.float64)
 

@@ -12,9 +12,12 @@ raises.
 from ._lib import PkdError, header_functions, load  # noqa: F401
 from .api import (  # noqa: F401
     DecodePlanRun,
+    PlanMismatchError,
     SharedPlanRun,
     append_paged_kv_cache,
     append_positions,
+    check_append_args,
+    check_run_args,
     float_workspace_bytes,
     host_workspace_bytes,
     int_workspace_bytes,

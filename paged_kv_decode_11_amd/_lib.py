@@ -66,6 +66,7 @@ SIGNATURES = {
     "pkd_num_slots": (_i32, [_vp]),
     "pkd_plan_id": (_i64, [_vp]),
     "pkd_planned_variant": (_i32, [_vp]),
+    "pkd_plan_shape": (ctypes.c_int, [_vp, _pi32]),
     "pkd_last_error": (ctypes.c_char_p, []),
     "pkd_int_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "pkd_float_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),

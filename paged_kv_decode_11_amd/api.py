@@ -16,6 +16,79 @@ from ._lib import PkdError, check, pkd_plan_opts  # noqa: F401
 _DTYPES = None
 
 
+class PlanMismatchError(PkdError, ValueError):
+    """A run's tensors do not have the shape the current plan was made for
+    (raised by the binding before anything is launched; status
+    PKD_ERR_STALE_PLAN)."""
+
+    def __init__(self, message: str):
+        super().__init__(_lib.PKD_ERR_STALE_PLAN, message)
+
+
+PLAN_SHAPE_FIELDS = ("batch", "num_qo_heads", "num_kv_heads", "head_dim", "page_size", "q_dtype",
+                     "kv_dtype", "kind")
+
+
+def check_run_args(plan_shape: dict, q, kv_cache, out=None, lse=None) -> None:
+    """Refuse a run whose tensors do not fit the plan (PlanMismatchError).
+
+    Uses only .shape / .dtype, so it runs on CPU or meta tensors too.  The
+    batch (rows of q) is compared with the plan by pkd_run itself; here q
+    must be [rows, num_qo_heads, head_dim], the cache [pages, 2, page_size,
+    num_kv_heads, head_dim], and a given out [rows, num_qo_heads, head_dim]
+    bf16 and lse [rows, num_qo_heads] fp32 (pkd_run writes exactly those
+    extents; any other shape would be read or written past its end)."""
+    import torch
+
+    Hq, Hkv, D, P = (plan_shape[k] for k in ("num_qo_heads", "num_kv_heads", "head_dim",
+                                            "page_size"))
+    if len(q.shape) != 3 or tuple(q.shape[1:]) != (Hq, D):
+        raise PlanMismatchError(f"q has shape {tuple(q.shape)}; the plan needs [batch, {Hq}, {D}]")
+    if len(kv_cache.shape) != 5 or tuple(kv_cache.shape[1:]) != (2, P, Hkv, D):
+        raise PlanMismatchError(f"kv_cache has shape {tuple(kv_cache.shape)}; the plan needs "
+                                f"[num_pages, 2, {P}, {Hkv}, {D}]")
+    if kv_cache.shape[0] < 1:
+        raise PlanMismatchError("kv_cache has no pages")
+    rows = q.shape[0]
+    if out is not None and (tuple(out.shape) != (rows, Hq, D) or out.dtype != torch.bfloat16):
+        raise PlanMismatchError(f"out is {out.dtype} {tuple(out.shape)}; the run writes bf16 "
+                                f"[{rows}, {Hq}, {D}]")
+    if lse is not None and (tuple(lse.shape) != (rows, Hq) or lse.dtype != torch.float32):
+        raise PlanMismatchError(f"lse is {lse.dtype} {tuple(lse.shape)}; the run writes float32 "
+                                f"[{rows}, {Hq}]")
+
+
+def check_append_args(k_new, v_new, batch_indices, positions, kv_cache, kv_indices,
+                      kv_indptr) -> None:
+    """Refuse an append whose tensors do not fit together (ValueError); only
+    .shape / .dtype / .numel() are read.  The kernel writes token t's rows
+    of num_kv_heads x head_dim values into a cache of that row size, reads
+    batch_indices[t] and positions[t] for t < nnz and kv_indptr[b],
+    kv_indptr[b + 1] for b < batch = len(kv_indptr) - 1."""
+    import torch
+
+    if len(k_new.shape) != 3:
+        raise ValueError(f"k_new must be [nnz, num_kv_heads, head_dim], got {tuple(k_new.shape)}")
+    nnz, Hkv, D = k_new.shape
+    if tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError(f"v_new has shape {tuple(v_new.shape)}, k_new {tuple(k_new.shape)}")
+    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise ValueError("k_new and v_new must be bf16")
+    if len(kv_cache.shape) != 5 or kv_cache.shape[1] != 2 or tuple(kv_cache.shape[3:]) != (Hkv, D):
+        raise ValueError(f"kv_cache has shape {tuple(kv_cache.shape)}; rows of [{Hkv}, {D}] need "
+                         f"[num_pages, 2, page_size, {Hkv}, {D}]")
+    if kv_cache.shape[0] < 1 or kv_cache.shape[2] < 1:
+        raise ValueError("kv_cache has no pages")
+    for name, t in (("batch_indices", batch_indices), ("positions", positions)):
+        if len(t.shape) != 1 or t.shape[0] < nnz:
+            raise ValueError(f"{name} must be 1-D with at least nnz = {nnz} entries, got "
+                             f"{tuple(t.shape)}")
+    if len(kv_indptr.shape) != 1 or kv_indptr.shape[0] < 2:
+        raise ValueError("kv_indptr must be 1-D with batch + 1 >= 2 entries")
+    if len(kv_indices.shape) != 1:
+        raise ValueError("kv_indices must be 1-D")
+
+
 def _dtype_code(dtype) -> int:
     import torch
 
@@ -129,7 +202,6 @@ class DecodePlanRun:
         self._host_raw = torch.empty(hb + 256, dtype=torch.uint8, pin_memory=True)
         off = (-self._host_raw.data_ptr()) % 256
         self.host_workspace = self._host_raw[off: off + hb]
-        self._planned = None
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -151,6 +223,17 @@ class DecodePlanRun:
         'mfma_pv'; '' before any plan)."""
         v = int(self._L.pkd_planned_variant(self._h))
         return {code: name for name, code in _lib.VARIANTS.items() if name != "auto"}.get(v, "")
+
+    @property
+    def plan_shape(self):
+        """The shape of the current plan (pkd_plan_shape) as a dict of
+        PLAN_SHAPE_FIELDS, or None before any plan."""
+        v = (ctypes.c_int32 * 8)()
+        rc = self._L.pkd_plan_shape(self._h, v)
+        if rc == _lib.PKD_ERR_STALE_PLAN:
+            return None
+        check(rc)
+        return dict(zip(PLAN_SHAPE_FIELDS, (int(x) for x in v)))
 
     def plan(self, kv_indptr, kv_indices, kv_last_page_len, num_qo_heads: int, num_kv_heads: int,
              head_dim: int, page_size: int, q_data_type=None, kv_data_type=None,
@@ -174,28 +257,27 @@ class DecodePlanRun:
             self.float_workspace.data_ptr(), self.float_workspace.numel(),
             self.host_workspace.data_ptr(), self.host_workspace.numel(), ctypes.byref(o),
             _stream_ptr(stream)))
-        self._planned = (last.shape[0], num_qo_heads, head_dim)
         self._keep = kv_indices  # the copy is queued on the stream; keep the source alive
 
     def run(self, q, kv_cache, out=None, lse=None, return_lse: bool = False, sm_scale=None,
             stream=None, k_scale=None, v_scale=None):
         """Decode for the planned batch; a float8_e4m3fn cache takes per-tensor
-        k_scale / v_scale (pkd_run_scaled when a scale is given)."""
+        k_scale / v_scale (pkd_run_scaled when a scale is given).  Tensors
+        whose shape does not fit the plan raise PlanMismatchError before any
+        launch."""
         import torch
 
-        if self._planned is None:
-            B, Hq, D = q.shape
-        else:
-            B, Hq, D = self._planned
-        if not (q.is_cuda and q.is_contiguous() and kv_cache.is_cuda and kv_cache.is_contiguous()):
-            raise ValueError("q and kv_cache must be contiguous GPU tensors")
-        if q.dim() != 3 or kv_cache.dim() != 5:
-            raise ValueError("q is [batch, Hq, D] and kv_cache [pages, 2, P, Hkv, D]")
+        shape = self.plan_shape
+        if shape is None:
+            raise PkdError(_lib.PKD_ERR_STALE_PLAN, "run before any plan on this handle")
+        check_run_args(shape, q, kv_cache, out, lse)
+        for name, t in (("q", q), ("kv_cache", kv_cache), ("out", out), ("lse", lse)):
+            if t is not None and not (t.is_cuda and t.is_contiguous() and t.device == q.device):
+                raise ValueError(f"{name} must be a contiguous tensor on {q.device}")
         if out is None:
-            out = torch.empty((q.shape[0], q.shape[1], q.shape[2]), dtype=torch.bfloat16,
-                              device=q.device)
+            out = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=q.device)
         if return_lse and lse is None:
-            lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=q.device)
+            lse = torch.empty(tuple(q.shape[:2]), dtype=torch.float32, device=q.device)
         args = (self._h, q.data_ptr(), q.shape[0], kv_cache.data_ptr(), kv_cache.shape[0],
                 _dtype_code(q.dtype), _dtype_code(kv_cache.dtype), out.data_ptr(),
                 lse.data_ptr() if lse is not None else None,
@@ -371,7 +453,6 @@ class SharedPlanRun(DecodePlanRun):
             self.float_workspace.data_ptr(), self.float_workspace.numel(),
             self.host_workspace.data_ptr(), self.host_workspace.numel(), ctypes.byref(o),
             _stream_ptr(stream)))
-        self._planned = (int(qo[-1]), num_qo_heads, head_dim)
         self._keep = kv_indices
 
 
@@ -402,12 +483,11 @@ def append_paged_kv_cache(k_new, v_new, batch_indices, positions, kv_cache, kv_i
     (pkd_append_paged_kv_scaled when a scale is given)."""
     import torch
 
+    check_append_args(k_new, v_new, batch_indices, positions, kv_cache, kv_indices, kv_indptr)
     nnz, Hkv, D = k_new.shape
     for t in (k_new, v_new, kv_cache):
         if not (t.is_cuda and t.is_contiguous()):
             raise ValueError("k_new, v_new and kv_cache must be contiguous GPU tensors")
-    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
-        raise ValueError("k_new and v_new must be bf16")
     for t in (batch_indices, positions, kv_indices, kv_indptr):
         if not (t.is_cuda and t.dtype == torch.int32 and t.is_contiguous()):
             raise ValueError("index arrays must be contiguous int32 GPU tensors")

@@ -15,6 +15,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <exception>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -141,6 +142,18 @@ int check_shapes(int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t q_dtype,
   return PKD_OK;
 }
 
+// plan_build without letting an exception (host memory for the work items
+// of an enormous plan) cross the C ABI.
+int guarded_plan_build(const pkd::PlanInput& in, pkd::PlanScratch& s, int32_t* image,
+                       int64_t image_ints, pkd::PlanLayout* layout, std::string* err) {
+  try {
+    return pkd::plan_build(in, s, image, image_ints, layout, err);
+  } catch (const std::exception& e) {
+    *err = std::string("planning failed on the host: ") + e.what();
+    return PKD_ERR_INVALID_ARG;
+  }
+}
+
 int check_shared_shapes(int32_t Hq, int32_t Hkv, int32_t P) {
   if (!pkd::prefix_variant_built(Hq / Hkv, P))
     return fail(PKD_ERR_UNSUPPORTED,
@@ -210,6 +223,15 @@ int32_t pkd_planned_variant(const pkd_handle* h) { return h && h->planned ? h->v
 
 int64_t pkd_plan_id(const pkd_handle* h) { return h && h->planned ? h->plan_counter : 0; }
 
+int pkd_plan_shape(const pkd_handle* h, int32_t* shape) {
+  if (!h || !shape) return fail(PKD_ERR_INVALID_ARG, "null argument");
+  if (!h->planned) return fail(PKD_ERR_STALE_PLAN, "no plan on this handle");
+  const int32_t v[8] = {h->batch, h->Hq, h->Hkv, h->D, h->P, h->q_dtype, h->kv_dtype,
+                        h->layout.kind};
+  std::memcpy(shape, v, sizeof(v));
+  return PKD_OK;
+}
+
 size_t pkd_int_workspace_bytes(int32_t max_batch, int32_t max_nnz, int32_t num_slots) {
   if (max_batch < 1 || max_nnz < 1 || num_slots < 1) return 0;
   const int64_t I = pkd::max_items(max_batch, num_slots);
@@ -256,7 +278,8 @@ int pkd_plan_host(const int32_t* kv_indptr, const int32_t* kv_last_page_len, int
   pkd::PlanScratch scratch;
   pkd::PlanLayout layout;
   std::string err;
-  int rc = pkd::plan_build(in, scratch, out, int64_t(out_bytes / sizeof(int32_t)), &layout, &err);
+  const int rc = guarded_plan_build(in, scratch, out, int64_t(out_bytes / sizeof(int32_t)),
+                                    &layout, &err);
   if (rc != PKD_OK) return fail(rc, err);
   if (out_ints) *out_ints = layout.off_indices;
   return PKD_OK;
@@ -274,7 +297,8 @@ int pkd_plan_shared_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
   pkd::PlanScratch scratch;
   pkd::PlanLayout layout;
   std::string err;
-  int rc = pkd::plan_build(in, scratch, out, int64_t(out_bytes / sizeof(int32_t)), &layout, &err);
+  const int rc = guarded_plan_build(in, scratch, out, int64_t(out_bytes / sizeof(int32_t)),
+                                    &layout, &err);
   if (rc != PKD_OK) return fail(rc, err);
   if (out_ints) *out_ints = layout.off_indices;
   return PKD_OK;
@@ -338,7 +362,7 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
   in.plan_id = h->plan_counter + 1;
   pkd::PlanLayout layout;
   std::string err;
-  rc = pkd::plan_build(in, h->scratch, image, half_ints, &layout, &err);
+  rc = guarded_plan_build(in, h->scratch, image, half_ints, &layout, &err);
   if (rc == PKD_ERR_WORKSPACE_TOO_SMALL)
     return fail(rc, "host workspace too small for this plan (size it with pkd_host_workspace_bytes)");
   if (rc != PKD_OK) return fail(rc, err);

@@ -21,16 +21,21 @@
 //   each lane's K bytes are 2 x 16 contiguous bytes.
 // * The result leaves lane l with row l & 15 and tokens 4 (l >> 4) + v of
 //   each half: the row maximum is an in-lane max over 8 values and a swap
-//   across the four 16-lane groups; the 8 probabilities of a lane are, in
-//   fp16, exactly the B operand of the P V product, so they never leave the
-//   registers.
-// * O^T += V^T P^T: eight v_mfma_f32_16x16x32_f16 (16 head dims each). V
-//   rows are written to LDS in token order permuted to match P's layout and
-//   read back transposed with ds_read_b64_tr_b8, 8 tokens of one head dim
-//   per lane, then widened to fp16 (exact).  The probabilities are scaled by
-//   2^15 before the fp16 conversion (folded into the exponent), which keeps
-//   them in fp16's normal range down to 2^-29; the scale cancels in o = acc
-//   / l.
+//   across the four 16-lane groups; the 8 probabilities of a lane, as fp16
+//   pairs, are exactly the B operands of the P V products, so they never
+//   leave the registers.
+// * O^T += V^T P^T: sixteen v_mfma_f32_16x16x32_f16 (two per 16 head dims).
+//   V rows are written to LDS in token order permuted to match P's layout
+//   and read back transposed with ds_read_b64_tr_b8, 8 tokens of one head
+//   dim per lane, then widened to fp16 (exact).  Each probability enters as
+//   an fp16 high part plus the fp16 rounding of its remainder (two products
+//   with the same V operand): their sum is p to about 2^-22 relative, where
+//   fp16 alone keeps 2^-11, so the output error does not grow with the
+//   magnitude of V (E4M3 values reach 448 times v_scale).  Every fp16 x fp16
+//   product is exact in the fp32 accumulator.  The probabilities are scaled
+//   by 2^15 before the split (folded into the exponent), which keeps the
+//   high part in fp16's normal range down to 2^-29; the scale cancels in
+//   o = acc / l.
 //
 // K and V of the next two steps stream into registers while the current one
 // is computed (two steps in a ring, each refilled with the step two ahead
@@ -81,11 +86,17 @@ __device__ __forceinline__ uint4 fp8x8_to_f16(uint32_t w0, uint32_t w1) {
       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.f, true)));
 }
 
-__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  f16x2_t v;
-  v.x = (_Float16)lo;
-  v.y = (_Float16)hi;
-  return __builtin_bit_cast(uint32_t, v);
+// Two probabilities as fp16 pairs: `hi` their fp16 roundings, `lo` the
+// fp16 roundings of what those leave over (a - fp16(a) is exact in fp32).
+__device__ __forceinline__ void split_f16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  f16x2_t h;
+  h.x = (_Float16)a;
+  h.y = (_Float16)b;
+  f16x2_t r;
+  r.x = (_Float16)(a - (float)h.x);
+  r.y = (_Float16)(b - (float)h.y);
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, r);
 }
 
 __device__ __forceinline__ floatx4_t mfma_bf16(uint4 a, uint4 b, floatx4_t c) {
@@ -280,8 +291,11 @@ __device__ __forceinline__ void f_step(FState<G>& st, const FStep& cur, FStep& n
     }
   st.lp = fmaf(st.lp, alpha, psum);
   st.m = mn;
-  const uint4 pb = make_uint4(pack_f16x2(p[0][0], p[0][1]), pack_f16x2(p[0][2], p[0][3]),
-                              pack_f16x2(p[1][0], p[1][1]), pack_f16x2(p[1][2], p[1][3]));
+  uint4 pb, pr;
+  split_f16x2(p[0][0], p[0][1], pb.x, pr.x);
+  split_f16x2(p[0][2], p[0][3], pb.y, pr.y);
+  split_f16x2(p[1][0], p[1][1], pb.z, pr.z);
+  split_f16x2(p[1][2], p[1][3], pb.w, pr.w);
 #pragma unroll
   for (int b = 0; b < 8; ++b) st.o[b] *= alpha;
 
@@ -296,7 +310,9 @@ __device__ __forceinline__ void f_step(FState<G>& st, const FStep& cur, FStep& n
   for (int b = 0; b < 8; ++b) {
     const i32x2_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
         (lds_i32x2_t*)((__attribute__((address_space(3))) char*)vr + 16 * b));
-    st.o[b] = mfma_f16(fp8x8_to_f16(uint32_t(w[0]), uint32_t(w[1])), pb, st.o[b]);
+    const uint4 vt = fp8x8_to_f16(uint32_t(w[0]), uint32_t(w[1]));
+    st.o[b] = mfma_f16(vt, pb, st.o[b]);
+    st.o[b] = mfma_f16(vt, pr, st.o[b]);
   }
   __builtin_amdgcn_wave_barrier();
 }

@@ -19,6 +19,7 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <cstdint>
 
 #include "pkd.h"
 #include "plan_layout.h"
@@ -63,7 +64,9 @@ struct SlotHeap {
   // Take the least-loaded slot, add `cost` to it, restore the heap.
   int32_t take(int64_t cost) {
     int32_t s = slot[0];
-    load[0] += cost;
+    // saturate: cost weights near 2^31 on long chunks could otherwise
+    // overflow a slot's sum
+    load[0] = load[0] > INT64_MAX - cost ? INT64_MAX : load[0] + cost;
     sift_down(0);
     return s;
   }
@@ -111,14 +114,19 @@ int plan_validate(const PlanInput& in, std::string* err) {
       return fail(PKD_ERR_UNSUPPORTED, "shared-prefix plans need num_qo_heads / num_kv_heads to divide 128");
     if (in.qo_indptr[0] != 0) return fail(PKD_ERR_INVALID_ARG, "qo_indptr[0] must be 0");
     for (int32_t g = 0; g < in.batch; ++g)
-      if (in.qo_indptr[g + 1] - in.qo_indptr[g] < 1)
+      if (int64_t(in.qo_indptr[g + 1]) - in.qo_indptr[g] < 1)
         return fail(PKD_ERR_INVALID_ARG, "every group needs at least one request (qo_indptr must increase)");
   }
   for (int32_t i = 0; i < in.batch; ++i) {
-    if (in.indptr[i + 1] - in.indptr[i] < 1)
+    // differences in 64 bits: a malformed table may hold any int32 values
+    const int64_t n = int64_t(in.indptr[i + 1]) - in.indptr[i];
+    if (n < 1)
       return fail(PKD_ERR_INVALID_ARG, "every request needs at least one page (kv_indptr must increase)");
     if (in.last[i] < 1 || in.last[i] > in.page_size)
       return fail(PKD_ERR_INVALID_ARG, "kv_last_page_len must lie in [1, page_size]");
+    // chunk and request lengths are 32-bit throughout (plan image, kernels)
+    if (int64_t(in.page_size) * (n - 1) + in.last[i] > INT32_MAX)
+      return fail(PKD_ERR_INVALID_ARG, "a request is longer than 2^31 - 1 tokens");
   }
   return PKD_OK;
 }

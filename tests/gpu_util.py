@@ -80,15 +80,23 @@ def o_tolerance(o_ref: np.ndarray) -> np.ndarray:
     return np.maximum(TOL_O, np.exp2(e - 8) + 1e-3)
 
 
-def check_o(o_got: np.ndarray, o_ref: np.ndarray, label="", extra: float = 0.0):
-    """o against the oracle within o_tolerance, plus `extra` where a test
-    derives a larger bound for its inputs."""
+def check_o(o_got: np.ndarray, o_ref: np.ndarray, label=""):
+    """o against the oracle within o_tolerance.  Elements whose bound is
+    above 1e-2 (|o_ref| >= 4, where a correctly rounded bf16 value may itself
+    be further off) are reported on stderr, so a run shows when the relaxed
+    part of the bound was used."""
     assert np.all(np.isfinite(o_got)), f"{label}: non-finite output"
     err = np.abs(o_got - o_ref)
-    bad = err > o_tolerance(o_ref) + extra
+    tol = o_tolerance(o_ref)
+    bad = err > tol
     assert not bad.any(), (f"{label}: {int(bad.sum())} elements over tolerance; "
                            f"max |o - o_ref| = {err.max()} at |o_ref| = "
                            f"{np.abs(o_ref).ravel()[np.argmax(err)]}")
+    wide = tol > TOL_O
+    if wide.any():
+        say(f"{label}: {int(wide.sum())} of {wide.size} outputs have |o_ref| >= 4 (bound half a "
+            f"bf16 ulp + 1e-3); largest error there {float(err[wide].max()):.3g}, elsewhere "
+            f"{float(err[~wide].max()) if (~wide).any() else 0.0:.3g}")
     return float(err.max())
 
 
@@ -101,10 +109,10 @@ def check_lse(lse_got: np.ndarray, lse_ref: np.ndarray, label=""):
     return err
 
 
-def assert_close(o_dev, lse_dev, o_ref, lse_ref, requests=None, label="", o_extra: float = 0.0):
+def assert_close(o_dev, lse_dev, o_ref, lse_ref, requests=None, label=""):
     o = dev_to_f64(o_dev)
     rows = slice(None) if requests is None else list(requests)
-    err_o = check_o(o[rows], o_ref[rows], label, o_extra)
+    err_o = check_o(o[rows], o_ref[rows], label)
     if lse_dev is not None:
         lse = lse_dev.detach().cpu().numpy().astype(np.float64)
         return err_o, check_lse(lse[rows], lse_ref[rows], label)

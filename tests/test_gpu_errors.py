@@ -164,3 +164,88 @@ def test_pageable_host_workspace_rejected():
         r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, 32, 8, 128, 16)
     assert e.value.code == _lib.PKD_ERR_INVALID_ARG
     assert r.plan_id == 0
+
+
+def test_run_shape_mismatch_refused_before_launch():
+    """q, cache, out or lse whose shape is not the plan's: refused by the
+    binding (PlanMismatchError, status PKD_ERR_STALE_PLAN) before pkd_run,
+    so nothing is read or written past a buffer."""
+    import torch
+    import paged_kv_decode_11_amd as pkd
+
+    batch, q, cache = _inputs()
+    r = pkd.DecodePlanRun(max_batch=4, max_nnz=64, max_qo_heads=64)
+    idx = torch.from_numpy(batch.kv_indices).cuda()
+    r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, 32, 8, 128, 16)
+    assert r.plan_shape == dict(batch=2, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                                page_size=16, q_dtype=_lib.PKD_DTYPE_BF16,
+                                kv_dtype=_lib.PKD_DTYPE_BF16, kind=_lib.PKD_PLAN_DECODE)
+    sentinel = torch.full((2, 32, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    bad_cases = [
+        dict(q=q[:, :16].contiguous()),                                        # fewer heads
+        dict(kv=cache.view(cache.shape[0] // 2, 2, 32, 8, 128)
+             if cache.shape[0] % 2 == 0 else cache[:, :, :8].contiguous()),    # other page size
+        dict(kv=cache.view(cache.shape[0], 2, 16, 4, 256)),                    # other head split
+        dict(out=torch.empty((2, 32, 64), dtype=torch.bfloat16, device="cuda")),
+        dict(lse=torch.empty((2, 16), dtype=torch.float32, device="cuda")),
+    ]
+    for case in bad_cases:
+        with pytest.raises(pkd.PlanMismatchError):
+            r.run(case.get("q", q), case.get("kv", cache), out=case.get("out", sentinel),
+                  lse=case.get("lse"))
+    torch.cuda.synchronize()
+    assert bool((sentinel == 7.0).all())  # nothing ran
+    sr = pkd.SharedPlanRun(2, 4, 64, 32, 8)
+    assert sr.plan_shape is None
+    with pytest.raises(pkd.PkdError) as e:
+        sr.run(q, cache)
+    assert e.value.code == _lib.PKD_ERR_STALE_PLAN
+
+
+@pytest.mark.parametrize("variant,P,kv", [("dot2", 16, "bf16"), ("mfma", 16, "bf16"),
+                                          ("mfma_pv", 16, "bf16"), ("dot2", 4, "bf16"),
+                                          ("mfma", 4, "bf16"), ("mfma_pv", 4, "bf16"),
+                                          ("mfma", 32, "e4m3")])
+@pytest.mark.parametrize("chunk", [0, 1])
+def test_out_of_range_page_id_in_decode(variant, P, kv, chunk):
+    """kv_indices entries outside [0, num_pages) (one past the end, far past
+    it, negative) at an item's first page, in its middle and at its last
+    page: every decode kernel reads page 0 in their place, sets
+    PKD_DEVERR_PAGE_ID, and otherwise computes the oracle's result with page
+    0 substituted."""
+    import torch
+    from oracle import attention as att
+
+    rng = np.random.default_rng(70 + P + chunk)
+    lens = [5 * P + 3, 3 * P, 2, 7 * P + 1]
+    need = sum(-(-l // P) for l in lens)
+    batch = workloads.make_batch(lens, P, need + 4, 32, 8, 128, rng)
+    num_pages = batch.num_pages
+    bad_idx = batch.kv_indices.copy()
+    bad_idx[batch.kv_indptr[0]] = num_pages              # first page of request 0
+    bad_idx[batch.kv_indptr[0] + 2] = -1                 # a middle page
+    bad_idx[batch.kv_indptr[3] + 6] = num_pages + 1000   # request 3's last page
+    bad_idx[batch.kv_indptr[2]] = 1 << 30                # the one-page request
+    sub = np.where((bad_idx < 0) | (bad_idx >= num_pages), 0, bad_idx).astype(np.int32)
+    q = workloads.host_query(batch, rng)
+    gu.say("bad page id", variant, "P", P, kv, "chunk", chunk)
+    r = gu.runner()
+    opts = dict(fixed_chunk_pages=chunk) if chunk else {}
+    if kv == "e4m3":
+        codes = workloads.host_cache_e4m3(batch, rng)
+        r.plan(batch.kv_indptr, torch.from_numpy(bad_idx).cuda(), batch.kv_last_page_len, 32, 8,
+               128, P, kv_data_type=torch.float8_e4m3fn, **opts)
+        o, lse = r.run(gu.bits_to_dev(q), gu.codes_to_dev(codes), return_lse=True,
+                       k_scale=1.0 / 64, v_scale=1.0 / 32)
+        o_ref, lse_ref = att.decode_fp8(q, codes, batch.kv_indptr, sub, batch.kv_last_page_len, 8,
+                                        k_scale=1.0 / 64, v_scale=1.0 / 32)
+    else:
+        cache = workloads.host_cache(batch, rng)
+        r.plan(batch.kv_indptr, torch.from_numpy(bad_idx).cuda(), batch.kv_last_page_len, 32, 8,
+               128, P, variant=variant, **opts)
+        o, lse = r.run(gu.bits_to_dev(q), gu.bits_to_dev(cache), return_lse=True)
+        o_ref, lse_ref = att.decode(q, cache, batch.kv_indptr, sub, batch.kv_last_page_len, 8)
+    torch.cuda.synchronize()
+    assert r.read_device_error() == _lib.PKD_DEVERR_PAGE_ID
+    assert r.read_device_error() == 0  # read clears the flag
+    gu.assert_close(o, lse, o_ref, lse_ref, label=f"bad page id {variant} P{P}")

@@ -73,3 +73,37 @@ def test_quantised_append_equals_append_of_quantised_rows():
     vq = fp8.f64_to_e4m3(att.bf16_to_f64(v) / 2.0)
     assert np.array_equal(out, ap.append(cache, kq, vq, b, pos, indptr, idx))
     assert fp8.e4m3_to_f64(out[idx[1], 0, 3]).tolist() == fp8.e4m3_to_f64(kq[0]).tolist()
+
+
+def test_quantised_append_rounds_the_float32_product():
+    """A non-power-of-two scale where the precision of x / scale decides the
+    code.  x = 91 * 2^-10 (bf16 0x3DB6) and scale 7: the exact quotient is
+    13 * 2^-10 = 6.5 * 2^-9, the midpoint of the E4M3 subnormal codes 0x06
+    (6 * 2^-9) and 0x07 (7 * 2^-9), which ties to the even code 0x06.  The
+    library's contract rounds the float32 product x * fl32(1 / 7) instead:
+    fl32(1 / 7) = 0x3E124925 lies above 1 / 7 and the product rounds to
+    0x3C500001, one float32 ulp above the midpoint, so the stored code is
+    0x07 (0x87 for -x).  An oracle that divided in float64 gives 0x06 here."""
+    assert np.float32(1.0 / 7.0).view(np.uint32) == 0x3E124925
+    assert (np.float32(91 * 2.0 ** -10) * np.float32(1.0 / 7.0)).view(np.uint32) == 0x3C500001
+    indptr, idx, last = pt.page_table([2], 16)
+    cache = np.zeros((1, 2, 16, 1, 2), dtype=np.uint8)
+    x = np.array([[[0x3DB6, 0xBDB6]]], dtype=np.uint16)   # +-91 * 2^-10, one token
+    out = ap.append_quantized(cache, x, x, np.array([0]), np.array([1]), indptr, idx,
+                              k_scale=7.0, v_scale=7.0)
+    assert out[0, 0, 1, 0].tolist() == [0x07, 0x87]
+    assert out[0, 1, 1, 0].tolist() == [0x07, 0x87]
+    # the exact quotient would tie to the even code
+    assert fp8.f64_to_e4m3(np.array([13 * 2.0 ** -10])).tolist() == [0x06]
+    # x = 9 * 2^-10 and scale 0.6, received as fl32(0.6) = 0x3F19999A: the
+    # exact x / fl32(0.6) lies just below the midpoint 7.5 * 2^-9 of codes 0x07
+    # and 0x08, but the float32 product x * fl32(1 / fl32(0.6)) rounds to the
+    # midpoint itself (0x3C700000), which ties to the even code 0x08
+    assert np.float32(0.6).view(np.uint32) == 0x3F19999A
+    inv = np.float32(1.0 / float(np.float32(0.6)))
+    assert (np.float32(9 * 2.0 ** -10) * inv).view(np.uint32) == 0x3C700000
+    y = np.array([[[0x3C10]]], dtype=np.uint16)            # 9 * 2^-10
+    out6 = ap.append_quantized(np.zeros((1, 2, 16, 1, 1), np.uint8), y, y, np.array([0]),
+                               np.array([0]), indptr, idx, k_scale=0.6, v_scale=0.6)
+    assert out6[0, :, 0, 0, 0].tolist() == [0x08, 0x08]
+    assert fp8.f64_to_e4m3(np.array([9 * 2.0 ** -10 / float(np.float32(0.6))])).tolist() == [0x07]
