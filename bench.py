@@ -7,7 +7,11 @@ kernel).  Default workload: the Llama-3-8B-like decode step (32 layers,
 Hq 32 / Hkv 8 / D 128, bf16, page_size 16, batch 64 with KV lengths uniform
 in [3000, 5000], pages scattered through a 32,768-page pool per layer).
 
-Prints one JSON line.  `value` is the achieved KV-stream rate in GB/s
+Prints one JSON line for the main workload; by default the skewed batch (63
+requests of 512 tokens and one of 100,000) is timed after it the same way
+and reported under `targets` beside the main one, each with its fraction of
+the HBM peak and the target fraction for that batch.  `value` is the
+achieved KV-stream rate in GB/s
 (KV bytes the step must read, 4096 B per token per layer, over the measured
 step time; 2048 B with --kv-dtype e4m3).  By default a step is the plan
 call followed by one replay of a
@@ -57,6 +61,12 @@ def parse():
                     help="decode kernel (auto = the library's default for the shape)")
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "e4m3"],
                     help="KV cache element type (e4m3: FP8 codes with per-tensor scales)")
+    ap.add_argument("--targets", default="skewed",
+                    help="comma-separated decode workloads also timed after the main one (graph "
+                         "mode, no oracle), reported under `targets` ('none' skips)")
+    ap.add_argument("--placement", default="scattered", choices=["scattered", "contiguous"],
+                    help="page placement: the workload's random scatter, or the same lengths on "
+                         "pages 0, 1, 2, ... in request order (a control for the page gather)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of this many MiB (5 times), "
                          "to calibrate HBM byte counters against a known size")
@@ -448,21 +458,15 @@ def bench_append(args):
     print(json.dumps(line), flush=True)
 
 
-def main():
-    args = parse()
-    if args.calibrate_copy:
-        calibrate_copy(args.calibrate_copy)
-        return
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU sharding is a design "
-                                   "note only (see the design document)", "n_gpus": args.gpus}))
-        sys.exit(2)
-    if args.workload == "shared_prefix":
-        bench_shared_prefix(args)
-        return
-    if args.workload == "append":
-        bench_append(args)
-        return
+# spec fractions of the HBM peak per workload
+TARGET_FRAC = {"llama8b_step": 0.70, "skewed": 0.60}
+
+
+def bench_decode(args, workload_name: str, cpu_seconds: float, ceilings: bool = True,
+                 placement: str = "scattered") -> dict:
+    """One decode workload: plan per step, runs per layer (graph-replayed by
+    default); returns its JSON line as a dict.  Every tensor it allocates is
+    freed on return."""
     import numpy as np
     import torch
 
@@ -471,10 +475,15 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    spec, rng, b = workloads.workload(args.workload)
+    spec, rng, b = workloads.workload(workload_name)
     batch = b["main"]
+    if placement == "contiguous":
+        # the same lengths on pages 0, 1, 2, ... in request order
+        batch = workloads.make_batch(batch.kv_lens, batch.page_size, batch.num_pages,
+                                     batch.num_qo_heads, batch.num_kv_heads, batch.head_dim,
+                                     None, scatter=False)
     fp8 = args.kv_dtype == "e4m3"
-    if fp8 and (args.variant == "dot2" or args.workload in ("token_sparse", "tiny")):
+    if fp8 and (args.variant == "dot2" or workload_name in ("token_sparse", "tiny")):
         raise SystemExit("an e4m3 cache runs on the matrix-core kernel with page sizes 16-64")
     kv_tok = batch.kv_bytes_per_token() // (2 if fp8 else 1)
     kernel = None  # set from the library's plan below
@@ -483,14 +492,14 @@ def main():
         n_layers, distinct = spec.num_layers, 2
     else:
         n_layers = min(16, max(1, math.ceil(ROTATE_BYTES / layer_bytes)))
-        if args.workload == "wide_gqa":
+        if workload_name == "wide_gqa":
             n_layers = 1  # its ~3.4 GB per layer already dwarfs the last-level cache
         distinct = 1
-    log(f"workload {args.workload}: B={batch.batch} T={batch.total_tokens} nnz={batch.nnz} "
+    log(f"workload {workload_name}: B={batch.batch} T={batch.total_tokens} nnz={batch.nnz} "
         f"pool={batch.num_pages} runs/step={n_layers}")
 
     # caches: `distinct` freshly drawn, the rest device copies (distinct addresses)
-    used_only = args.workload == "wide_gqa"
+    used_only = workload_name == "wide_gqa"
     if fp8:
         fresh = [workloads.device_cache_e4m3(batch, spec.seed * 1000 + j, dev)
                  for j in range(distinct)]
@@ -625,16 +634,20 @@ def main():
     torch.cuda.synchronize()
     cpu = None
     spot = None
-    if args.cpu_seconds > 0:
+    if cpu_seconds > 0:
         log("cpu baseline (oracle) ...")
-        cpu, spot = cpu_baseline(batch, q_bits, caches[0], outs[0], lses[0], args.cpu_seconds,
+        cpu, spot = cpu_baseline(batch, q_bits, caches[0], outs[0], lses[0], cpu_seconds,
                                  (scales["k_scale"], scales["v_scale"]) if fp8 else None)
 
-    ceiling = read_ceilings(caches, batch)
-    ceiling["decode_kernel_frac_of_page_gather"] = round(achieved / ceiling["page_gather_gbs"], 4)
-    log(f"read ceilings: {ceiling}")
+    ceiling = None
+    if ceilings:
+        ceiling = read_ceilings(caches, batch)
+        ceiling["decode_kernel_frac_of_page_gather"] = round(
+            achieved / ceiling["page_gather_gbs"], 4)
+        log(f"read ceilings: {ceiling}")
 
-    traffic = measured_traffic(args.workload, kernel, args.kv_dtype)
+    traffic = measured_traffic(workload_name, kernel, args.kv_dtype) \
+        if placement == "scattered" else None
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -651,12 +664,12 @@ def main():
                  "scales 1/64, seeded lengths and page placement)" if fp8 else
                  "synthetic (seeded N(0,1) bf16 q/K/V, seeded lengths and page placement)"),
         "config": {
-            "workload": args.workload, "batch": batch.batch, "layers": n_layers,
+            "workload": workload_name, "batch": batch.batch, "layers": n_layers,
             "num_qo_heads": batch.num_qo_heads, "num_kv_heads": batch.num_kv_heads,
             "head_dim": batch.head_dim, "page_size": batch.page_size,
             "kv_tokens_per_layer": batch.total_tokens, "pages_per_layer": batch.nnz,
             "pool_pages": batch.num_pages, "slots": r.num_slots, "kv_dtype": args.kv_dtype,
-            "decode_kernel": kernel,
+            "decode_kernel": kernel, "page_placement": placement,
             "parallelism": "single GPU",
         },
         "us_per_layer_step": round(ms_per_step * 1e3 / n_layers, 2),
@@ -678,6 +691,62 @@ def main():
         "cpu_baseline": cpu,
         "parity_spot_check": spot,
     }
+    return line
+
+
+
+
+def target_summary(line: dict) -> dict:
+    """The fields of a secondary workload's line that the headline carries."""
+    w = line["config"]["workload"]
+    frac = line["frac_of_hbm_peak"]
+    out = {"us_per_layer_step": line["us_per_layer_step"], "kv_gbs": line["value"],
+           "frac_of_hbm_peak": frac, "target_frac": TARGET_FRAC.get(w),
+           "meets_target": None if w not in TARGET_FRAC else bool(frac >= TARGET_FRAC[w]),
+           "layers": line["config"]["layers"], "mode": line["mode"],
+           "decode_kernel": line["config"]["decode_kernel"],
+           "kv_tokens_per_layer": line["config"]["kv_tokens_per_layer"],
+           "plan_host_us_median": line["plan_host_us_median"], "roofline": line["roofline"]}
+    if line.get("graph"):
+        out["us_per_layer_step_p10_p50_p90"] = line["graph"]["us_per_layer_step_p10_p50_p90"]
+    return out
+
+
+def main():
+    args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU sharding is a design "
+                                   "note only (see the design document)", "n_gpus": args.gpus}))
+        sys.exit(2)
+    if args.workload == "shared_prefix":
+        bench_shared_prefix(args)
+        return
+    if args.workload == "append":
+        bench_append(args)
+        return
+    import gc
+
+    import torch
+
+    line = bench_decode(args, args.workload, args.cpu_seconds, placement=args.placement)
+    w = args.workload
+    if w in TARGET_FRAC:
+        line["target_frac"] = TARGET_FRAC[w]
+        line["meets_target"] = bool(line["frac_of_hbm_peak"] >= TARGET_FRAC[w])
+    extra = [t for t in args.targets.split(",") if t and t != "none" and t != w]
+    if extra:
+        line["targets"] = {w: target_summary(line)}
+        for t in extra:
+            gc.collect()
+            torch.cuda.empty_cache()
+            log(f"secondary workload {t}")
+            sub = bench_decode(args, t, 0.0, ceilings=False, placement=args.placement)
+            line["targets"][t] = target_summary(sub)
+            log(f"{t}: {line['targets'][t]['us_per_layer_step']} us/layer-step, "
+                f"{line['targets'][t]['frac_of_hbm_peak']} of HBM peak")
     print(json.dumps(line), flush=True)
 
 
