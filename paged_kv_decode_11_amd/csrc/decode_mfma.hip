@@ -10,9 +10,12 @@
 // into the rows of a 16 x 16 logit tile (aicassindra "GQA, tensor cores and
 // MLA": the g queries of a group form a small matrix), S = Q K^T, computed by
 // four v_mfma_f32_16x16x32_bf16 over head_dim 128.  Rows g..15 of Q are zero.
-// Each lane loads its K operand straight from the cache: lane l holds 8
-// elements of token (l & 15)'s row per 32-wide step, 16 bytes, so one load
-// instruction reads 64 contiguous bytes of each of the tile's 16 rows.  The
+// The B operand gives lane l 8 elements of token (l & 15)'s row per 32-wide
+// step.  With pages of 16 tokens or more each lane loads 16-byte pieces of
+// K row-major (whole 256-byte head rows per instruction) and the tile is
+// transposed into operand layout through a per-wave LDS area whose pieces
+// are XOR-rotated by row; smaller pages load the operand layout directly
+// (16 bytes of each of the 16 rows per instruction).  The
 // result leaves lane l with S[4 (l >> 4) + v][l & 15], v = 0..3: the online
 // softmax needs only a 16-lane row maximum per register (DPP) and 8
 // exponentials per tile.  The probabilities and the rescale factors go
