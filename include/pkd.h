@@ -305,6 +305,46 @@ int pkd_plan_shared_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
                          int32_t page_size, int32_t num_slots, const pkd_plan_opts* opts,
                          int32_t* out, size_t out_bytes, int64_t* out_ints);
 
+/* ------------------------ plan without workspaces ----------------------- */
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * pkd_plan_static is pkd_plan with its three workspaces replaced by the
+ * library's own device array of PKD_STATIC_SCRATCH_BYTES, which every GPU
+ * the library runs on holds from the library's load until the process
+ * ends: the plan image and the kv_indices snapshot go to its first
+ * PKD_STATIC_INT_BYTES, the partial states of split requests to the next
+ * PKD_STATIC_FLOAT_BYTES, and the plan image is staged through the last
+ * PKD_STATIC_STAGE_BYTES (copied there from the handle's host memory).
+ * Nothing is allocated on the device; the handle's host staging (2 x
+ * PKD_STATIC_STAGE_BYTES) is allocated on its first static plan and reused.
+ * Runs follow with pkd_run / pkd_run_scaled as after pkd_plan, and a run
+ * captured in a graph replays correctly after later static plans on the
+ * same handle (the regions never move).
+ *
+ * Limits and sharing: a plan whose image, image plus kv_indices or partial
+ * states do not fit their region returns PKD_ERR_WORKSPACE_TOO_SMALL before
+ * anything is queued.  The array is shared by every handle and every call
+ * on one GPU and keeps the last call's contents, so static plans and their
+ * runs on different handles of one GPU must not overlap in time (they would
+ * race on the array); a run whose handle's static plan has since been
+ * replaced by another handle's returns PKD_ERR_STALE_PLAN (checked on the
+ * host at the call, not at graph replay).  A handle's first static plan
+ * clears the device error word.  Not under graph capture
+ * (PKD_ERR_INVALID_ARG).  Other arguments, errors and ordering rules as
+ * pkd_plan; shared-prefix plans need pkd_plan_shared. */
+#define PKD_STATIC_INT_BYTES ((size_t)8 << 20)
+#define PKD_STATIC_FLOAT_BYTES ((size_t)52 << 20)
+#define PKD_STATIC_STAGE_BYTES ((size_t)4 << 20)
+#define PKD_STATIC_SCRATCH_BYTES \
+  (PKD_STATIC_INT_BYTES + PKD_STATIC_FLOAT_BYTES + PKD_STATIC_STAGE_BYTES)
+int pkd_plan_static(pkd_handle* h, const int32_t* kv_indptr, const int32_t* kv_indices,
+                    const int32_t* kv_last_page_len, int32_t batch, int32_t num_qo_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t q_dtype,
+                    int32_t kv_dtype, int32_t kv_layout, const pkd_plan_opts* opts,
+                    pkd_stream_t stream);
+
 /* --------------------------------- run -------------------------------- */
 
 /* Decode attention for the planned batch on one layer's cache: o (and lse

@@ -14,6 +14,7 @@ from .api import (  # noqa: F401
     DecodePlanRun,
     PlanMismatchError,
     SharedPlanRun,
+    StaticPlanRun,
     append_paged_kv_cache,
     append_positions,
     check_append_args,

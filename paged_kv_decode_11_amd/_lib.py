@@ -73,6 +73,8 @@ SIGNATURES = {
     "pkd_host_workspace_bytes": (_sz, [_i32, _i32]),
     "pkd_plan": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                 _vp, _sz, _vp, _sz, _vp, _sz, ctypes.POINTER(pkd_plan_opts), _vp]),
+    "pkd_plan_static": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                       _i32, _i32, ctypes.POINTER(pkd_plan_opts), _vp]),
     "pkd_plan_host": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                      ctypes.POINTER(pkd_plan_opts), _vp, _sz,
                                      ctypes.POINTER(_i64)]),

@@ -377,6 +377,39 @@ def read_pages(base, num_pages: int, page_bytes: int, page_ids, grid: int = 1024
     return sink
 
 
+class StaticPlanRun(DecodePlanRun):
+    """A plan slot that needs no workspaces (pkd_plan_static): the plan and
+    the partial states live in the library's own device array, so neither
+    construction nor planning allocates device memory.  Every StaticPlanRun
+    on one GPU shares that array: their plans and runs must not overlap in
+    time, and a run after another object's static plan raises
+    PKD_ERR_STALE_PLAN."""
+
+    def __init__(self, num_slots: int = 0, device=None):
+        self._create(device, num_slots)
+        self.max_batch = self.max_nnz = None
+
+    def plan(self, kv_indptr, kv_indices, kv_last_page_len, num_qo_heads: int, num_kv_heads: int,
+             head_dim: int, page_size: int, q_data_type=None, kv_data_type=None,
+             kv_layout: str = "NHD", stream=None, **opts):
+        import torch
+
+        q_data_type = torch.bfloat16 if q_data_type is None else q_data_type
+        kv_data_type = torch.bfloat16 if kv_data_type is None else kv_data_type
+        indptr = _host_i32(kv_indptr)
+        last = _host_i32(kv_last_page_len)
+        if not (isinstance(kv_indices, torch.Tensor) and kv_indices.is_cuda
+                and kv_indices.dtype == torch.int32 and kv_indices.is_contiguous()):
+            raise ValueError("kv_indices must be a contiguous int32 tensor on the GPU")
+        layout = {"NHD": _lib.PKD_LAYOUT_NHD, "HND": _lib.PKD_LAYOUT_HND}[kv_layout]
+        o = _opts(**opts)
+        check(self._L.pkd_plan_static(
+            self._h, indptr.ctypes.data, kv_indices.data_ptr(), last.ctypes.data, last.shape[0],
+            num_qo_heads, num_kv_heads, head_dim, page_size, _dtype_code(q_data_type),
+            _dtype_code(kv_data_type), layout, ctypes.byref(o), _stream_ptr(stream)))
+        self._keep = kv_indices
+
+
 def plan_shared_host(qo_indptr, kv_indptr, kv_last_page_len, num_qo_heads, num_kv_heads, head_dim,
                      page_size, num_slots, **opts) -> dict:
     """The schedule pkd_plan_shared would upload (pkd_plan_shared_host),

@@ -54,6 +54,12 @@ struct pkd_handle {
 
   pkd::PlanScratch scratch;
 
+  // pkd_plan_static: the two host halves the plan image is built in before it
+  // is copied to the static array's staging region (allocated on the first
+  // static plan, then reused)
+  std::vector<int32_t> static_host;
+  bool static_plan = false;  // the current plan lives in the static array
+
   // profiling
   bool profile = false;
   std::vector<hipEvent_t> prof_events;  // 3 per run: start, after decode, after merge
@@ -192,6 +198,9 @@ int pkd_create(pkd_handle** out, int32_t device, int32_t num_slots) {
                                : h->cu_count * pkd::decode_blocks_per_cu(h->waves_per_block);
   if (num_slots == 0 && h->num_slots > 2 * h->cu_count) h->num_slots = 2 * h->cu_count;
   h->merge_grid = 4 * h->cu_count;
+  // the address of the library's device scratch on this device (taken once
+  // per device; a failure is reported by pkd_plan_static, the only user)
+  (void)pkd::static_scratch_init(device);
   for (int i = 0; i < 2; ++i) {
     e = hipEventCreateWithFlags(&h->staging_done[i], hipEventDisableTiming);
     if (e != hipSuccess) {
@@ -205,6 +214,7 @@ int pkd_create(pkd_handle** out, int32_t device, int32_t num_slots) {
 
 int pkd_destroy(pkd_handle* h) {
   if (!h) return PKD_OK;
+  pkd::static_scratch_release(h->device, h);
   DeviceGuard guard(h->device);
   for (int i = 0; i < 2; ++i) {
     if (h->staging_done[i]) {
@@ -313,8 +323,28 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
                      void* int_workspace, size_t int_workspace_bytes, void* float_workspace,
                      size_t float_workspace_bytes, void* host_workspace,
                      size_t host_workspace_bytes, const pkd_plan_opts* opts,
-                     pkd_stream_t stream) {
+                     pkd_stream_t stream, bool use_static = false) {
   if (!h) return fail(PKD_ERR_INVALID_ARG, "null handle");
+  if (use_static) {
+    // the library's device array in place of the int and float workspaces,
+    // the handle's host memory in place of the pinned staging
+    char* base = static_cast<char*>(pkd::static_scratch_ptr(h->device));
+    if (!base) {
+      DeviceGuard g(h->device);
+      const hipError_t e = g.ok ? pkd::static_scratch_init(h->device) : g.err;
+      base = static_cast<char*>(pkd::static_scratch_ptr(h->device));
+      if (!base) return hip_fail(e == hipSuccess ? hipErrorInvalidValue : e,
+                                 "address of the static scratch array");
+    }
+    int_workspace = base;
+    int_workspace_bytes = PKD_STATIC_INT_BYTES;
+    float_workspace = base + PKD_STATIC_INT_BYTES;
+    float_workspace_bytes = PKD_STATIC_FLOAT_BYTES;
+    if (h->static_host.empty())
+      h->static_host.assign(2 * PKD_STATIC_STAGE_BYTES / sizeof(int32_t), 0);
+    host_workspace = h->static_host.data();
+    host_workspace_bytes = 2 * size_t(PKD_STATIC_STAGE_BYTES);
+  }
   int rc = check_shapes(num_qo_heads, num_kv_heads, head_dim, page_size, q_dtype, kv_dtype,
                         kv_layout);
   if (rc != PKD_OK) return rc;
@@ -326,7 +356,7 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
     return fail(PKD_ERR_INVALID_ARG, "kv_indices and the three workspaces must be non-null");
   if ((reinterpret_cast<uintptr_t>(int_workspace) & 255) ||
       (reinterpret_cast<uintptr_t>(float_workspace) & 255) ||
-      (reinterpret_cast<uintptr_t>(host_workspace) & 255))
+      (!use_static && (reinterpret_cast<uintptr_t>(host_workspace) & 255)))
     return fail(PKD_ERR_INVALID_ARG, "workspaces must be 256-byte aligned");
 
   const int32_t variant = opts ? opts->variant : PKD_VARIANT_AUTO;
@@ -344,6 +374,13 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
   DeviceGuard guard(h->device);
   if (!guard.ok) return hip_fail(guard.err, "hipSetDevice");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (use_static) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(s, &cs);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone)
+      return fail(PKD_ERR_INVALID_ARG, "pkd_plan_static runs outside graph capture (capture the runs)");
+  }
 
   // Build into the staging half that is not the latest in-flight copy.
   const int half = h->staging_next;
@@ -364,7 +401,9 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
   std::string err;
   rc = guarded_plan_build(in, h->scratch, image, half_ints, &layout, &err);
   if (rc == PKD_ERR_WORKSPACE_TOO_SMALL)
-    return fail(rc, "host workspace too small for this plan (size it with pkd_host_workspace_bytes)");
+    return fail(rc, use_static ? "the plan image exceeds PKD_STATIC_STAGE_BYTES"
+                               : "host workspace too small for this plan (size it with "
+                                 "pkd_host_workspace_bytes)");
   if (rc != PKD_OK) return fail(rc, err);
 
   const size_t need_int = ints_to_bytes(layout.off_indices + layout.nnz);
@@ -384,7 +423,10 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
     if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync");
     h->err_cleared_for = int_workspace;
   }
-  if (h->host_view_for != host_workspace) {
+  if (use_static) {
+    // the image goes from the handle's (pageable) host half to the staging
+    // region at the end of the array; the upload kernel reads it there
+  } else if (h->host_view_for != host_workspace) {
     // the GPU reads the staging area directly, so it must be pinned memory
     void* view = nullptr;
     e = hipHostGetDevicePointer(&view, host_workspace, 0);
@@ -402,7 +444,19 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
   // and 7; a shared-prefix plan keeps row block and head there
   const int64_t item_rows =
       layout.kind == PKD_PLAN_DECODE ? int64_t(h->num_slots) + layout.num_items : 0;
-  e = pkd::launch_plan_upload(h->host_view + half * half_ints + PKD_HEADER_BASE,
+  const int32_t* src = nullptr;
+  if (!use_static) {
+    src = h->host_view + half * half_ints;
+  } else {
+    int32_t* stage = reinterpret_cast<int32_t*>(static_cast<char*>(int_workspace) +
+                                                PKD_STATIC_INT_BYTES + PKD_STATIC_FLOAT_BYTES);
+    e = hipMemcpyAsync(stage + PKD_HEADER_BASE, image + PKD_HEADER_BASE,
+                       ints_to_bytes(layout.off_indices - PKD_HEADER_BASE),
+                       hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "copy of the plan image to the static scratch");
+    src = stage;
+  }
+  e = pkd::launch_plan_upload(src + PKD_HEADER_BASE,
                               dev + PKD_HEADER_BASE, layout.off_indices - PKD_HEADER_BASE,
                               kv_indices, dev + layout.off_indices, layout.nnz,
                               layout.off_first - PKD_HEADER_BASE, item_rows, s);
@@ -414,6 +468,8 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
 
   h->planned = true;
   h->plan_counter += 1;
+  h->static_plan = use_static;
+  if (use_static) pkd::static_scratch_claim(h->device, h);
   h->batch = layout.num_requests;
   h->Hq = num_qo_heads;
   h->Hkv = num_kv_heads;
@@ -476,6 +532,16 @@ int pkd_plan_shared(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_i
                    host_workspace, host_workspace_bytes, opts, stream);
 }
 
+int pkd_plan_static(pkd_handle* h, const int32_t* kv_indptr, const int32_t* kv_indices,
+                    const int32_t* kv_last_page_len, int32_t batch, int32_t num_qo_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t q_dtype,
+                    int32_t kv_dtype, int32_t kv_layout, const pkd_plan_opts* opts,
+                    pkd_stream_t stream) {
+  return plan_impl(h, nullptr, kv_indptr, kv_indices, kv_last_page_len, batch, num_qo_heads,
+                   num_kv_heads, head_dim, page_size, q_dtype, kv_dtype, kv_layout, nullptr, 0,
+                   nullptr, 0, nullptr, 0, opts, stream, true);
+}
+
 int pkd_run(pkd_handle* h, const void* q, int32_t batch, const void* kv_cache, int64_t num_pages,
             int32_t q_dtype, int32_t kv_dtype, void* o, float* lse, float sm_scale,
             pkd_stream_t stream) {
@@ -493,6 +559,10 @@ int pkd_run_scaled(pkd_handle* h, const void* q, int32_t batch, const void* kv_c
                                         std::to_string(h->batch) + " (call pkd_plan for this batch)");
   if (q_dtype != h->q_dtype || kv_dtype != h->kv_dtype)
     return fail(PKD_ERR_DTYPE_MISMATCH, "run dtypes differ from the dtypes the plan was made for");
+  if (h->static_plan && pkd::static_scratch_owner(h->device) != h)
+    return fail(PKD_ERR_STALE_PLAN,
+                "another handle's pkd_plan_static has replaced this handle's plan in the static "
+                "scratch array (plan again)");
   if (!q || !kv_cache || !o) return fail(PKD_ERR_INVALID_ARG, "q, kv_cache and o must be non-null");
   if (num_pages < 1) return fail(PKD_ERR_INVALID_ARG, "num_pages must be >= 1");
   if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(kv_cache) & 15) ||

@@ -107,6 +107,16 @@ hipError_t launch_merge_two_bf16(const uint16_t* o_a, const float* lse_a, const 
                                  const float* lse_b, int64_t rows, uint16_t* o_out,
                                  float* lse_out, hipStream_t stream);
 
+// The library's device scratch array (static_scratch.hip): its address on
+// `device` is taken once, with that device current; until then, and after a
+// failure, static_scratch_ptr returns null.
+hipError_t static_scratch_init(int device);
+void* static_scratch_ptr(int device);
+// The handle whose plan the array on `device` holds (set by pkd_plan_static).
+void static_scratch_claim(int device, const void* owner);
+void static_scratch_release(int device, const void* owner);  // if `owner` holds it
+const void* static_scratch_owner(int device);
+
 // Read-ceiling kernels (read_ceiling.hip): `grid` workgroups of
 // read_ceiling_threads() lanes, one 32-bit XOR per lane into `sink`.
 int read_ceiling_threads();
