@@ -61,6 +61,16 @@ def parse():
                     help="decode kernel (auto = the library's default for the shape)")
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "e4m3"],
                     help="KV cache element type (e4m3: FP8 codes with per-tensor scales)")
+    ap.add_argument("--prefix-chunk-tokens", type=int, default=0,
+                    help="shared_prefix: smallest chunk of the prefix plan in tokens (0 = the "
+                         "library's default)")
+    ap.add_argument("--prefix-slots", type=int, default=-1,
+                    help="shared_prefix: workgroups of the shared-prefix kernel (0 = the "
+                         "library's default, -1 = half the compute units)")
+    ap.add_argument("--suffix-slots", type=int, default=-1,
+                    help="shared_prefix: workgroups of the suffix decode kernel (0 = the "
+                         "library's default, -1 = half the compute units, so the two kernels "
+                         "run side by side)")
     ap.add_argument("--targets", default="skewed",
                     help="comma-separated decode workloads also timed after the main one (graph "
                          "mode, no oracle), reported under `targets` ('none' skips)")
@@ -259,6 +269,17 @@ def time_graph(fn, steps: int, warmup: int, before=None) -> float:
     return ms
 
 
+def plan_chunk_pages(r) -> int:
+    """Chunk size (pages) of the handle's current plan, read back from its
+    int workspace header."""
+    import torch
+
+    import paged_kv_decode_11_amd as pkd
+
+    hdr = r.int_workspace[4 * pkd._lib.HEADER_BASE: 4 * (pkd._lib.HEADER_BASE + 32)].cpu()
+    return int(hdr.view(torch.int32)[pkd._lib.H["CHUNK_PAGES"]])
+
+
 def bench_shared_prefix(args):
     """32 requests over one 8192-token prefix plus their own suffixes, one
     layer, caches rotated over R copies.  Composable: the prefix state of all
@@ -303,59 +324,105 @@ def bench_shared_prefix(args):
         for j in range(R):
             r1.run(qs[j], caches[j], out=outs1[j], lse=lses1[j])
 
-    # composable
-    rp = pkd.SharedPlanRun(4, main.batch, n_prefix_pages, H, main.num_kv_heads, device=0)
-    rs = pkd.DecodePlanRun(max_batch=suffix.batch, max_nnz=suffix.nnz, max_qo_heads=H, device=0)
+    # composable: one shared-prefix plan (all 32 requests over the prefix
+    # pages) and one decode plan (each request's own suffix), both writing
+    # every chunk's state as a partial; pkd_run_composable runs the prefix
+    # kernel, the suffix decode and one merge
+    half = torch.cuda.get_device_properties(dev).multi_processor_count // 2
+    rp = pkd.SharedPlanRun(4, main.batch, n_prefix_pages, H, main.num_kv_heads,
+                           num_slots=half if args.prefix_slots < 0 else args.prefix_slots,
+                           device=0)
+    rs = pkd.DecodePlanRun(max_batch=suffix.batch, max_nnz=suffix.nnz, max_qo_heads=H,
+                           num_slots=half if args.suffix_slots < 0 else args.suffix_slots,
+                           device=0)
     qo = np.array([0, main.batch], np.int32)
     kv_indptr = np.array([0, n_prefix_pages], np.int32)
     idx_pre = torch.from_numpy(prefix.kv_indices[:n_prefix_pages].astype(np.int32)).to(dev)
     idx_suf = torch.from_numpy(suffix.kv_indices.astype(np.int32)).to(dev)
+    outs2 = [torch.empty_like(qs[0]) for _ in range(R)]
+    lses2 = [torch.empty((main.batch, H), dtype=torch.float32, device=dev) for _ in range(R)]
+
+    pre_opts = {"min_chunk_tokens": args.prefix_chunk_tokens} if args.prefix_chunk_tokens else {}
+
+    def plan2():
+        rp.plan(qo, kv_indptr, idx_pre, prefix.kv_last_page_len[:1], H, main.num_kv_heads, 128, 16,
+                all_partials=True, **pre_opts)
+        rs.plan(suffix.kv_indptr, idx_suf, suffix.kv_last_page_len, H, main.num_kv_heads, 128, 16,
+                all_partials=True)
+
+    def run2():
+        for j in range(R):
+            pkd.run_composable(rp, rs, qs[j], caches[j], out=outs2[j], lse=lses2[j])
+
+    # the same states through separate calls (prefix run with its merge,
+    # suffix run with its merge, merge_state): five launches per layer
+    rp5 = pkd.SharedPlanRun(4, main.batch, n_prefix_pages, H, main.num_kv_heads, device=0)
+    rs5 = pkd.DecodePlanRun(max_batch=suffix.batch, max_nnz=suffix.nnz, max_qo_heads=H, device=0)
     op = [torch.empty_like(qs[0]) for _ in range(R)]
     lp = [torch.empty((main.batch, H), dtype=torch.float32, device=dev) for _ in range(R)]
     os_ = [torch.empty_like(qs[0]) for _ in range(R)]
     ls = [torch.empty((main.batch, H), dtype=torch.float32, device=dev) for _ in range(R)]
-    outs2 = [torch.empty_like(qs[0]) for _ in range(R)]
-    lses2 = [torch.empty((main.batch, H), dtype=torch.float32, device=dev) for _ in range(R)]
+    outs5 = [torch.empty_like(qs[0]) for _ in range(R)]
+    lses5 = [torch.empty((main.batch, H), dtype=torch.float32, device=dev) for _ in range(R)]
 
-    def plan2():
-        rp.plan(qo, kv_indptr, idx_pre, prefix.kv_last_page_len[:1], H, main.num_kv_heads, 128, 16)
-        rs.plan(suffix.kv_indptr, idx_suf, suffix.kv_last_page_len, H, main.num_kv_heads, 128, 16)
+    def plan5():
+        rp5.plan(qo, kv_indptr, idx_pre, prefix.kv_last_page_len[:1], H, main.num_kv_heads, 128,
+                 16, **pre_opts)
+        rs5.plan(suffix.kv_indptr, idx_suf, suffix.kv_last_page_len, H, main.num_kv_heads, 128, 16)
 
-    def run2():
+    def run5():
         for j in range(R):
-            rp.run(qs[j], caches[j], out=op[j], lse=lp[j])
-            rs.run(qs[j], caches[j], out=os_[j], lse=ls[j])
-            pkd.merge_state(op[j], lp[j], os_[j], ls[j], out=outs2[j], lse_out=lses2[j])
+            rp5.run(qs[j], caches[j], out=op[j], lse=lp[j])
+            rs5.run(qs[j], caches[j], out=os_[j], lse=ls[j])
+            pkd.merge_state(op[j], lp[j], os_[j], ls[j], out=outs5[j], lse_out=lses5[j])
 
     plan1()
     plan2()
+    plan5()
     run1()
     run2()
+    run5()
     torch.cuda.synchronize()
-    # the two formats agree (both are checked against the oracle by the tests)
+    # the formats agree (each is checked against the oracle by the tests)
     diff = max(float((outs1[j].float() - outs2[j].float()).abs().max()) for j in range(R))
     dlse = max(float((lses1[j] - lses2[j]).abs().max()) for j in range(R))
-    log(f"formats agree: max |o1 - o2| {diff:.3g}, max |lse1 - lse2| {dlse:.3g}")
+    diff5 = max(float((outs5[j].float() - outs2[j].float()).abs().max()) for j in range(R))
+    log(f"formats agree: max |o1 - o2| {diff:.3g}, max |lse1 - lse2| {dlse:.3g}, "
+        f"five-launch vs one-call {diff5:.3g}")
 
-    # per-kernel time of the shared-prefix kernel (eager, HIP events)
+    # per-launch times of the composable layer (eager, HIP events recorded by
+    # the library): prefix handle = prefix kernel; suffix handle = suffix
+    # decode, then the merge
     rp.profile_enable(True)
+    rs.profile_enable(True)
     for _ in range(args.steps):
         plan2()
         run2()
     torch.cuda.synchronize()
-    pre_ms, pre_merge_ms, runs = rp.profile_read()
+    pre_ms, pre_tail_ms, runs = rp.profile_read()
+    suf_ms, suf_tail_ms, sruns = rs.profile_read()
     rp.profile_enable(False)
+    rs.profile_enable(False)
     prefix_us = pre_ms * 1e3 / runs
-    prefix_merge_us = pre_merge_ms * 1e3 / runs
+    # the two kernels run side by side; each handle's second interval runs
+    # from its kernel's end to the merge's end, so the shorter one is the
+    # merge (after whichever kernel ended last)
+    prefix_merge_us = min(pre_tail_ms * 1e3 / runs, suf_tail_ms * 1e3 / sruns)
+    breakdown = {"prefix_kernel": round(prefix_us, 2),
+                 "suffix_decode": round(suf_ms * 1e3 / sruns, 2),
+                 "merge": round(prefix_merge_us, 2),
+                 "prefix_slots": rp.num_slots, "suffix_slots": rs.num_slots}
+    log(f"composable launches (us): {breakdown}")
 
     ms1 = time_graph(run1, args.steps, args.warmup, plan1)
     ms2 = time_graph(run2, args.steps, args.warmup, plan2)
-    us1, us2 = ms1 * 1e3 / R, ms2 * 1e3 / R
+    ms5 = time_graph(run5, args.steps, args.warmup, plan5)
+    us1, us2, us5 = ms1 * 1e3 / R, ms2 * 1e3 / R, ms5 * 1e3 / R
     value = unique_bytes * R / (ms2 / 1e3) / 1e9
     prefix_bytes = prefix_tokens * kv_tok
     achieved = prefix_bytes / (prefix_us / 1e6) / 1e9
-    log(f"single format {us1:.1f} us/layer, composable {us2:.1f} us/layer "
-        f"(prefix kernel {prefix_us:.1f} us + its merge {prefix_merge_us:.1f} us)")
+    log(f"single format {us1:.1f} us/layer, composable {us2:.1f} us/layer (five launches "
+        f"{us5:.1f}; prefix kernel {prefix_us:.1f} us)")
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms2, 4),
@@ -368,6 +435,7 @@ def bench_shared_prefix(args):
         "us_per_layer_step": round(us2, 2),
         "frac_of_hbm_peak": round(value / PEAK_HBM_GBS, 4),
         "composable_us_per_layer": round(us2, 2),
+        "composable_five_launch_us_per_layer": round(us5, 2),
         "single_format_us_per_layer": round(us1, 2),
         "speedup_over_single_format": round(us1 / us2, 2),
         "unique_kv_bytes_per_layer": unique_bytes,
@@ -379,6 +447,9 @@ def bench_shared_prefix(args):
                      "kernel": "prefix_mfma_kernel", "avg_launch_us": round(prefix_us, 2),
                      "algorithmic_bytes_per_launch": prefix_bytes,
                      "merge_avg_launch_us": round(prefix_merge_us, 2)},
+        "composable_launch_us": breakdown,
+        "formats_max_abs_diff_five_launch": diff5,
+        "prefix_chunk_pages": plan_chunk_pages(rp),
         "formats_max_abs_diff": {"o": diff, "lse": dlse},
         "cpu_baseline": None,
     }

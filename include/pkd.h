@@ -83,7 +83,15 @@ typedef struct pkd_plan_opts {
   int32_t alpha;             /* cost = alpha * l_q + beta * chunk_len, l_q = 1; */
   int32_t beta;              /*   alpha < 0 or beta <= 0: 1 */
   int32_t variant;           /* decode kernel for runs of this plan: PKD_VARIANT_* */
+  int32_t flags;             /* PKD_PLAN_* flags below (0: none) */
 } pkd_plan_opts;
+
+/* Plan flags.  PKD_PLAN_ALL_PARTIALS: every request (every group of a
+ * shared-prefix plan) writes its chunks' states as partial states, even a
+ * request of one chunk, and the merge list names every request, in request
+ * order, so entry r is request row r; pkd_run_composable needs both its
+ * plans made this way. */
+enum { PKD_PLAN_ALL_PARTIALS = 1 };
 
 /* Decode kernels.  Both compute the same result (to rounding); they differ
  * in where q.k is evaluated. */
@@ -168,6 +176,7 @@ enum {
   PKD_H_ROWS_PER_BLOCK, /* shared-prefix plans: requests per workgroup (128 / gqa) */
   PKD_H_MIN_CHUNKS,     /* fewest partial states of a merge-list entry (0 if none) */
   PKD_H_MAX_CHUNKS,     /* most partial states of a merge-list entry (0 if none) */
+  PKD_H_FLAGS,          /* the plan's PKD_PLAN_* flags */
   PKD_H_COUNT
 };
 #define PKD_HEADER_BASE 32
@@ -379,6 +388,31 @@ int pkd_run(pkd_handle* h, const void* q, int32_t batch, const void* kv_cache,
 int pkd_run_scaled(pkd_handle* h, const void* q, int32_t batch, const void* kv_cache,
                    int64_t num_pages, int32_t q_dtype, int32_t kv_dtype, void* o, float* lse,
                    float sm_scale, float k_scale, float v_scale, pkd_stream_t stream);
+
+/* The composable format in one call (pinghaoyang page, section "Composable
+ * Format：共享前缀与独有后缀分开算": a shared prefix and each request's own
+ * suffix are computed apart and their states merged exactly).  `prefix`
+ * holds a shared-prefix plan (pkd_plan_shared) over the groups' prefix
+ * pages and `suffix` a decode plan (pkd_plan) over each request's own pages,
+ * both made with PKD_PLAN_ALL_PARTIALS, for the same `batch` requests, head
+ * configuration, page size and dtypes (else PKD_ERR_INVALID_ARG,
+ * PKD_ERR_STALE_PLAN or PKD_ERR_DTYPE_MISMATCH, before any launch).  Launches
+ * three kernels with fixed grids: the shared-prefix kernel on the prefix
+ * plan and the decode kernel on the suffix plan, both writing every chunk's
+ * state to their own float workspace, then one merge that combines, for
+ * every request and query head, the prefix chunks' states and then the
+ * suffix chunks' states into o (bf16 [batch, num_qo_heads, head_dim]) and
+ * lse (fp32 [batch, num_qo_heads], may be NULL).  When the two handles' slot
+ * counts together fit the compute units (one workgroup each, e.g. half of
+ * them each), the decode kernel runs beside the prefix kernel on a stream
+ * the suffix handle keeps for this (made on its first such run, forked from
+ * `stream` and joined back before the merge); otherwise the three run on
+ * `stream` in turn.  A run captured in a graph replays correctly after
+ * re-plans of either handle on the same workspaces.  Device errors are
+ * raised on each handle's own flag. */
+int pkd_run_composable(pkd_handle* prefix, pkd_handle* suffix, const void* q, int32_t batch,
+                       const void* kv_cache, int64_t num_pages, int32_t q_dtype, int32_t kv_dtype,
+                       void* o, float* lse, float sm_scale, pkd_stream_t stream);
 
 /* Waits for `stream`, returns the device error flags raised by runs since
  * the last read (PKD_DEVERR_*, 0 if none) and clears them. */

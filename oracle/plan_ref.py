@@ -26,10 +26,17 @@ Readings where the pages leave a step open (also in the design notes):
 * ties: items are ordered by (-cost, request, chunk); an item goes to the
   least-loaded slot, the lowest slot id among equals;
 * split request i gets partial ids base_i .. base_i + k_i - 1, with base_i
-  the number of chunks of the split requests before it.
+  the number of chunks of the split requests before it;
+* with ``all_partials`` every request counts as split (a request of one
+  chunk gets one partial id and a merge-list entry), so that its state can be
+  merged with states from another plan; the merge list then names every
+  request in order.
 
-Two independent implementations are given (a heap and a plain scan over the
-slots); the tests require them to agree.
+The least-loaded-slot choice is written twice, as a binary heap (``plan``)
+and as a plain scan over the slots (``plan_naive``), and the tests require
+the two to agree; both share the chunking, the item order (``_prepare``) and
+the output assembly, which are pinned on their own by hand-worked schedules
+and by invariants (every page once, in order; lengths summing to T).
 """
 
 from __future__ import annotations
@@ -54,7 +61,8 @@ def chunk_pages(total_tokens: int, page_size: int, num_slots: int,
     return max(1, _ceil_div(int(min_chunk_tokens), page_size), _ceil_div(bound, page_size))
 
 
-def work_items(kv_indptr, kv_last_page_len, page_size: int, cp: int, alpha: int, beta: int):
+def work_items(kv_indptr, kv_last_page_len, page_size: int, cp: int, alpha: int, beta: int,
+               all_partials: bool = False):
     """Chunks of every request, in request/chunk order, and the split map.
 
     Each item is a dict with request, chunk, page_begin, num_pages, last_len,
@@ -66,7 +74,7 @@ def work_items(kv_indptr, kv_last_page_len, page_size: int, cp: int, alpha: int,
     for i in range(len(last)):
         n = indptr[i + 1] - indptr[i]
         k = _ceil_div(n, cp)
-        split = k > 1
+        split = k > 1 or all_partials
         base = next_partial
         if split:
             merges.append((i, base, k))
@@ -104,14 +112,14 @@ def _assemble(assignments, num_slots, items_in_order, merges, n_partials, header
 
 
 def _prepare(kv_indptr, kv_last_page_len, page_size, num_slots, fixed_chunk_pages,
-             min_chunk_tokens, alpha, beta):
+             min_chunk_tokens, alpha, beta, all_partials=False):
     indptr = np.asarray(kv_indptr, dtype=np.int64)
     last = np.asarray(kv_last_page_len, dtype=np.int64)
     n = indptr[1:] - indptr[:-1]
     lengths = page_size * (n - 1) + last
     total = int(lengths.sum())
     cp = chunk_pages(total, page_size, num_slots, fixed_chunk_pages, min_chunk_tokens)
-    items, merges, n_partials = work_items(indptr, last, page_size, cp, alpha, beta)
+    items, merges, n_partials = work_items(indptr, last, page_size, cp, alpha, beta, all_partials)
     order = sorted(items, key=lambda it: (-it["cost"], it["request"], it["chunk"]))
     header = dict(batch=int(last.shape[0]), page_size=int(page_size), num_slots=int(num_slots),
                   chunk_pages=cp, total_tokens=total, alpha=alpha, beta=beta)
@@ -120,11 +128,11 @@ def _prepare(kv_indptr, kv_last_page_len, page_size, num_slots, fixed_chunk_page
 
 def plan(kv_indptr, kv_last_page_len, page_size: int, num_slots: int,
          fixed_chunk_pages: int = 0, min_chunk_tokens: int = DEFAULT_MIN_CHUNK_TOKENS,
-         alpha: int = 1, beta: int = 1):
+         alpha: int = 1, beta: int = 1, all_partials: bool = False):
     """The schedule, with a binary heap keyed (load, slot)."""
     items, order, merges, n_partials, header = _prepare(
         kv_indptr, kv_last_page_len, page_size, num_slots, fixed_chunk_pages,
-        min_chunk_tokens, alpha, beta)
+        min_chunk_tokens, alpha, beta, all_partials)
     heap = [(0, s) for s in range(num_slots)]
     assignments = []
     for it in order:
@@ -136,11 +144,11 @@ def plan(kv_indptr, kv_last_page_len, page_size: int, num_slots: int,
 
 def plan_naive(kv_indptr, kv_last_page_len, page_size: int, num_slots: int,
                fixed_chunk_pages: int = 0, min_chunk_tokens: int = DEFAULT_MIN_CHUNK_TOKENS,
-               alpha: int = 1, beta: int = 1):
+               alpha: int = 1, beta: int = 1, all_partials: bool = False):
     """The same schedule with a linear scan for the least-loaded slot."""
     items, order, merges, n_partials, header = _prepare(
         kv_indptr, kv_last_page_len, page_size, num_slots, fixed_chunk_pages,
-        min_chunk_tokens, alpha, beta)
+        min_chunk_tokens, alpha, beta, all_partials)
     loads = [0] * num_slots
     assignments = []
     for it in order:
@@ -182,7 +190,8 @@ def plan_naive(kv_indptr, kv_last_page_len, page_size: int, num_slots: int,
 #   within the group) the partial ids base_g + r k_g + j, j = 0..k_g-1, with
 #   base_g the partial count of the split groups before it; the merge list
 #   has one entry (request, base_g + r k_g, k_g) per request of every split
-#   group, in request order.
+#   group, in request order;
+# * with ``all_partials`` every group counts as split, as in ``plan``.
 
 SHARED_ROWS_PER_WORKGROUP = 128
 
@@ -190,7 +199,7 @@ SHARED_ROWS_PER_WORKGROUP = 128
 def plan_shared(qo_indptr, kv_indptr, kv_last_page_len, page_size: int, num_slots: int,
                 gqa: int, num_kv_heads: int, fixed_chunk_pages: int = 0,
                 min_chunk_tokens: int = DEFAULT_MIN_CHUNK_TOKENS, alpha: int = 1,
-                beta: int = 1):
+                beta: int = 1, all_partials: bool = False):
     """Schedule of a shared-prefix plan (heap LPT, as ``plan``)."""
     qo = [int(x) for x in qo_indptr]
     indptr = [int(x) for x in kv_indptr]
@@ -208,7 +217,7 @@ def plan_shared(qo_indptr, kv_indptr, kv_last_page_len, page_size: int, num_slot
     next_partial = 0
     for g in range(G):
         k = _ceil_div(npages[g], cp)
-        split = k > 1
+        split = k > 1 or all_partials
         base = next_partial if split else -1
         if split:
             for r in range(rows[g]):

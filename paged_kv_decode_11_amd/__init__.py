@@ -28,4 +28,5 @@ from .api import (  # noqa: F401
     plan_shared_host,
     read_pages,
     read_stream,
+    run_composable,
 )

@@ -33,11 +33,12 @@ VARIANTS = {"auto": PKD_VARIANT_AUTO, "dot2": PKD_VARIANT_DOT2, "mfma": PKD_VARI
 
 HEADER_BASE = 32
 PKD_PLAN_DECODE, PKD_PLAN_SHARED = 0, 1
+PKD_PLAN_ALL_PARTIALS = 1
 H_FIELDS = ["MAGIC", "VERSION", "BATCH", "QO_HEADS", "KV_HEADS", "HEAD_DIM", "PAGE_SIZE",
             "SLOTS", "CHUNK_PAGES", "ITEMS", "PARTIALS", "SPLIT", "ALPHA", "BETA", "NNZ",
             "PLAN_ID", "OFF_SLOTS", "OFF_ITEMS", "OFF_MERGE", "OFF_INDICES",
             "TOTAL_TOKENS_LO", "TOTAL_TOKENS_HI", "OFF_FIRST", "KIND", "NUM_GROUPS",
-            "OFF_GROUPS", "ROWS_PER_BLOCK", "MIN_CHUNKS", "MAX_CHUNKS"]
+            "OFF_GROUPS", "ROWS_PER_BLOCK", "MIN_CHUNKS", "MAX_CHUNKS", "FLAGS"]
 H = {name: i for i, name in enumerate(H_FIELDS)}
 
 _STATUS_NAMES = {0: "PKD_OK", 1: "PKD_ERR_INVALID_ARG", 2: "PKD_ERR_UNSUPPORTED",
@@ -53,7 +54,8 @@ class PkdError(RuntimeError):
 
 class pkd_plan_opts(ctypes.Structure):
     _fields_ = [("fixed_chunk_pages", ctypes.c_int32), ("min_chunk_tokens", ctypes.c_int32),
-                ("alpha", ctypes.c_int32), ("beta", ctypes.c_int32), ("variant", ctypes.c_int32)]
+                ("alpha", ctypes.c_int32), ("beta", ctypes.c_int32), ("variant", ctypes.c_int32),
+                ("flags", ctypes.c_int32)]
 
 
 _i32, _i64, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
@@ -97,6 +99,8 @@ SIGNATURES = {
                                _vp]),
     "pkd_run_scaled": (ctypes.c_int, [_vp, _vp, _i32, _vp, _i64, _i32, _i32, _vp, _vp,
                                       ctypes.c_float, ctypes.c_float, ctypes.c_float, _vp]),
+    "pkd_run_composable": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _vp, _vp,
+                                          ctypes.c_float, _vp]),
     "pkd_read_device_error": (ctypes.c_int, [_vp, _pi32, _vp]),
     "pkd_merge_state": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "pkd_merge_states": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),

@@ -103,9 +103,12 @@ def _dtype_code(dtype) -> int:
     return _DTYPES[dtype]
 
 
-def _opts(fixed_chunk_pages=0, min_chunk_tokens=0, alpha=-1, beta=0, variant="auto"):
+def _opts(fixed_chunk_pages=0, min_chunk_tokens=0, alpha=-1, beta=0, variant="auto",
+          all_partials=False):
     v = _lib.VARIANTS[variant] if isinstance(variant, str) else int(variant)
-    return pkd_plan_opts(int(fixed_chunk_pages), int(min_chunk_tokens), int(alpha), int(beta), v)
+    flags = _lib.PKD_PLAN_ALL_PARTIALS if all_partials else 0
+    return pkd_plan_opts(int(fixed_chunk_pages), int(min_chunk_tokens), int(alpha), int(beta), v,
+                         flags)
 
 
 def _host_i32(x) -> np.ndarray:
@@ -408,6 +411,36 @@ class StaticPlanRun(DecodePlanRun):
             num_qo_heads, num_kv_heads, head_dim, page_size, _dtype_code(q_data_type),
             _dtype_code(kv_data_type), layout, ctypes.byref(o), _stream_ptr(stream)))
         self._keep = kv_indices
+
+
+def run_composable(prefix, suffix, q, kv_cache, out=None, lse=None, return_lse: bool = False,
+                   sm_scale=None, stream=None):
+    """The composable format in one call (pkd_run_composable): ``prefix`` a
+    SharedPlanRun and ``suffix`` a DecodePlanRun, both planned with
+    ``all_partials=True`` for the same requests; returns o (and lse) of every
+    request over its group's prefix and its own pages."""
+    import torch
+
+    shapes = []
+    for r in (prefix, suffix):
+        shape = r.plan_shape
+        if shape is None:
+            raise PkdError(_lib.PKD_ERR_STALE_PLAN, "run_composable before both plans")
+        check_run_args(shape, q, kv_cache, out, lse)
+        shapes.append(shape)
+    for name, t in (("q", q), ("kv_cache", kv_cache), ("out", out), ("lse", lse)):
+        if t is not None and not (t.is_cuda and t.is_contiguous() and t.device == q.device):
+            raise ValueError(f"{name} must be a contiguous tensor on {q.device}")
+    if out is None:
+        out = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty(tuple(q.shape[:2]), dtype=torch.float32, device=q.device)
+    check(_lib.load().pkd_run_composable(
+        prefix._h, suffix._h, q.data_ptr(), q.shape[0], kv_cache.data_ptr(), kv_cache.shape[0],
+        _dtype_code(q.dtype), _dtype_code(kv_cache.dtype), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None,
+        float(sm_scale) if sm_scale is not None else 0.0, _stream_ptr(stream)))
+    return (out, lse) if (return_lse or lse is not None) else out
 
 
 def plan_shared_host(qo_indptr, kv_indptr, kv_last_page_len, num_qo_heads, num_kv_heads, head_dim,

@@ -59,6 +59,13 @@ struct pkd_handle {
   // static plan, then reused)
   std::vector<int32_t> static_host;
   bool static_plan = false;  // the current plan lives in the static array
+  int32_t plan_flags = 0;    // PKD_PLAN_* flags of the current plan
+
+  // pkd_run_composable, as the suffix handle: the stream its decode kernel
+  // runs on beside the prefix kernel, and the events of that fork and join
+  // (made on the first such run)
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
 
   // profiling
   bool profile = false;
@@ -123,6 +130,7 @@ pkd::PlanInput make_input(const int32_t* indptr, const int32_t* last, int32_t ba
     in.min_chunk_tokens = opts->min_chunk_tokens;
     in.alpha = opts->alpha;
     in.beta = opts->beta;
+    in.flags = opts->flags;
   }
   return in;
 }
@@ -158,6 +166,30 @@ int guarded_plan_build(const pkd::PlanInput& in, pkd::PlanScratch& s, int32_t* i
     *err = std::string("planning failed on the host: ") + e.what();
     return PKD_ERR_INVALID_ARG;
   }
+}
+
+// Three profiling events for one run of `h` (start, after the decode
+// kernel, after the merge) when its profiling is on and `s` is not being
+// captured; *ev stays null otherwise.
+hipError_t profile_events(pkd_handle* h, hipStream_t s, hipEvent_t** ev) {
+  *ev = nullptr;
+  if (!h->profile) return hipSuccess;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+    return hipSuccess;
+  if (h->prof_used + 3 > h->prof_events.size()) {
+    for (int i = 0; i < 3; ++i) {
+      hipEvent_t x;
+      // device-scope release only: a system-scope fence per record would
+      // stretch the gaps between the timed kernels
+      hipError_t e = hipEventCreateWithFlags(&x, hipEventDisableSystemFence);
+      if (e != hipSuccess) return e;
+      h->prof_events.push_back(x);
+    }
+  }
+  *ev = &h->prof_events[h->prof_used];
+  h->prof_used += 3;
+  return hipSuccess;
 }
 
 int check_shared_shapes(int32_t Hq, int32_t Hkv, int32_t P) {
@@ -223,6 +255,12 @@ int pkd_destroy(pkd_handle* h) {
     }
   }
   for (hipEvent_t ev : h->prof_events) (void)hipEventDestroy(ev);
+  if (h->side) {
+    (void)hipStreamSynchronize(h->side);
+    (void)hipStreamDestroy(h->side);
+  }
+  if (h->fork) (void)hipEventDestroy(h->fork);
+  if (h->join) (void)hipEventDestroy(h->join);
   delete h;
   return PKD_OK;
 }
@@ -469,6 +507,7 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
   h->planned = true;
   h->plan_counter += 1;
   h->static_plan = use_static;
+  h->plan_flags = in.flags;
   if (use_static) pkd::static_scratch_claim(h->device, h);
   h->batch = layout.num_requests;
   h->Hq = num_qo_heads;
@@ -604,26 +643,10 @@ int pkd_run_scaled(pkd_handle* h, const void* q, int32_t batch, const void* kv_c
   mp.o_out = static_cast<uint16_t*>(o);
   mp.lse_out = lse;
 
-  bool prof = false;
   hipEvent_t* ev = nullptr;
-  if (h->profile) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone) {
-      if (h->prof_used + 3 > h->prof_events.size()) {
-        for (int i = 0; i < 3; ++i) {
-          hipEvent_t x;
-          // device-scope release only: a system-scope fence per record
-          // would stretch the gaps between the timed kernels
-          hipError_t e = hipEventCreateWithFlags(&x, hipEventDisableSystemFence);
-          if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
-          h->prof_events.push_back(x);
-        }
-      }
-      ev = &h->prof_events[h->prof_used];
-      h->prof_used += 3;
-      prof = true;
-    }
-  }
+  hipError_t pe = profile_events(h, s, &ev);
+  if (pe != hipSuccess) return hip_fail(pe, "hipEventCreate");
+  const bool prof = ev != nullptr;
 
   hipError_t e;
   if (prof && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -642,6 +665,117 @@ int pkd_run_scaled(pkd_handle* h, const void* q, int32_t batch, const void* kv_c
   e = pkd::launch_merge_partials(mp, h->merge_grid, s);
   if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
   if (prof && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return PKD_OK;
+}
+
+int pkd_run_composable(pkd_handle* prefix, pkd_handle* suffix, const void* q, int32_t batch,
+                       const void* kv_cache, int64_t num_pages, int32_t q_dtype, int32_t kv_dtype,
+                       void* o, float* lse, float sm_scale, pkd_stream_t stream) {
+  if (!prefix || !suffix || prefix == suffix)
+    return fail(PKD_ERR_INVALID_ARG, "two distinct handles are needed (prefix plan, suffix plan)");
+  if (!prefix->planned || !suffix->planned)
+    return fail(PKD_ERR_STALE_PLAN, "pkd_run_composable before both plans");
+  if (prefix->layout.kind != PKD_PLAN_SHARED || suffix->layout.kind != PKD_PLAN_DECODE)
+    return fail(PKD_ERR_INVALID_ARG,
+                "the first handle needs a shared-prefix plan, the second a decode plan");
+  if (!(prefix->plan_flags & PKD_PLAN_ALL_PARTIALS) || !(suffix->plan_flags & PKD_PLAN_ALL_PARTIALS))
+    return fail(PKD_ERR_INVALID_ARG, "both plans must be made with PKD_PLAN_ALL_PARTIALS");
+  if (batch != prefix->batch || batch != suffix->batch)
+    return fail(PKD_ERR_STALE_PLAN, "batch differs from the plans' batch (plan both for this batch)");
+  if (prefix->Hq != suffix->Hq || prefix->Hkv != suffix->Hkv || prefix->D != suffix->D ||
+      prefix->P != suffix->P)
+    return fail(PKD_ERR_INVALID_ARG, "the two plans differ in heads, head_dim or page size");
+  if (q_dtype != prefix->q_dtype || kv_dtype != prefix->kv_dtype || q_dtype != suffix->q_dtype ||
+      kv_dtype != suffix->kv_dtype)
+    return fail(PKD_ERR_DTYPE_MISMATCH, "run dtypes differ from the dtypes the plans were made for");
+  if (prefix->device != suffix->device)
+    return fail(PKD_ERR_INVALID_ARG, "the two handles are on different devices");
+  for (pkd_handle* h : {prefix, suffix})
+    if (h->static_plan && pkd::static_scratch_owner(h->device) != h)
+      return fail(PKD_ERR_STALE_PLAN,
+                  "another handle's pkd_plan_static has replaced a plan in the static scratch array");
+  if (prefix->static_plan && suffix->static_plan)
+    return fail(PKD_ERR_INVALID_ARG, "the two plans cannot both live in the static scratch array");
+  if (!q || !kv_cache || !o) return fail(PKD_ERR_INVALID_ARG, "q, kv_cache and o must be non-null");
+  if (num_pages < 1) return fail(PKD_ERR_INVALID_ARG, "num_pages must be >= 1");
+  if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(kv_cache) & 15) ||
+      (reinterpret_cast<uintptr_t>(o) & 15))
+    return fail(PKD_ERR_INVALID_ARG, "q, kv_cache and o must be 16-byte aligned");
+  if (!(std::isfinite(sm_scale))) return fail(PKD_ERR_INVALID_ARG, "sm_scale must be finite");
+
+  DeviceGuard guard(prefix->device);
+  if (!guard.ok) return hip_fail(guard.err, "hipSetDevice");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float scale = sm_scale > 0.f ? sm_scale : 1.f / std::sqrt(float(prefix->D));
+  auto params = [&](pkd_handle* h) {
+    pkd::DecodeParams dp;
+    dp.q = static_cast<const uint16_t*>(q);
+    dp.kv = static_cast<const uint16_t*>(kv_cache);
+    dp.o = static_cast<uint16_t*>(o);  // not written: every item writes a partial state
+    dp.lse = lse;
+    dp.ws = static_cast<const int32_t*>(h->int_ws);
+    dp.fws = static_cast<float*>(h->float_ws);
+    dp.err = static_cast<int32_t*>(h->int_ws);
+    dp.num_pages = num_pages;
+    dp.scale_log2 = scale * 1.44269504088896341f;
+    dp.out_scale = 1.f;
+    dp.num_qo_heads = h->Hq;
+    dp.num_kv_heads = h->Hkv;
+    return dp;
+  };
+  // When the two grids fit the chip side by side (one workgroup per compute
+  // unit each), the suffix decode runs on the suffix handle's side stream,
+  // forked from `s` and joined back before the merge, beside the prefix
+  // kernel; otherwise each kernel would only slow the other (measured), and
+  // they run one after the other on `s`.
+  const bool side_by_side = prefix->num_slots + suffix->num_slots <= prefix->cu_count;
+  hipError_t e = hipSuccess;
+  if (side_by_side && !suffix->side) {
+    e = hipStreamCreateWithFlags(&suffix->side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&suffix->fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&suffix->join, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "side stream for the suffix decode");
+  }
+  hipStream_t side = side_by_side ? suffix->side : s;
+  // prefix handle: start, after its kernel, after the merge; suffix handle:
+  // start and end of its kernel (side stream), after the merge
+  hipEvent_t *ep = nullptr, *es = nullptr;
+  e = profile_events(prefix, s, &ep);
+  if (e == hipSuccess) e = profile_events(suffix, s, &es);
+  if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  if (side_by_side && ((e = hipEventRecord(suffix->fork, s)) != hipSuccess ||
+                       (e = hipStreamWaitEvent(side, suffix->fork, 0)) != hipSuccess))
+    return hip_fail(e, "fork to the side stream");
+  if (es && (e = hipEventRecord(es[0], side)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  const pkd::DecodeParams ds = params(suffix);
+  const int g = suffix->Hq / suffix->Hkv;
+  if (suffix->kv_dtype == PKD_DTYPE_FP8_E4M3)
+    e = pkd::launch_decode_fp8(ds, g, suffix->P, suffix->num_slots, side);
+  else if (suffix->variant == PKD_VARIANT_MFMA_PV)
+    e = pkd::launch_decode_pv(ds, g, suffix->P, suffix->num_slots, side);
+  else if (suffix->variant == PKD_VARIANT_DOT2)
+    e = pkd::launch_decode(ds, g, suffix->P, suffix->num_slots, side);
+  else
+    e = pkd::launch_decode_mfma(ds, g, suffix->P, suffix->num_slots, side);
+  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+  if (es && (e = hipEventRecord(es[1], side)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (side_by_side && (e = hipEventRecord(suffix->join, side)) != hipSuccess)
+    return hip_fail(e, "join from the side stream");
+  if (ep && (e = hipEventRecord(ep[0], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = pkd::launch_prefix_mfma(params(prefix), prefix->Hq / prefix->Hkv, prefix->P,
+                              prefix->num_slots, s);
+  if (e != hipSuccess) return hip_fail(e, "shared-prefix kernel launch");
+  if (ep && (e = hipEventRecord(ep[1], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (side_by_side && (e = hipStreamWaitEvent(s, suffix->join, 0)) != hipSuccess)
+    return hip_fail(e, "join from the side stream");
+  e = pkd::launch_merge_composable(static_cast<const int32_t*>(prefix->int_ws),
+                                   static_cast<const float*>(prefix->float_ws),
+                                   static_cast<const int32_t*>(suffix->int_ws),
+                                   static_cast<const float*>(suffix->float_ws), prefix->Hq,
+                                   static_cast<uint16_t*>(o), lse, prefix->merge_grid, s);
+  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  if (ep && (e = hipEventRecord(ep[2], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (es && (e = hipEventRecord(es[2], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   return PKD_OK;
 }
 

@@ -100,6 +100,11 @@ hipError_t launch_append_kv_fp8(const void* k_new, const void* v_new,
 
 // Merge of the split requests of the current plan (reads the plan image).
 hipError_t launch_merge_partials(const MergeParams& p, int grid, hipStream_t stream);
+// Merge of two all-partials plans' states per request (plan A's first):
+// the composable format's one merge (merge.hip).
+hipError_t launch_merge_composable(const int32_t* ws_a, const float* fws_a, const int32_t* ws_b,
+                                   const float* fws_b, int H, uint16_t* o_out, float* lse_out,
+                                   int grid, hipStream_t stream);
 // Merge of `k` bf16 states per row, rows laid out uniformly.
 hipError_t launch_merge_states_bf16(const MergeParams& p, hipStream_t stream);
 // Row-wise merge of two bf16 states.

@@ -246,6 +246,130 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(MergePara
   }
 }
 
+// The composable format's merge: for each request r and query head h, the
+// partial states of r in plan A (a shared-prefix plan: the chunks of r's
+// group) followed by those of r in plan B (a decode plan: the chunks of r's
+// own pages), both plans made with every request's states as partials, so
+// entry r of each plan's merge list is request r.  The states are dealt to
+// the 8 lane groups as in merge_task, state c of the joint sequence being
+// A's c-th for c < k_A and B's (c - k_A)-th after, and combined by the same
+// rule in the same fixed order.
+struct Segment {
+  const float* o;    // partial o of the plan, [n_partials, H, 128]
+  const float* lse;  // partial lse, [n_partials, H]
+  int64_t first;
+  int k;
+};
+
+__device__ void merge_segments(const Segment& a, const Segment& b, int H, int h, int64_t out_row,
+                               uint16_t* o_out, float* lse_out, float* grp_m, float* grp_s,
+                               float4* grp_acc) {
+  const int tid = threadIdx.x;
+  const int grp = tid >> 5;
+  const int gl = tid & 31;
+  const int k = a.k + b.k;
+  float m = kNegInf, s = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = grp; c0 < k; c0 += 8 * kRound) {
+    float L[kRound];
+    float4 v[kRound];
+#pragma unroll
+    for (int r = 0; r < kRound; ++r) {
+      const int c = c0 + 8 * r;
+      L[r] = kNegInf;
+      v[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c < k) {
+        const bool in_a = c < a.k;
+        const Segment& g = in_a ? a : b;
+        const int64_t st = g.first + (in_a ? c : c - a.k);
+        L[r] = g.lse[st * H + h];
+        v[r] = load4(g.o + (st * H + h) * kHeadDim + gl * 4);
+      }
+    }
+    float mr = m;
+#pragma unroll
+    for (int r = 0; r < kRound; ++r) mr = fmaxf(mr, L[r]);
+    if (mr == kNegInf) continue;
+    const float keep = __builtin_amdgcn_exp2f((m - mr) * kLog2e);
+    s *= keep;
+    acc.x *= keep;
+    acc.y *= keep;
+    acc.z *= keep;
+    acc.w *= keep;
+#pragma unroll
+    for (int r = 0; r < kRound; ++r) {
+      const float w = __builtin_amdgcn_exp2f((L[r] - mr) * kLog2e);
+      s += w;
+      acc.x = fmaf(w, v[r].x, acc.x);
+      acc.y = fmaf(w, v[r].y, acc.y);
+      acc.z = fmaf(w, v[r].z, acc.z);
+      acc.w = fmaf(w, v[r].w, acc.w);
+    }
+    m = mr;
+  }
+  if (gl == 0) {
+    grp_m[grp] = m;
+    grp_s[grp] = s;
+  }
+  grp_acc[grp * 32 + gl] = acc;
+  __syncthreads();
+  if (grp == 0) {
+    float M = kNegInf;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) M = fmaxf(M, grp_m[g]);
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lse = kNegInf;
+    if (M != kNegInf) {
+      float S = 0.f;
+      float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const float w = __builtin_amdgcn_exp2f((grp_m[g] - M) * kLog2e);
+        const float4 x = grp_acc[g * 32 + gl];
+        S = fmaf(w, grp_s[g], S);
+        A.x = fmaf(w, x.x, A.x);
+        A.y = fmaf(w, x.y, A.y);
+        A.z = fmaf(w, x.z, A.z);
+        A.w = fmaf(w, x.w, A.w);
+      }
+      const float inv = 1.f / S;
+      o = make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
+      lse = M + __log2f(S) * kLn2;
+    }
+    uint2 w;
+    w.x = pack_bf16x2(o.x, o.y);
+    w.y = pack_bf16x2(o.z, o.w);
+    *reinterpret_cast<uint2*>(o_out + (out_row * H + h) * kHeadDim + gl * 4) = w;
+    if (lse_out && gl == 0) lse_out[out_row * H + h] = lse;
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kMergeThreads) void merge_composable_kernel(
+    const int32_t* __restrict__ ws_a, const float* __restrict__ fws_a,
+    const int32_t* __restrict__ ws_b, const float* __restrict__ fws_b, int H,
+    uint16_t* __restrict__ o_out, float* __restrict__ lse_out) {
+  __shared__ float grp_m[8];
+  __shared__ float grp_s[8];
+  __shared__ float4 grp_acc[8 * 32];
+  const int32_t* ha = ws_a + PKD_HEADER_BASE;
+  const int32_t* hb = ws_b + PKD_HEADER_BASE;
+  // both lists name every request in order (checked on the host)
+  const int n = min(ha[PKD_H_SPLIT], hb[PKD_H_SPLIT]);
+  const int32_t* ma = ws_a + ha[PKD_H_OFF_MERGE];
+  const int32_t* mb = ws_b + hb[PKD_H_OFF_MERGE];
+  const float* lse_a = fws_a + int64_t(ha[PKD_H_PARTIALS]) * H * kHeadDim;
+  const float* lse_b = fws_b + int64_t(hb[PKD_H_PARTIALS]) * H * kHeadDim;
+  const int64_t tasks = int64_t(n) * H;
+  for (int64_t task = blockIdx.x; task < tasks; task += gridDim.x) {
+    const int e = int(task / H);
+    const int h = int(task - int64_t(e) * H);
+    const Segment a = {fws_a, lse_a, ma[4 * e + 1], ma[4 * e + 2]};
+    const Segment b = {fws_b, lse_b, mb[4 * e + 1], mb[4 * e + 2]};
+    merge_segments(a, b, H, h, ma[4 * e], o_out, lse_out, grp_m, grp_s, grp_acc);
+  }
+}
+
 // k bf16 states per row, rows laid out uniformly.
 __global__ __launch_bounds__(kMergeThreads) void merge_states_kernel(MergeParams p) {
   __shared__ float grp_m[8];
@@ -297,6 +421,14 @@ __global__ __launch_bounds__(256) void merge_two_kernel(const uint16_t* o_a, con
 
 hipError_t launch_merge_partials(const MergeParams& p, int grid, hipStream_t stream) {
   hipLaunchKernelGGL(merge_partials_kernel, dim3(grid), dim3(kMergeThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_composable(const int32_t* ws_a, const float* fws_a, const int32_t* ws_b,
+                                   const float* fws_b, int H, uint16_t* o_out, float* lse_out,
+                                   int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(merge_composable_kernel, dim3(grid), dim3(kMergeThreads), 0, stream, ws_a,
+                     fws_a, ws_b, fws_b, H, o_out, lse_out);
   return hipGetLastError();
 }
 

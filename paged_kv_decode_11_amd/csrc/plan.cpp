@@ -28,6 +28,8 @@ namespace pkd {
 
 namespace {
 
+static_assert(PKD_H_COUNT <= 32, "the header fills the 32 words before slot_indptr");
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t align_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
@@ -101,6 +103,7 @@ int plan_validate(const PlanInput& in, std::string* err) {
   if (!in.indptr || !in.last) return fail(PKD_ERR_INVALID_ARG, "kv_indptr and kv_last_page_len must be non-null");
   if (in.batch < 1) return fail(PKD_ERR_INVALID_ARG, "batch must be >= 1");
   if (in.num_slots < 1) return fail(PKD_ERR_INVALID_ARG, "num_slots must be >= 1");
+  if (in.flags & ~int32_t(PKD_PLAN_ALL_PARTIALS)) return fail(PKD_ERR_INVALID_ARG, "unknown plan flags");
   if (in.page_size < 1) return fail(PKD_ERR_INVALID_ARG, "page_size must be >= 1");
   if (in.num_qo_heads < 1 || in.num_kv_heads < 1)
     return fail(PKD_ERR_INVALID_ARG, "head counts must be >= 1");
@@ -169,7 +172,7 @@ int plan_measure(const PlanInput& in, PlanScratch& s, PlanLayout* layout, std::s
     const int64_t n = in.indptr[i + 1] - in.indptr[i];
     const int64_t k = ceil_div(n, cp);
     const int64_t rows = rows_of(i);
-    const bool split = k > 1;
+    const bool split = k > 1 || (in.flags & PKD_PLAN_ALL_PARTIALS);
     const int64_t base = split ? next_partial : -1;
     if (split) {
       if (next_partial + rows * k > INT32_MAX) {
@@ -293,6 +296,7 @@ int plan_build(const PlanInput& in, PlanScratch& s, int32_t* image, int64_t imag
   }
   hdr[PKD_H_MIN_CHUNKS] = kmin;
   hdr[PKD_H_MAX_CHUNKS] = kmax;
+  hdr[PKD_H_FLAGS] = in.flags;
 
   int32_t* slot_indptr = image + layout->off_slots;
   for (int32_t q = 0; q <= S; ++q) slot_indptr[q] = 0;

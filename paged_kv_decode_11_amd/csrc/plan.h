@@ -29,6 +29,7 @@ struct PlanInput {
   int32_t min_chunk_tokens = 128;
   int32_t alpha = 1;
   int32_t beta = 1;
+  int32_t flags = 0;  // PKD_PLAN_* (PKD_PLAN_ALL_PARTIALS: every row writes partial states)
   int64_t plan_id = 0;
 };
 

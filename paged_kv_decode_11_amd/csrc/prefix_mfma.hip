@@ -56,9 +56,21 @@ constexpr int kTile = 64;   // tokens per tile (four quarters of 16)
 constexpr int kDepth = 4;   // tiles in flight per workgroup
 constexpr int kLdRows = kTile / 32;  // tile rows each lane loads (32 rows per pass)
 
-struct PShared {
+// A wave's 16 fp32 output rows, staged in LDS at the end of an item so that
+// each store instruction writes two whole 512-byte rows: rows 528 bytes apart
+// (512 + 16), so the 16 rows one wave writes per instruction start 4 banks
+// apart.
+constexpr int kEpiRowBytes = 528;
+constexpr int kEpiWaveBytes = 16 * kEpiRowBytes;
+
+struct PTiles {
   uint4 k[2][kTile][16];  // K tile, row r's 16-byte piece c at [r][c ^ (r & 15)]
   uint4 v[2][kTile][16];  // V tile, same layout
+};
+
+union PShared {
+  PTiles t;
+  char epi[kWaves * kEpiWaveBytes];  // partial-state rows of each wave, after the last tile
 };
 
 __device__ __forceinline__ floatx4_t mfma32(uint4 a, uint4 b, floatx4_t c) {
@@ -224,8 +236,8 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < kLdRows; ++i) {
         const int r = 32 * i + ld_row;
-        sh.k[stage][r][ld_slot] = sk[i];
-        sh.v[stage][r][ld_slot] = r < valid ? sv[i] : make_uint4(0u, 0u, 0u, 0u);
+        sh.t.k[stage][r][ld_slot] = sk[i];
+        sh.t.v[stage][r][ld_slot] = r < valid ? sv[i] : make_uint4(0u, 0u, 0u, 0u);
       }
       lds_barrier();
       if (reload) {
@@ -250,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int h = 0; h < 4; ++h)
-          sq[h] = mfma32(sh.k[stage][16 * h + row16][(4 * j + kg) ^ row16], qv[j], sq[h]);
+          sq[h] = mfma32(sh.t.k[stage][16 * h + row16][(4 * j + kg) ^ row16], qv[j], sq[h]);
       float sc[16];
       float mx = kNegInf;
 #pragma unroll
@@ -293,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
 #pragma unroll
         for (int h = 0; h < 4; ++h)
           b[h] = lds_read_tr(
-              reinterpret_cast<const char*>(&sh.v[stage][16 * h + tr_row][piece ^ tr_row]) +
+              reinterpret_cast<const char*>(&sh.t.v[stage][16 * h + tr_row][piece ^ tr_row]) +
               8 * (tr_q & 1));
         acc[cb] *= alpha;
         acc[cb] = mfma32(make_uint4(b[0].x, b[0].y, b[1].x, b[1].y), pb[0], acc[cb]);
@@ -313,14 +325,43 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
     for (int d = 0; d < kDepth; ++d)
       if (full * kDepth + d < ntiles) step(rk[d], rv[d], pid[d], full * kDepth + d, false);
 
+    // a chunk's state goes out as fp32 rows staged through LDS: wait until
+    // every wave is done with the last tile's K and V there (out is the
+    // same for all waves of the item)
+    if (out >= 0) lds_barrier();
     if (compute) {
       // lane l: query row l & 15, head dims 16 cb + 4 kg + v
       const float lt = rows_sum(lsum);
       const int i = row16 / G;
+      const float inv = 1.f / lt;
+      if (out >= 0) {
+        char* epi = sh.epi + wave * kEpiWaveBytes;
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb)
+          *reinterpret_cast<float4*>(epi + row16 * kEpiRowBytes + 64 * cb + 16 * kg) =
+              make_float4(acc[cb][0] * inv, acc[cb][1] * inv, acc[cb][2] * inv,
+                          acc[cb][3] * inv);
+        // one wave's LDS accesses complete in order: its reads below see
+        // every lane's writes
+        __builtin_amdgcn_wave_barrier();
+        // store s: rows 2 s and 2 s + 1, 16 bytes of a row per lane
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          const int r = 2 * st + (lane >> 5);
+          const float4 v = *reinterpret_cast<const float4*>(epi + r * kEpiRowBytes +
+                                                             16 * (lane & 31));
+          const int ri = r / G;
+          if (ri < nreq) {
+            const int64_t pid_out = int64_t(out) + int64_t(wrow + ri) * kchunks;
+            const int64_t qh_r = int64_t(kh) * G + r % G;
+            *reinterpret_cast<float4*>(o_part + (pid_out * Hq + qh_r) * kHeadDim +
+                                       4 * (lane & 31)) = v;
+          }
+        }
+      }
       if (i < nreq) {
         const int req_in_group = wrow + i;
         const int64_t qh = int64_t(kh) * G + row16 % G;
-        const float inv = 1.f / lt;
         const float lse_nat = (m + __log2f(lt)) * kLn2;
         if (out < 0) {
           uint16_t* orow =
@@ -333,12 +374,6 @@ __global__ __launch_bounds__(kThreads) void prefix_mfma_kernel(
           if (lse_ptr && kg == 0) lse_ptr[(int64_t(row0) + req_in_group) * Hq + qh] = lse_nat;
         } else {
           const int64_t pid_out = int64_t(out) + int64_t(req_in_group) * kchunks;
-          float* prow = o_part + (pid_out * Hq + qh) * kHeadDim + 4 * kg;
-#pragma unroll
-          for (int cb = 0; cb < 8; ++cb)
-            *reinterpret_cast<float4*>(prow + 16 * cb) =
-                make_float4(acc[cb][0] * inv, acc[cb][1] * inv, acc[cb][2] * inv,
-                            acc[cb][3] * inv);
           if (kg == 0) lse_part[pid_out * Hq + qh] = lse_nat;
         }
       }

@@ -15,10 +15,10 @@
 //   * every item lies within its row's pages, and the chunks of each row (per
 //     row block and KV head in shared-prefix plans) cover its pages exactly
 //     once, in order, with the last page's length only on the last chunk;
-//   * unsplit rows write their output directly (out = -1); the chunks of a
-//     split row, in page order, write consecutive partial ids, and the merge
-//     list names each request of a split row once, in ascending order, with
-//     its ids;
+//   * unsplit rows write their output directly (out = -1), unless the plan
+//     asks for all partials; the chunks of a split row, in page order, write
+//     consecutive partial ids, and the merge list names each request of a
+//     split row once, in ascending order, with its ids;
 //   * with derived chunks, I <= S + 2 B (decode plans);
 //   * the longest-first bound: the largest slot load is at most the mean load
 //     plus the largest item cost.
@@ -56,7 +56,7 @@ struct Failure {
 struct Case {
   std::vector<int32_t> indptr, last, qo_indptr;
   int32_t batch = 0, Hq = 32, Hkv = 8, D = 128, P = 16, S = 8;
-  int32_t fixed = 0, min_tokens = 0, alpha = -1, beta = 0;
+  int32_t fixed = 0, min_tokens = 0, alpha = -1, beta = 0, flags = 0;
   bool shared = false;
   int expect = PKD_OK;  // status the plan must return (OK unless the case is broken)
 };
@@ -83,6 +83,7 @@ Case make_case(std::mt19937_64& rng, int n) {
   if (uni(0, 2) == 0) c.alpha = int32_t(uni(-3, 100));
   if (uni(0, 2) == 0) c.beta = int32_t(uni(-3, 100));
   if (uni(0, 30) == 0) c.alpha = c.beta = std::numeric_limits<int32_t>::max();
+  if (uni(0, 3) == 0) c.flags = PKD_PLAN_ALL_PARTIALS;
   c.indptr.assign(c.batch + 1, 0);
   c.last.assign(c.batch, 1);
   const int64_t max_pages = n % 11 == 0 ? 3000 : 40;
@@ -157,6 +158,7 @@ pkd::PlanInput input_of(const Case& c) {
   in.min_chunk_tokens = c.min_tokens;
   in.alpha = c.alpha;
   in.beta = c.beta;
+  in.flags = c.flags;
   in.plan_id = 7;
   return in;
 }
@@ -167,6 +169,8 @@ void check_image(const Case& c, const pkd::PlanLayout& L, const int32_t* img) {
   EXPECT(h[PKD_H_MAGIC] == PKD_PLAN_MAGIC, "magic %x", h[PKD_H_MAGIC]);
   EXPECT(h[PKD_H_SLOTS] == S && h[PKD_H_ITEMS] == I, "header counts");
   EXPECT(h[PKD_H_KIND] == (c.shared ? PKD_PLAN_SHARED : PKD_PLAN_DECODE), "kind");
+  EXPECT(h[PKD_H_FLAGS] == c.flags, "flags %d", h[PKD_H_FLAGS]);
+  const bool all_partials = (c.flags & PKD_PLAN_ALL_PARTIALS) != 0;
   for (int w = 0; w < PKD_HEADER_BASE; ++w) EXPECT(img[w] == 0, "device word %d not zero", w);
   const int32_t* slots = img + pkd::plan_off_slots();
   EXPECT(slots[0] == 0 && slots[S] == I, "slot_indptr ends %d %d (I=%d)", slots[0], slots[S], I);
@@ -226,7 +230,7 @@ void check_image(const Case& c, const pkd::PlanLayout& L, const int32_t* img) {
   std::vector<int64_t> base_of(c.batch, -1);
   int64_t next_id = 0;
   for (int32_t r = 0; r < c.batch; ++r) {
-    if (chunks_of[r] > 1) {
+    if (chunks_of[r] > 1 || all_partials) {
       base_of[r] = next_id;
       next_id += (c.shared ? c.qo_indptr[r + 1] - c.qo_indptr[r] : 1) * int64_t(chunks_of[r]);
     }
@@ -248,7 +252,7 @@ void check_image(const Case& c, const pkd::PlanLayout& L, const int32_t* img) {
         EXPECT(q.ll == (last_chunk ? c.last[r] : P), "row %d chunk %d last_len %d", r, j, q.ll);
         EXPECT(q.len == int64_t(q.np - 1) * P + q.ll, "row %d chunk %d length", r, j);
         if (c.fixed > 0) EXPECT(q.np <= c.fixed, "row %d chunk %d above the forced size", r, j);
-        EXPECT(q.out == (chunks_of[r] > 1 ? base_of[r] + j : -1), "row %d chunk %d out %d", r, j,
+        EXPECT(q.out == (base_of[r] >= 0 ? base_of[r] + j : -1), "row %d chunk %d out %d", r, j,
                q.out);
       }
       EXPECT(next == c.indptr[r + 1], "row %d unit %lld covers pages up to %lld of %d", r,
@@ -261,7 +265,7 @@ void check_image(const Case& c, const pkd::PlanLayout& L, const int32_t* img) {
   const int32_t* merge = img + L.off_merge;
   int32_t prev = -1, split = 0;
   for (int32_t r = 0; r < c.batch; ++r) {
-    if (chunks_of[r] > 1) {
+    if (base_of[r] >= 0) {
       const int32_t rows = c.shared ? c.qo_indptr[r + 1] - c.qo_indptr[r] : 1;
       const int32_t row0 = c.shared ? c.qo_indptr[r] : r;
       for (int32_t q = 0; q < rows; ++q, ++split) {

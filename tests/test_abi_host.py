@@ -92,6 +92,8 @@ def test_plan_host_matches_oracle_bit_exact(S, seed):
     indptr, _, last = pt.page_table(lens, P)
     opts = [dict(), dict(min_chunk_tokens=16), dict(fixed_chunk_pages=3), dict(alpha=5, beta=2),
             dict(min_chunk_tokens=512), dict(fixed_chunk_pages=1)][seed]
+    if S in (3, 512):
+        opts["all_partials"] = True
     ref_opts = {k: v for k, v in opts.items()}
     if S == 1 and opts.get("fixed_chunk_pages") == 1 and int(indptr[-1]) > 20000:
         pytest.skip("oversized for a one-slot scan")
@@ -101,6 +103,9 @@ def test_plan_host_matches_oracle_bit_exact(S, seed):
     _lengths_ok(p_lib, P)
     h = p_lib["header"]
     assert h["MAGIC"] == 0x31444B50 and h["VERSION"] == 2 and h["BATCH"] == B
+    assert h["FLAGS"] == (_lib.PKD_PLAN_ALL_PARTIALS if opts.get("all_partials") else 0)
+    if opts.get("all_partials"):
+        assert p_lib["n_split"] == B and p_lib["merges"][:, 0].tolist() == list(range(B))
     assert h["SLOTS"] == S and h["PAGE_SIZE"] == P and h["NNZ"] == int(indptr[-1])
     assert h["TOTAL_TOKENS_LO"] + (h["TOTAL_TOKENS_HI"] << 32) == int(lens.sum())
 
@@ -178,6 +183,8 @@ def test_plan_shared_host_matches_oracle_bit_exact(seed):
     S = [256, 7, 1, 512, 33, 256, 64, 100][seed]
     opts = [dict(), dict(min_chunk_tokens=16), dict(fixed_chunk_pages=3), dict(alpha=5, beta=2),
             dict(min_chunk_tokens=1024), dict(), dict(fixed_chunk_pages=1), dict()][seed]
+    if seed in (3, 4, 7):
+        opts["all_partials"] = True
     lib = pkd.plan_shared_host(qo, indptr, last, Hq, Hkv, 128, P, S, **opts)
     ref = plan_ref.plan_shared(qo, indptr, last, P, S, Hq // Hkv, Hkv, **opts)
     assert lib["chunk_pages"] == ref["chunk_pages"]
@@ -188,6 +195,9 @@ def test_plan_shared_host_matches_oracle_bit_exact(seed):
     assert np.array_equal(lib["groups"], ref["groups"])
     h = lib["header"]
     assert h["KIND"] == 1 and h["BATCH"] == int(qo[-1]) and h["NUM_GROUPS"] == G
+    if opts.get("all_partials"):
+        assert lib["n_split"] == int(qo[-1])
+        assert lib["merges"][:, 0].tolist() == list(range(int(qo[-1])))
     assert h["ROWS_PER_BLOCK"] == 128 // (Hq // Hkv)
     _first_items_ok(dict(lib, first_items=lib["first_items"]))
 

@@ -155,3 +155,197 @@ def test_shared_prefix_workload_composable_full():
     o_ref, lse_ref = att.decode(q, cache, main.kv_indptr, main.kv_indices, main.kv_last_page_len,
                                 main.num_kv_heads, requests=req)
     gu.assert_close(o, lse, o_ref, lse_ref, requests=req, label="composable-shared-kernel")
+
+
+# ---------------------------------------------------------------------------
+# the composable format in one call: pkd_run_composable
+# ---------------------------------------------------------------------------
+
+def _composable_inputs(seed, rows, prefix_lens, suffix_lens, P, Hq, Hkv):
+    """Groups over prefixes and every request's own suffix, in one pool: the
+    group table, the suffix table and the cache."""
+    rng = np.random.default_rng(seed)
+    lens = list(prefix_lens) + list(suffix_lens)
+    need = int(sum(-(-l // P) for l in lens))
+    allb = workloads.make_batch(lens, P, need + 5, Hq, Hkv, 128, rng)
+    G = len(prefix_lens)
+    gi = allb.kv_indptr
+    gb = workloads.PagedBatch(P, Hq, Hkv, 128, allb.num_pages,
+                              np.asarray(prefix_lens, np.int64), gi[:G + 1].copy(),
+                              allb.kv_indices[:gi[G]].copy(), allb.kv_last_page_len[:G].copy())
+    sb = workloads.PagedBatch(P, Hq, Hkv, 128, allb.num_pages,
+                              np.asarray(suffix_lens, np.int64), (gi[G:] - gi[G]).astype(np.int32),
+                              allb.kv_indices[gi[G]:].copy(), allb.kv_last_page_len[G:].copy())
+    qo = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    q = workloads.normal_bf16(rng, (int(qo[-1]), Hq, 128))
+    cache = workloads.host_cache(allb, rng, poison=True)
+    return gb, sb, qo, q, cache
+
+
+def _composable_ref(gb, sb, qo, q, cache, Hkv, sm_scale=None):
+    from oracle import merge as om
+
+    indptr, indices, last = _expanded(gb, qo)
+    o_p, l_p = att.decode(q, cache, indptr, indices, last, Hkv, sm_scale=sm_scale)
+    o_s, l_s = att.decode(q, cache, sb.kv_indptr, sb.kv_indices, sb.kv_last_page_len, Hkv,
+                          sm_scale=sm_scale)
+    return om.merge_rows(o_p, l_p, o_s, l_s)
+
+
+def _plan_both(rp, rs, gb, sb, qo, P, Hq, Hkv, popts=None, sopts=None):
+    import torch
+
+    rp.plan(qo, gb.kv_indptr, torch.from_numpy(gb.kv_indices.astype(np.int32)).cuda(),
+            gb.kv_last_page_len, Hq, Hkv, 128, P, all_partials=True, **(popts or {}))
+    rs.plan(sb.kv_indptr, torch.from_numpy(sb.kv_indices.astype(np.int32)).cuda(),
+            sb.kv_last_page_len, Hq, Hkv, 128, P, all_partials=True, **(sopts or {}))
+
+
+@pytest.mark.parametrize("side_by_side", [False, True])
+@pytest.mark.parametrize("case", range(6))
+def test_run_composable(case, side_by_side):
+    """Prefix groups and per-request suffixes in one call (three launches)
+    against the oracle's merge of the two exact states; unsplit and split on
+    either side, one-token suffixes, several groups, group sizes 1-8."""
+    import torch
+    import paged_kv_decode_11_amd as pkd
+
+    P, Hq, Hkv, rows, plens, popts, sopts = [
+        (16, 32, 8, [32], [8 * 16 + 5], {}, {}),
+        (16, 32, 8, [5, 40, 1], [300, 2000, 17], {"fixed_chunk_pages": 2}, {"fixed_chunk_pages": 1}),
+        (32, 64, 8, [20], [1000], {"min_chunk_tokens": 32}, {}),
+        (64, 8, 8, [9, 3], [700, 64], {}, {"fixed_chunk_pages": 3}),
+        (16, 16, 2, [33], [5000], {}, {"min_chunk_tokens": 16}),
+        (16, 32, 8, [2, 2, 2, 2], [16, 32, 48, 1], {"fixed_chunk_pages": 1}, {}),
+    ][case]
+    B = int(sum(rows))
+    rng = np.random.default_rng(600 + case)
+    slens = rng.integers(1, 900, size=B).tolist()
+    slens[0] = 1
+    gb, sb, qo, q, cache = _composable_inputs(610 + case, rows, plens, slens, P, Hq, Hkv)
+    gu.say("composable", case, "side by side", side_by_side, "rows", rows, "prefix", plens, "P", P,
+           "Hq", Hq, "Hkv", Hkv)
+    # workspaces with room for the forced one- and two-page chunks
+    slots = _half_cus() if side_by_side else 0
+    rp = pkd.SharedPlanRun(64, 256, 1 << 14, Hq, Hkv, num_slots=slots)
+    rs = pkd.DecodePlanRun(max_batch=1024, max_nnz=1 << 14, max_qo_heads=Hq, num_slots=slots)
+    _plan_both(rp, rs, gb, sb, qo, P, Hq, Hkv, popts, sopts)
+    o, lse = pkd.run_composable(rp, rs, gu.bits_to_dev(q), gu.bits_to_dev(cache), return_lse=True)
+    torch.cuda.synchronize()
+    assert rp.read_device_error() == 0 and rs.read_device_error() == 0
+    o_ref, lse_ref = _composable_ref(gb, sb, qo, q, cache, Hkv)
+    gu.assert_close(o, lse, o_ref, lse_ref, label=f"composable-{case}")
+
+
+def test_run_composable_refusals():
+    import torch
+    import paged_kv_decode_11_amd as pkd
+    from paged_kv_decode_11_amd import _lib
+
+    gb, sb, qo, q, cache = _composable_inputs(620, [4], [100], [5, 6, 7, 8], 16, 32, 8)
+    qd, cd = gu.bits_to_dev(q), gu.bits_to_dev(cache)
+    rp = pkd.SharedPlanRun(2, 16, 1 << 10, 32, 8)
+    rs = pkd.DecodePlanRun(max_batch=16, max_nnz=1 << 10, max_qo_heads=32)
+    idx_g = torch.from_numpy(gb.kv_indices.astype(np.int32)).cuda()
+    idx_s = torch.from_numpy(sb.kv_indices.astype(np.int32)).cuda()
+    # plans without all_partials
+    rp.plan(qo, gb.kv_indptr, idx_g, gb.kv_last_page_len, 32, 8, 128, 16)
+    rs.plan(sb.kv_indptr, idx_s, sb.kv_last_page_len, 32, 8, 128, 16)
+    with pytest.raises(pkd.PkdError) as e:
+        pkd.run_composable(rp, rs, qd, cd)
+    assert e.value.code == _lib.PKD_ERR_INVALID_ARG
+    _plan_both(rp, rs, gb, sb, qo, 16, 32, 8)
+    with pytest.raises(pkd.PkdError) as e:   # handles swapped
+        pkd.run_composable(rs, rp, qd, cd)
+    assert e.value.code == _lib.PKD_ERR_INVALID_ARG
+    # a suffix plan for another batch
+    rs.plan(sb.kv_indptr[:3], idx_s, sb.kv_last_page_len[:2], 32, 8, 128, 16, all_partials=True)
+    with pytest.raises(pkd.PkdError) as e:
+        pkd.run_composable(rp, rs, qd, cd)
+    assert e.value.code == _lib.PKD_ERR_STALE_PLAN
+
+
+def _half_cus():
+    import torch
+
+    return torch.cuda.get_device_properties(0).multi_processor_count // 2
+
+
+@pytest.mark.parametrize("side_by_side", [False, True])
+def test_run_composable_graph_replay(side_by_side):
+    """A composable run captured once replays correctly after both handles
+    are planned again for other lengths: with the default slot counts (the
+    three kernels one after the other) and with half of the compute units
+    for each handle (the decode kernel on the suffix handle's own stream,
+    forked and joined inside the captured run)."""
+    import torch
+    import paged_kv_decode_11_amd as pkd
+
+    P, Hq, Hkv, rows = 16, 32, 8, [6, 10]
+    B = sum(rows)
+    slots = _half_cus() if side_by_side else 0
+    rp = pkd.SharedPlanRun(4, 64, 1 << 12, Hq, Hkv, num_slots=slots)
+    rs = pkd.DecodePlanRun(max_batch=512, max_nnz=1 << 12, max_qo_heads=Hq, num_slots=slots)
+    steps = []
+    for seed in range(3):
+        rng = np.random.default_rng(700 + seed)
+        plens = rng.integers(1, 1500, size=2).tolist()
+        slens = rng.integers(1, 600, size=B).tolist()
+        steps.append(_composable_inputs(710 + seed, rows, plens, slens, P, Hq, Hkv))
+    pool = max(s[0].num_pages for s in steps)
+    # one device cache large enough for every step's pool
+    cd = torch.zeros((pool, 2, P, Hkv, 128), dtype=torch.bfloat16, device="cuda")
+    q_buf = torch.zeros((B, Hq, 128), dtype=torch.bfloat16, device="cuda")
+    o_buf = torch.zeros((B, Hq, 128), dtype=torch.bfloat16, device="cuda")
+    lse_buf = torch.zeros((B, Hq), dtype=torch.float32, device="cuda")
+    gb, sb, qo, q, cache = steps[0]
+    _plan_both(rp, rs, gb, sb, qo, P, Hq, Hkv)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        pkd.run_composable(rp, rs, q_buf, cd, out=o_buf, lse=lse_buf, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pkd.run_composable(rp, rs, q_buf, cd, out=o_buf, lse=lse_buf)
+    torch.cuda.synchronize()
+    for n, (gb, sb, qo, q, cache) in enumerate(steps[1:] + steps[:1]):
+        gu.say("composable graph step", n)
+        _plan_both(rp, rs, gb, sb, qo, P, Hq, Hkv, sopts={"fixed_chunk_pages": n + 1})
+        cd[:cache.shape[0]].copy_(gu.bits_to_dev(cache))
+        q_buf.copy_(gu.bits_to_dev(q))
+        for _ in range(2):
+            o_buf.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            o_ref, lse_ref = _composable_ref(gb, sb, qo, q, cache, Hkv)
+            gu.assert_close(o_buf, lse_buf, o_ref, lse_ref, label=f"composable replay {n}")
+
+
+def test_shared_prefix_workload_run_composable_full():
+    """The shared-prefix workload at full size through pkd_run_composable,
+    against the single-format oracle on 8 requests."""
+    import torch
+    import paged_kv_decode_11_amd as pkd
+
+    spec, rng, b = workloads.workload("shared_prefix")
+    main, prefix, suffix = b["main"], b["prefix"], b["suffix"]
+    q = workloads.host_query(main, rng)
+    cache = workloads.host_cache(main, rng)
+    gu.say("shared_prefix run_composable", main.batch, main.total_tokens)
+    qd, cd = gu.bits_to_dev(q), gu.bits_to_dev(cache)
+    n_pages = int(prefix.kv_indptr[1])
+    rp = pkd.SharedPlanRun(4, 64, 1 << 12, 32, 8)
+    rs = pkd.DecodePlanRun(max_batch=64, max_nnz=1 << 12, max_qo_heads=32)
+    rp.plan(np.array([0, main.batch], np.int32), np.array([0, n_pages], np.int32),
+            torch.from_numpy(prefix.kv_indices[:n_pages].astype(np.int32)).cuda(),
+            prefix.kv_last_page_len[:1], 32, 8, 128, 16, all_partials=True)
+    rs.plan(suffix.kv_indptr, torch.from_numpy(suffix.kv_indices.astype(np.int32)).cuda(),
+            suffix.kv_last_page_len, 32, 8, 128, 16, all_partials=True)
+    o, lse = pkd.run_composable(rp, rs, qd, cd, return_lse=True)
+    torch.cuda.synchronize()
+    req = [0, 3, 7, 12, 18, 24, 29, 31]
+    o_ref, lse_ref = att.decode(q, cache, main.kv_indptr, main.kv_indices, main.kv_last_page_len,
+                                main.num_kv_heads, requests=req)
+    gu.assert_close(o, lse, o_ref, lse_ref, requests=req, label="run_composable full")

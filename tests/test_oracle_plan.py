@@ -43,6 +43,26 @@ def test_hand_worked_split_and_writethrough():
         assert p["n_partials"] == 4 and p["n_split"] == 1 and p["num_items"] == 5
 
 
+def test_hand_worked_all_partials():
+    # The same schedule as above with every request's states as partials:
+    # request 1's one chunk now gets partial id 4 (after request 0's four)
+    # and a merge-list entry of its own; slots and order do not change.
+    indptr, _, last = pt.page_table([100, 20], 16)
+    for impl in (plan_ref.plan, plan_ref.plan_naive):
+        p = impl(indptr, last, 16, 4, min_chunk_tokens=16, all_partials=True)
+        assert p["slot_indptr"].tolist() == [0, 1, 2, 3, 5]
+        assert p["items"].tolist() == [
+            [0, 0, 2, 16, 0], [0, 2, 2, 16, 1], [0, 4, 2, 16, 2],
+            [1, 7, 2, 4, 4], [0, 6, 1, 4, 3]]
+        assert p["merges"].tolist() == [[0, 0, 4], [1, 4, 1]]
+        assert p["n_partials"] == 5 and p["n_split"] == 2
+    # the worked example, none of it split: ids 0, 1, 2, one per request
+    indptr, _, last = pt.page_table([37, 16, 5], 16)
+    p = plan_ref.plan(indptr, last, 16, 512, all_partials=True)
+    assert p["items"].tolist() == [[0, 0, 3, 5, 0], [1, 3, 1, 16, 1], [2, 4, 1, 5, 2]]
+    assert p["merges"].tolist() == [[0, 0, 1], [1, 1, 1], [2, 2, 1]]
+
+
 def test_worked_example_batch_is_not_split():
     # [37,16,5] at P 16 on 512 slots: cp = max(ceil(128/16), ceil(ceil(58/512)/16)) = 8
     indptr, _, last = pt.page_table([37, 16, 5], 16)
