@@ -772,6 +772,7 @@ def target_summary(line: dict) -> dict:
     w = line["config"]["workload"]
     frac = line["frac_of_hbm_peak"]
     out = {"us_per_layer_step": line["us_per_layer_step"], "kv_gbs": line["value"],
+           "steps": line["steps"], "warmup": line["warmup"],
            "frac_of_hbm_peak": frac, "target_frac": TARGET_FRAC.get(w),
            "meets_target": None if w not in TARGET_FRAC else bool(frac >= TARGET_FRAC[w]),
            "layers": line["config"]["layers"], "mode": line["mode"],
@@ -810,11 +811,16 @@ def main():
     extra = [t for t in args.targets.split(",") if t and t != "none" and t != w]
     if extra:
         line["targets"] = {w: target_summary(line)}
+        # a single-layer step is short (the skewed batch: about 0.37 ms for its
+        # four rotated layers), so time at least 250 steps after at least 10
+        # warm-up steps: about 0.1 s, past the start-up transient of the loop
+        sub_args = argparse.Namespace(**vars(args))
+        sub_args.steps, sub_args.warmup = max(args.steps, 250), max(args.warmup, 10)
         for t in extra:
             gc.collect()
             torch.cuda.empty_cache()
             log(f"secondary workload {t}")
-            sub = bench_decode(args, t, 0.0, ceilings=False, placement=args.placement)
+            sub = bench_decode(sub_args, t, 0.0, ceilings=False, placement=args.placement)
             line["targets"][t] = target_summary(sub)
             log(f"{t}: {line['targets'][t]['us_per_layer_step']} us/layer-step, "
                 f"{line['targets'][t]['frac_of_hbm_peak']} of HBM peak")

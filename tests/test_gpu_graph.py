@@ -70,3 +70,61 @@ def test_graph_replay_across_plans(variant):
         assert torch.isfinite(junk)
         o_ref, lse_ref = att.decode(q, cache, b.kv_indptr, b.kv_indices, b.kv_last_page_len, Hkv)
         gu.assert_close(o_buf[:B], lse_buf[:B], o_ref, lse_ref, label=f"replay-{variant}-{seed}")
+
+
+def test_merge_long_and_short_entries_across_replays():
+    """Merge-list entries of up to 10 states and of up to 300 (one request cut
+    into 300 one-page chunks): eager, and a run captured on a plan of one
+    kind replayed after a plan of the other."""
+    import torch
+    import paged_kv_decode_11_amd as pkd
+
+    P, Hq, Hkv = 16, 32, 8
+    pool = 1400
+    rng = np.random.default_rng(91)
+    r = pkd.DecodePlanRun(max_batch=1024, max_nnz=pool, max_qo_heads=Hq)
+    full = workloads.make_batch([1] * 4, P, pool, Hq, Hkv, 128, rng)
+    cache = workloads.host_cache(full, rng, fill_pages="all")
+    cd = gu.bits_to_dev(cache)
+    q = workloads.normal_bf16(rng, (4, Hq, 128))
+    qd = gu.bits_to_dev(q)
+    o_buf = torch.zeros((4, Hq, 128), dtype=torch.bfloat16, device="cuda")
+    lse_buf = torch.zeros((4, Hq), dtype=torch.float32, device="cuda")
+    # shallow: at most 10 chunks per request; deep: 300 one-page chunks
+    shallow = workloads.make_batch([160, 90, 33, 7], P, pool, Hq, Hkv, 128, rng)
+    deep = workloads.make_batch([300 * P, 70 * P - 3, 5, 1000], P, pool, Hq, Hkv, 128, rng)
+
+    def plan(b, fixed):
+        r.plan(b.kv_indptr, torch.from_numpy(b.kv_indices).cuda(), b.kv_last_page_len, Hq, Hkv,
+               128, P, fixed_chunk_pages=fixed)
+
+    for b, fixed in ((shallow, 1), (deep, 1)):
+        gu.say("merge entries eager", int(b.kv_lens.max()), fixed)
+        plan(b, fixed)
+        r.run(qd, cd, out=o_buf, lse=lse_buf)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = att.decode(q, cache, b.kv_indptr, b.kv_indices, b.kv_last_page_len, Hkv)
+        gu.assert_close(o_buf, lse_buf, o_ref, lse_ref, label="merge entries eager")
+    for first, then in (((shallow, 1), (deep, 1)), ((deep, 1), (shallow, 1))):
+        plan(*first)
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            r.run(qd, cd, out=o_buf, lse=lse_buf, stream=s)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            r.run(qd, cd, out=o_buf, lse=lse_buf)
+        torch.cuda.synchronize()
+        plan(*then)
+        b = then[0]
+        for _ in range(2):
+            o_buf.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            o_ref, lse_ref = att.decode(q, cache, b.kv_indptr, b.kv_indices, b.kv_last_page_len,
+                                        Hkv)
+            gu.assert_close(o_buf, lse_buf, o_ref, lse_ref, label="merge entries replay")
+        del g
