@@ -88,8 +88,11 @@ KERNEL_FILES = {
     "decode_mfma_kernel": ("decode_mfma.hip", "device_common.h", "plan_layout.h"),
     "decode_kernel": ("decode.hip", "device_common.h", "plan_layout.h"),
     "decode_fp8_kernel": ("decode_fp8.hip", "device_common.h", "plan_layout.h"),
-    "decode_pv_kernel": ("decode_pv.hip", "device_common.h", "plan_layout.h"),
-    "prefix_mfma_kernel": ("prefix_mfma.hip", "device_common.h", "plan_layout.h"),
+    "decode_pv_kernel": ("decode_pv.hip", "decode_pv.h", "device_common.h", "plan_layout.h"),
+    "prefix_mfma_kernel": ("prefix_mfma.hip", "prefix_mfma.h", "device_common.h",
+                           "plan_layout.h"),
+    "composable_kernel": ("composable.hip", "prefix_mfma.h", "decode_pv.h", "device_common.h",
+                          "plan_layout.h"),
 }
 
 
@@ -399,19 +402,20 @@ def bench_shared_prefix(args):
         plan2()
         run2()
     torch.cuda.synchronize()
-    pre_ms, pre_tail_ms, runs = rp.profile_read()
-    suf_ms, suf_tail_ms, sruns = rs.profile_read()
+    attn_ms, merge_ms, runs = rp.profile_read()
+    rs.profile_read()
     rp.profile_enable(False)
     rs.profile_enable(False)
-    prefix_us = pre_ms * 1e3 / runs
-    # the two kernels run side by side; each handle's second interval runs
-    # from its kernel's end to the merge's end, so the shorter one is the
-    # merge (after whichever kernel ended last)
-    prefix_merge_us = min(pre_tail_ms * 1e3 / runs, suf_tail_ms * 1e3 / sruns)
-    breakdown = {"prefix_kernel": round(prefix_us, 2),
-                 "suffix_decode": round(suf_ms * 1e3 / sruns, 2),
-                 "merge": round(prefix_merge_us, 2),
-                 "prefix_slots": rp.num_slots, "suffix_slots": rs.num_slots}
+    # pkd_run_composable runs both attention kernels in one launch when the
+    # two handles' slots fit the compute units side by side and the suffix
+    # plan runs the matrix-core P.V kernel
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    one_launch = rp.num_slots + rs.num_slots <= cus and rs.planned_variant == "mfma_pv"
+    attn_us = attn_ms * 1e3 / runs
+    prefix_merge_us = merge_ms * 1e3 / runs
+    breakdown = {"attention_kernels": round(attn_us, 2), "merge": round(prefix_merge_us, 2),
+                 "one_launch": one_launch, "prefix_slots": rp.num_slots,
+                 "suffix_slots": rs.num_slots}
     log(f"composable launches (us): {breakdown}")
 
     ms1 = time_graph(run1, args.steps, args.warmup, plan1)
@@ -419,10 +423,12 @@ def bench_shared_prefix(args):
     ms5 = time_graph(run5, args.steps, args.warmup, plan5)
     us1, us2, us5 = ms1 * 1e3 / R, ms2 * 1e3 / R, ms5 * 1e3 / R
     value = unique_bytes * R / (ms2 / 1e3) / 1e9
-    prefix_bytes = prefix_tokens * kv_tok
-    achieved = prefix_bytes / (prefix_us / 1e6) / 1e9
+    # the attention launch(es) read the prefix once per KV head and every
+    # suffix once: the unique K/V bytes
+    achieved = unique_bytes / (attn_us / 1e6) / 1e9
+    roof_kernel = "composable_kernel" if one_launch else "prefix_mfma_kernel + decode kernel"
     log(f"single format {us1:.1f} us/layer, composable {us2:.1f} us/layer (five launches "
-        f"{us5:.1f}; prefix kernel {prefix_us:.1f} us)")
+        f"{us5:.1f}; attention {attn_us:.1f} us, merge {prefix_merge_us:.1f} us)")
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms2, 4),
@@ -443,9 +449,10 @@ def bench_shared_prefix(args):
         "single_format_kv_gbs": round(single_bytes * R / (ms1 / 1e3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic("shared_prefix", "prefix_mfma_kernel", "bf16"),
-                     "kernel": "prefix_mfma_kernel", "avg_launch_us": round(prefix_us, 2),
-                     "algorithmic_bytes_per_launch": prefix_bytes,
+                     "traffic": (measured_traffic("shared_prefix", "composable_kernel", "bf16")
+                                 if one_launch else None),
+                     "kernel": roof_kernel, "avg_launch_us": round(attn_us, 2),
+                     "algorithmic_bytes_per_launch": unique_bytes,
                      "merge_avg_launch_us": round(prefix_merge_us, 2)},
         "composable_launch_us": breakdown,
         "formats_max_abs_diff_five_launch": diff5,

@@ -404,12 +404,14 @@ int pkd_run_scaled(pkd_handle* h, const void* q, int32_t batch, const void* kv_c
  * suffix chunks' states into o (bf16 [batch, num_qo_heads, head_dim]) and
  * lse (fp32 [batch, num_qo_heads], may be NULL).  When the two handles' slot
  * counts together fit the compute units (one workgroup each, e.g. half of
- * them each), the decode kernel runs beside the prefix kernel on a stream
- * the suffix handle keeps for this (made on its first such run, forked from
- * `stream` and joined back before the merge); otherwise the three run on
- * `stream` in turn.  A run captured in a graph replays correctly after
- * re-plans of either handle on the same workspaces.  Device errors are
- * raised on each handle's own flag. */
+ * them each) and the suffix plan runs PKD_VARIANT_MFMA_PV (its default for
+ * short suffixes), the two attention kernels are one launch whose
+ * workgroups split between the plans, so they run side by side; otherwise
+ * they run one after the other.  All launches are on `stream`.  A run
+ * captured in a graph replays correctly after re-plans of either handle on
+ * the same workspaces (the choice between the two forms is made at the call
+ * from the handles' slot counts and the suffix plan's kernel).  Device
+ * errors are raised on each handle's own flag. */
 int pkd_run_composable(pkd_handle* prefix, pkd_handle* suffix, const void* q, int32_t batch,
                        const void* kv_cache, int64_t num_pages, int32_t q_dtype, int32_t kv_dtype,
                        void* o, float* lse, float sm_scale, pkd_stream_t stream);

@@ -29,7 +29,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I", I
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 KERNEL_SOURCES = ["decode.hip", "decode_mfma.hip", "decode_pv.hip", "decode_fp8.hip", "merge.hip",
                   "upload.hip", "prefix_mfma.hip", "append.hip", "read_ceiling.hip",
-                  "static_scratch.hip"]
+                  "static_scratch.hip", "composable.hip"]
 HOST_SOURCES = ["plan.cpp", "api.cpp"]
 
 

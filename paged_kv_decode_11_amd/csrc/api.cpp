@@ -61,11 +61,6 @@ struct pkd_handle {
   bool static_plan = false;  // the current plan lives in the static array
   int32_t plan_flags = 0;    // PKD_PLAN_* flags of the current plan
 
-  // pkd_run_composable, as the suffix handle: the stream its decode kernel
-  // runs on beside the prefix kernel, and the events of that fork and join
-  // (made on the first such run)
-  hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
 
   // profiling
   bool profile = false;
@@ -255,12 +250,6 @@ int pkd_destroy(pkd_handle* h) {
     }
   }
   for (hipEvent_t ev : h->prof_events) (void)hipEventDestroy(ev);
-  if (h->side) {
-    (void)hipStreamSynchronize(h->side);
-    (void)hipStreamDestroy(h->side);
-  }
-  if (h->fork) (void)hipEventDestroy(h->fork);
-  if (h->join) (void)hipEventDestroy(h->join);
   delete h;
   return PKD_OK;
 }
@@ -724,58 +713,49 @@ int pkd_run_composable(pkd_handle* prefix, pkd_handle* suffix, const void* q, in
     return dp;
   };
   // When the two grids fit the chip side by side (one workgroup per compute
-  // unit each), the suffix decode runs on the suffix handle's side stream,
-  // forked from `s` and joined back before the merge, beside the prefix
-  // kernel; otherwise each kernel would only slow the other (measured), and
-  // they run one after the other on `s`.
-  const bool side_by_side = prefix->num_slots + suffix->num_slots <= prefix->cu_count;
-  hipError_t e = hipSuccess;
-  if (side_by_side && !suffix->side) {
-    e = hipStreamCreateWithFlags(&suffix->side, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&suffix->fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&suffix->join, hipEventDisableTiming);
-    if (e != hipSuccess) return hip_fail(e, "side stream for the suffix decode");
-  }
-  hipStream_t side = side_by_side ? suffix->side : s;
-  // prefix handle: start, after its kernel, after the merge; suffix handle:
-  // start and end of its kernel (side stream), after the merge
+  // unit each) and the suffix plan runs the matrix-core P.V kernel, one
+  // launch runs both: the prefix plan's workgroups and the suffix plan's on
+  // disjoint compute units at the same time.  Otherwise the two kernels run
+  // one after the other.  (Two streams forked and joined inside the call were
+  // measured first: the waits between them cost more than the overlap gave.)
+  const bool one_launch = prefix->num_slots + suffix->num_slots <= prefix->cu_count &&
+                          suffix->variant == PKD_VARIANT_MFMA_PV &&
+                          suffix->kv_dtype == PKD_DTYPE_BF16;
+  // profiling, both handles: start, after the attention kernel(s), after the merge
   hipEvent_t *ep = nullptr, *es = nullptr;
-  e = profile_events(prefix, s, &ep);
+  hipError_t e = profile_events(prefix, s, &ep);
   if (e == hipSuccess) e = profile_events(suffix, s, &es);
   if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
-  if (side_by_side && ((e = hipEventRecord(suffix->fork, s)) != hipSuccess ||
-                       (e = hipStreamWaitEvent(side, suffix->fork, 0)) != hipSuccess))
-    return hip_fail(e, "fork to the side stream");
-  if (es && (e = hipEventRecord(es[0], side)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  const pkd::DecodeParams ds = params(suffix);
+  for (hipEvent_t* ev : {ep, es})
+    if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  const pkd::DecodeParams dpre = params(prefix), ds = params(suffix);
   const int g = suffix->Hq / suffix->Hkv;
-  if (suffix->kv_dtype == PKD_DTYPE_FP8_E4M3)
-    e = pkd::launch_decode_fp8(ds, g, suffix->P, suffix->num_slots, side);
-  else if (suffix->variant == PKD_VARIANT_MFMA_PV)
-    e = pkd::launch_decode_pv(ds, g, suffix->P, suffix->num_slots, side);
-  else if (suffix->variant == PKD_VARIANT_DOT2)
-    e = pkd::launch_decode(ds, g, suffix->P, suffix->num_slots, side);
-  else
-    e = pkd::launch_decode_mfma(ds, g, suffix->P, suffix->num_slots, side);
-  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
-  if (es && (e = hipEventRecord(es[1], side)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  if (side_by_side && (e = hipEventRecord(suffix->join, side)) != hipSuccess)
-    return hip_fail(e, "join from the side stream");
-  if (ep && (e = hipEventRecord(ep[0], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  e = pkd::launch_prefix_mfma(params(prefix), prefix->Hq / prefix->Hkv, prefix->P,
-                              prefix->num_slots, s);
-  if (e != hipSuccess) return hip_fail(e, "shared-prefix kernel launch");
-  if (ep && (e = hipEventRecord(ep[1], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  if (side_by_side && (e = hipStreamWaitEvent(s, suffix->join, 0)) != hipSuccess)
-    return hip_fail(e, "join from the side stream");
+  if (one_launch) {
+    e = pkd::launch_composable(dpre, ds, g, prefix->P, prefix->num_slots, suffix->num_slots, s);
+    if (e != hipSuccess) return hip_fail(e, "composable kernel launch");
+  } else {
+    e = pkd::launch_prefix_mfma(dpre, prefix->Hq / prefix->Hkv, prefix->P, prefix->num_slots, s);
+    if (e != hipSuccess) return hip_fail(e, "shared-prefix kernel launch");
+    if (suffix->kv_dtype == PKD_DTYPE_FP8_E4M3)
+      e = pkd::launch_decode_fp8(ds, g, suffix->P, suffix->num_slots, s);
+    else if (suffix->variant == PKD_VARIANT_MFMA_PV)
+      e = pkd::launch_decode_pv(ds, g, suffix->P, suffix->num_slots, s);
+    else if (suffix->variant == PKD_VARIANT_DOT2)
+      e = pkd::launch_decode(ds, g, suffix->P, suffix->num_slots, s);
+    else
+      e = pkd::launch_decode_mfma(ds, g, suffix->P, suffix->num_slots, s);
+    if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+  }
+  for (hipEvent_t* ev : {ep, es})
+    if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   e = pkd::launch_merge_composable(static_cast<const int32_t*>(prefix->int_ws),
                                    static_cast<const float*>(prefix->float_ws),
                                    static_cast<const int32_t*>(suffix->int_ws),
                                    static_cast<const float*>(suffix->float_ws), prefix->Hq,
                                    static_cast<uint16_t*>(o), lse, prefix->merge_grid, s);
   if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
-  if (ep && (e = hipEventRecord(ep[2], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  if (es && (e = hipEventRecord(es[2], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  for (hipEvent_t* ev : {ep, es})
+    if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   return PKD_OK;
 }
 

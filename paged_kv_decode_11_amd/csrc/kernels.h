@@ -64,6 +64,13 @@ bool fp8_variant_built(int g, int page_size);
 hipError_t launch_prefix_mfma(const DecodeParams& p, int g, int page_size, int num_slots,
                               hipStream_t stream);
 bool prefix_variant_built(int g, int page_size);
+// The shared-prefix kernel on a prefix plan (workgroups [0, prefix_slots))
+// and the matrix-core P.V decode kernel on a suffix plan (the next
+// suffix_slots workgroups) in one launch (composable.hip); page sizes 16,
+// 32, 64.
+hipError_t launch_composable(const DecodeParams& pre, const DecodeParams& suf, int g,
+                             int page_size, int prefix_slots, int suffix_slots,
+                             hipStream_t stream);
 // Occupancy (workgroups per CU) of the matrix-core decode kernel at g=4,
 // P=16 (the default kernel), and of the dot-product kernel.
 int decode_blocks_per_cu(int waves_per_block);

@@ -204,9 +204,12 @@ def _plan_both(rp, rs, gb, sb, qo, P, Hq, Hkv, popts=None, sopts=None):
 @pytest.mark.parametrize("side_by_side", [False, True])
 @pytest.mark.parametrize("case", range(6))
 def test_run_composable(case, side_by_side):
-    """Prefix groups and per-request suffixes in one call (three launches)
-    against the oracle's merge of the two exact states; unsplit and split on
-    either side, one-token suffixes, several groups, group sizes 1-8."""
+    """Prefix groups and per-request suffixes in one call against the
+    oracle's merge of the two exact states; unsplit and split on either side,
+    one-token suffixes, several groups, group sizes 1-8; with the default
+    slot counts (three launches) and with half of the compute units per
+    handle (both attention kernels in one launch, KV head counts 2 and 8
+    among the cases)."""
     import torch
     import paged_kv_decode_11_amd as pkd
 
@@ -276,8 +279,8 @@ def test_run_composable_graph_replay(side_by_side):
     """A composable run captured once replays correctly after both handles
     are planned again for other lengths: with the default slot counts (the
     three kernels one after the other) and with half of the compute units
-    for each handle (the decode kernel on the suffix handle's own stream,
-    forked and joined inside the captured run)."""
+    for each handle (both attention kernels in one launch, then the
+    merge)."""
     import torch
     import paged_kv_decode_11_amd as pkd
 
