@@ -268,8 +268,9 @@ int pkd_plan_host(const int32_t* kv_indptr, const int32_t* kv_last_page_len, int
  * "Composable Format：共享前缀与独有后缀分开算", puts a prefix that several
  * requests share in one block row of the KV matrix so that one workgroup
  * reads each prefix page once for all of them (pyshine, "Cascades, Merges,
- * and the Autotuner": attention over the shared pages once for all queries,
- * then the exact merge with each request's own suffix state).
+ * and the Autotuner", describes the same cascade: one pass over the shared
+ * prefix serves every request of the group, and each request's suffix
+ * state is merged in afterwards).
  *
  * num_groups groups: group g's requests are rows qo_indptr[g] ..
  * qo_indptr[g+1]-1 of q (host int32 [num_groups+1], qo_indptr[0] = 0, every
