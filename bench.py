@@ -808,8 +808,6 @@ def main():
         return
     import gc
 
-    import torch
-
     line = bench_decode(args, args.workload, args.cpu_seconds, placement=args.placement)
     w = args.workload
     if w in TARGET_FRAC:
@@ -824,8 +822,9 @@ def main():
         sub_args = argparse.Namespace(**vars(args))
         sub_args.steps, sub_args.warmup = max(args.steps, 250), max(args.warmup, 10)
         for t in extra:
+            # the freed caches stay in torch's pool: handed back to the driver,
+            # their clearing would share HBM with the next workload's timing
             gc.collect()
-            torch.cuda.empty_cache()
             log(f"secondary workload {t}")
             sub = bench_decode(sub_args, t, 0.0, ceilings=False, placement=args.placement)
             line["targets"][t] = target_summary(sub)

@@ -118,7 +118,11 @@ enum {
  *                                 can read it without waiting for
  *                                 slot_indptr; off_first = 64 + S + 1
  *                                 rounded up to a multiple of 8
- *   [off_items, +8*I)             off_items = off_first + 8*S.
+ *   [off_merge, +4*n_split)       off_merge = off_first + 8*S.  Split
+ *                                 requests in ascending order: request,
+ *                                 first partial id, number of partials, 0
+ *   [off_items, +8*I)             off_items = off_merge + 4*n_split rounded
+ *                                 up to a multiple of 8.
  *                                 Items, 8 ints each: request, page_begin
  *                                 (index into kv_indices), num_pages,
  *                                 last_len, out (partial id, -1 = write the
@@ -129,9 +133,8 @@ enum {
  *                                 are the page ids kv_indices[page_begin]
  *                                 and kv_indices[page_begin + 1] (the first
  *                                 twice for a one-page item)
- *   [off_merge, +4*n_split)       split requests in ascending order: request,
- *                                 first partial id, number of partials, 0
- *   [off_groups, +4*num_groups)   shared-prefix plans only: per group, its
+ *   [off_groups, +4*num_groups)   off_groups = off_items + 8*I.
+ *                                 Shared-prefix plans only: per group, its
  *                                 first request row, request count, chunk
  *                                 count k and first partial id (-1 when
  *                                 k = 1)
@@ -181,7 +184,7 @@ enum {
 };
 #define PKD_HEADER_BASE 32
 #define PKD_PLAN_MAGIC 0x31444B50
-#define PKD_PLAN_VERSION 2
+#define PKD_PLAN_VERSION 3
 
 /* ------------------------------- handle ------------------------------- */
 

@@ -13,6 +13,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <exception>
@@ -23,6 +24,7 @@
 #include "kernels.h"
 #include "pkd.h"
 #include "plan.h"
+#include "plan_layout.h"
 
 struct pkd_handle {
   int device = 0;
@@ -99,6 +101,15 @@ struct DeviceGuard {
 };
 
 size_t ints_to_bytes(int64_t n) { return size_t(n) * sizeof(int32_t); }
+
+// Merge-list entries the current plan's int workspace holds from the list's
+// fixed offset on: a merge workgroup may request its first entry before it
+// knows the list's length, and stays inside the workspace this way.
+int32_t merge_cap(const pkd_handle* h) {
+  const int64_t ints = int64_t(h->int_bytes / sizeof(int32_t));
+  const int64_t cap = (ints - pkd::plan_off_merge(h->num_slots)) / 4;
+  return int32_t(std::max<int64_t>(0, std::min<int64_t>(cap, INT32_MAX)));
+}
 
 constexpr int64_t kStagingAlignInts = 64;  // 256-byte aligned halves
 
@@ -466,11 +477,12 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
     h->host_view_for = host_workspace;
   }
   int32_t* dev = static_cast<int32_t*>(int_workspace);
-  // the item rows of a decode plan (the first-item table and the items,
-  // contiguous) get their items' first two page ids on the device, in words 6
-  // and 7; a shared-prefix plan keeps row block and head there
-  const int64_t item_rows =
-      layout.kind == PKD_PLAN_DECODE ? int64_t(h->num_slots) + layout.num_items : 0;
+  // the item rows of a decode plan (the first-item table and the items) get
+  // their items' first two page ids on the device, in words 6 and 7; a
+  // shared-prefix plan keeps row block and head there
+  const bool decode_rows = layout.kind == PKD_PLAN_DECODE;
+  const int64_t first_rows = decode_rows ? int64_t(h->num_slots) : 0;
+  const int64_t item_rows = decode_rows ? int64_t(layout.num_items) : 0;
   const int32_t* src = nullptr;
   if (!use_static) {
     src = h->host_view + half * half_ints;
@@ -486,7 +498,8 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
   e = pkd::launch_plan_upload(src + PKD_HEADER_BASE,
                               dev + PKD_HEADER_BASE, layout.off_indices - PKD_HEADER_BASE,
                               kv_indices, dev + layout.off_indices, layout.nnz,
-                              layout.off_first - PKD_HEADER_BASE, item_rows, s);
+                              layout.off_first - PKD_HEADER_BASE, first_rows,
+                              layout.off_items - PKD_HEADER_BASE, item_rows, s);
   if (e != hipSuccess) return hip_fail(e, "plan upload kernel");
   e = hipEventRecord(h->staging_done[half], s);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -631,6 +644,8 @@ int pkd_run_scaled(pkd_handle* h, const void* q, int32_t batch, const void* kv_c
   mp.H = h->Hq;
   mp.o_out = static_cast<uint16_t*>(o);
   mp.lse_out = lse;
+  mp.num_slots = h->num_slots;
+  mp.merge_cap = merge_cap(h);
 
   hipEvent_t* ev = nullptr;
   hipError_t pe = profile_events(h, s, &ev);
@@ -750,8 +765,10 @@ int pkd_run_composable(pkd_handle* prefix, pkd_handle* suffix, const void* q, in
     if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   e = pkd::launch_merge_composable(static_cast<const int32_t*>(prefix->int_ws),
                                    static_cast<const float*>(prefix->float_ws),
+                                   prefix->num_slots, merge_cap(prefix),
                                    static_cast<const int32_t*>(suffix->int_ws),
-                                   static_cast<const float*>(suffix->float_ws), prefix->Hq,
+                                   static_cast<const float*>(suffix->float_ws),
+                                   suffix->num_slots, merge_cap(suffix), prefix->Hq,
                                    static_cast<uint16_t*>(o), lse, prefix->merge_grid, s);
   if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
   for (hipEvent_t* ev : {ep, es})

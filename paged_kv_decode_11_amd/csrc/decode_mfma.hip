@@ -325,16 +325,18 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __re
   const int num_slots = gridDim.x;
   const int32_t* slot_indptr = ws + plan_off_slots();
   const int32_t* first = ws + plan_off_first(num_slots) + 8 * int64_t(blockIdx.x);
-  const int32_t* items = ws + plan_off_items(num_slots);
   const int it_begin = slot_indptr[blockIdx.x];
   const int it_end = slot_indptr[blockIdx.x + 1];
   const int first_req = first[0], first_page = first[1], first_out = first[4],
             first_len = first[5], first_id0 = first[6], first_id1 = first[7];
   const int off_indices = hdr[PKD_H_OFF_INDICES];
   const int partials = hdr[PKD_H_PARTIALS];
+  const int off_items = hdr[PKD_H_OFF_ITEMS];
 
   asm volatile("" ::"s"(it_begin), "s"(it_end), "s"(first_req), "s"(first_page), "s"(first_out),
-               "s"(first_len), "s"(first_id0), "s"(first_id1), "s"(off_indices), "s"(partials));
+               "s"(first_len), "s"(first_id0), "s"(first_id1), "s"(off_indices), "s"(partials),
+               "s"(off_items));
+  const int32_t* items = ws + off_items;
   if ((threadIdx.x & 63) == 0) progress[threadIdx.x >> 6] = 0;
   __syncthreads();
   int done_tiles = 0;

@@ -40,6 +40,10 @@ struct MergeParams {
   int32_t H;
   uint16_t* o_out;     // bf16 [.., H, 128]
   float* lse_out;      // fp32 [.., H] or null
+  // partials mode: the plan's slot count (which fixes the merge list's
+  // offset) and how many merge-list entries the int workspace can hold
+  int32_t num_slots;
+  int32_t merge_cap;
 };
 
 // Decode kernel for group size g and page size P (both must be built):
@@ -79,12 +83,14 @@ int decode_blocks_per_cu_dot2(int waves_per_block);
 // Copy `image_ints` ints (a multiple of 4, 16-byte aligned ends) of a plan
 // image from pinned host memory (device-visible pointer) to the workspace,
 // and `nnz` page ids from `indices` to `dst_indices`, in one kernel.  Words
-// 6 and 7 of each of the `item_rows` 8-int item rows starting at image int
-// `rows_off` receive the page ids of that item's first two pages (its first
-// twice for a one-page item; a row with no pages is left as it is).
+// 6 and 7 of each 8-int item row -- `first_rows` of them from image int
+// `first_off` on and `item_rows` from `items_off` on (both multiples of 8) --
+// receive the page ids of that item's first two pages (its first twice for a
+// one-page item; a row with no pages is left as it is).
 hipError_t launch_plan_upload(const int32_t* image, int32_t* dst, int64_t image_ints,
                               const int32_t* indices, int32_t* dst_indices, int64_t nnz,
-                              int64_t rows_off, int64_t item_rows, hipStream_t stream);
+                              int64_t first_off, int64_t first_rows, int64_t items_off,
+                              int64_t item_rows, hipStream_t stream);
 
 // New tokens' requests and positions, and their K/V rows into the paged
 // cache (append.hip).
@@ -109,9 +115,12 @@ hipError_t launch_append_kv_fp8(const void* k_new, const void* v_new,
 hipError_t launch_merge_partials(const MergeParams& p, int grid, hipStream_t stream);
 // Merge of two all-partials plans' states per request (plan A's first):
 // the composable format's one merge (merge.hip).
-hipError_t launch_merge_composable(const int32_t* ws_a, const float* fws_a, const int32_t* ws_b,
-                                   const float* fws_b, int H, uint16_t* o_out, float* lse_out,
-                                   int grid, hipStream_t stream);
+// (slots_x: plan x's slot count; cap_x: merge-list entries its int
+// workspace can hold)
+hipError_t launch_merge_composable(const int32_t* ws_a, const float* fws_a, int slots_a, int cap_a,
+                                   const int32_t* ws_b, const float* fws_b, int slots_b, int cap_b,
+                                   int H, uint16_t* o_out, float* lse_out, int grid,
+                                   hipStream_t stream);
 // Merge of `k` bf16 states per row, rows laid out uniformly.
 hipError_t launch_merge_states_bf16(const MergeParams& p, hipStream_t stream);
 // Row-wise merge of two bf16 states.

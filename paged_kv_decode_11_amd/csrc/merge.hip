@@ -7,12 +7,14 @@
 // lse = M + log sum_c w_c.  States are merged in a fixed order with no
 // atomics, so results are reproducible (pinghaoyang, Stream-K paragraph).
 //
-// One workgroup (256 lanes) per (row, query head) task, tasks taken in a
-// grid-stride loop so the grid is fixed.  Each of 8 groups of 32 lanes
-// (4 elements of head_dim per lane) folds every 8th state into a running
-// (max, weight sum, weighted o); the group states are then merged, in group
-// order, by the same rule.  Empty states (lse = -inf) get weight 0; a task
-// with only empty states yields o = 0, lse = -inf.
+// Work units are taken in a grid-stride loop so the grid is fixed.  A
+// (row, query head) task of few states is done by 32 lanes in one round trip
+// (merge_small); a task of many plan partials is cut across head_dim over
+// several workgroups (merge_wide); the uniform bf16 merge gives each task a
+// workgroup whose 8 groups of 32 lanes fold every 8th state (merge_task).
+// Every path folds its states in a fixed order, by the rule above, into a
+// running (max, weight sum, weighted o).  Empty states (lse = -inf) get
+// weight 0; a task with only empty states yields o = 0, lse = -inf.
 
 #include <hip/hip_runtime.h>
 
@@ -20,6 +22,7 @@
 
 #include "kernels.h"
 #include "pkd.h"
+#include "plan_layout.h"
 
 namespace pkd {
 namespace {
@@ -190,58 +193,184 @@ __device__ void merge_small(const MergeParams& p, const Task& t, int h, int gl) 
   if (p.lse_out && gl == 0) p.lse_out[t.out_row * p.H + h] = lse;
 }
 
+// A task of many fp32 states, cut across head_dim into kSlices work units of
+// 16 dims, so that one long task (a request split over every slot) spreads
+// over as many workgroups.  Lane l of a unit covers dims 4 (l & 3) .. + 3 of
+// the slice and the states c = (l >> 2) + 64 i: up to kWideRound of them per
+// round trip to memory, all 256 states of a round requested at once.  Each
+// lane folds its states in order into a running (max, weight sum, weighted
+// o); the 16 lanes of a wave that share dims then combine pairwise (lanes
+// 4 and 8, 16, 32 apart, a fixed tree) and the 4 waves in wave order.
+constexpr int kSlices = 8;
+constexpr int kWideRound = 4;
+
+struct Running {
+  float m, s;
+  float4 a;
+};
+
+// x := the merge of states x and y (an empty state has m = -inf, s = 0).
+__device__ __forceinline__ void fold(Running& x, const Running& y) {
+  const float M = fmaxf(x.m, y.m);
+  if (M == kNegInf) return;
+  const float wx = __builtin_amdgcn_exp2f((x.m - M) * kLog2e);  // 0 when x.m = -inf
+  const float wy = __builtin_amdgcn_exp2f((y.m - M) * kLog2e);
+  x.m = M;
+  x.s = wx * x.s + wy * y.s;
+  x.a = make_float4(wx * x.a.x + wy * y.a.x, wx * x.a.y + wy * y.a.y, wx * x.a.z + wy * y.a.z,
+                    wx * x.a.w + wy * y.a.w);
+}
+
+__device__ __forceinline__ Running shfl_xor(const Running& x, int d) {
+  Running y;
+  y.m = __shfl_xor(x.m, d);
+  y.s = __shfl_xor(x.s, d);
+  y.a = make_float4(__shfl_xor(x.a.x, d), __shfl_xor(x.a.y, d), __shfl_xor(x.a.z, d),
+                    __shfl_xor(x.a.w, d));
+  return y;
+}
+
+__device__ void merge_wide(const MergeParams& p, const Task& t, int h, int slice,
+                           Running* wave_state) {
+  const int tid = threadIdx.x;
+  const int piece = tid & 3;
+  const int dim = 16 * slice + 4 * piece;
+  const float* o_in = static_cast<const float*>(p.o_in);
+  Running x = {kNegInf, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+  for (int c0 = tid >> 2; c0 < t.k; c0 += 64 * kWideRound) {
+    float L[kWideRound];
+    float4 v[kWideRound];
+#pragma unroll
+    for (int r = 0; r < kWideRound; ++r) {
+      const int c = c0 + 64 * r;
+      L[r] = kNegInf;
+      v[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c < t.k) {
+        const int64_t st = t.first + c;
+        L[r] = p.lse_in[st * p.lse_stride_c + h];
+        v[r] = load4(o_in + st * p.o_stride_c + int64_t(h) * kHeadDim + dim);
+      }
+    }
+    float mr = x.m;
+#pragma unroll
+    for (int r = 0; r < kWideRound; ++r) mr = fmaxf(mr, L[r]);
+    if (mr == kNegInf) continue;  // only empty states so far
+    const float keep = __builtin_amdgcn_exp2f((x.m - mr) * kLog2e);  // 0 when x.m = -inf
+    x.s *= keep;
+    x.a = make_float4(x.a.x * keep, x.a.y * keep, x.a.z * keep, x.a.w * keep);
+#pragma unroll
+    for (int r = 0; r < kWideRound; ++r) {
+      const float w = __builtin_amdgcn_exp2f((L[r] - mr) * kLog2e);  // 0 for empty states
+      x.s += w;
+      x.a.x = fmaf(w, v[r].x, x.a.x);
+      x.a.y = fmaf(w, v[r].y, x.a.y);
+      x.a.z = fmaf(w, v[r].z, x.a.z);
+      x.a.w = fmaf(w, v[r].w, x.a.w);
+    }
+    x.m = mr;
+  }
+#pragma unroll
+  for (int d = 4; d < 64; d <<= 1) fold(x, shfl_xor(x, d));
+  const int wave = tid >> 6;
+  if ((tid & 63) < 4) wave_state[4 * wave + piece] = x;
+  __syncthreads();
+  if (tid < 4) {
+    Running z = wave_state[piece];
+#pragma unroll
+    for (int w = 1; w < kMergeThreads / 64; ++w) fold(z, wave_state[4 * w + piece]);
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lse = kNegInf;
+    if (z.m != kNegInf) {
+      const float inv = 1.f / z.s;
+      o = make_float4(z.a.x * inv, z.a.y * inv, z.a.z * inv, z.a.w * inv);
+      lse = z.m + __log2f(z.s) * kLn2;
+    }
+    uint2 w;
+    w.x = pack_bf16x2(o.x, o.y);
+    w.y = pack_bf16x2(o.z, o.w);
+    *reinterpret_cast<uint2*>(p.o_out + (t.out_row * p.H + h) * kHeadDim + dim) = w;
+    if (p.lse_out && slice == 0 && piece == 0) p.lse_out[t.out_row * p.H + h] = lse;
+  }
+  __syncthreads();
+}
+
 // Split requests of the current plan: fp32 partials in the float workspace.
 // Tasks (split request e, q head h) = e H + h form blocks of 8.  A block where
 // no task has more than kSmallK states is one work unit: each group of 32
 // lanes does one of its tasks in a single round trip to memory.  The tasks of
-// the other blocks are work units of their own, done with all 256 lanes
-// (merge_task), so a few long tasks still spread over many workgroups.
+// the other blocks are cut into kSlices work units each (merge_wide), so a
+// few long tasks still spread over many workgroups.
+__device__ __forceinline__ Task task_of_entry(const int4 m) {
+  Task t;
+  t.out_row = m.x;
+  t.first = m.y;
+  t.k = m.z;
+  return t;
+}
+
+__device__ __forceinline__ int4 merge_entry(const int32_t* merges, int e) {
+  return *reinterpret_cast<const int4*>(merges + 4 * int64_t(e));
+}
+
 __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(MergeParams p) {
-  __shared__ float grp_m[8];
-  __shared__ float grp_s[8];
-  __shared__ float4 grp_acc[8 * 32];
+  __shared__ Running wave_state[4 * (kMergeThreads / 64)];
   const int32_t* hdr = p.ws + PKD_HEADER_BASE;
-  const int n_split = hdr[PKD_H_SPLIT];
+  const int32_t* merges = p.ws + plan_off_merge(p.num_slots);
   const int H = p.H;
-  const int64_t n_partials = hdr[PKD_H_PARTIALS];
-  const int32_t* merges = p.ws + hdr[PKD_H_OFF_MERGE];
-  MergeParams q = p;
-  q.lse_in = static_cast<const float*>(p.o_in) + n_partials * H * kHeadDim;
-  const int tasks = n_split * H;
-  const int blocks = (tasks + 7) / 8;
   const int grp = threadIdx.x >> 5;
   const int gl = threadIdx.x & 31;
-  auto task_of = [&](int task) {
-    const int e = task / H;
-    Task t;
-    t.out_row = merges[4 * e + 0];
-    t.first = merges[4 * e + 1];
-    t.k = merges[4 * e + 2];
-    return t;
-  };
+  // The merge list sits at an offset fixed by the slot count, so the entry
+  // of this workgroup's first work unit on either pass is requested together
+  // with the header (clamped into the workspace; an entry past the list is
+  // never used) and both are waited for at once.
+  const int b = blockIdx.x;
+  const int last_entry = max(p.merge_cap - 1, 0);
+  const int4 pre_small = merge_entry(merges, min((8 * b + grp) / H, last_entry));
+  // (a vector load, so that it is issued with the other, not after the
+  // header's scalar loads have been waited for)
+  int e_wide = min(b / kSlices / H, last_entry);
+  asm volatile("" : "+v"(e_wide));
+  const int4 pre_wide = merge_entry(merges, e_wide);
+  const int n_split = hdr[PKD_H_SPLIT];
+  const int n_partials = hdr[PKD_H_PARTIALS];
+  const int kmin = hdr[PKD_H_MIN_CHUNKS];
+  const int kmax = hdr[PKD_H_MAX_CHUNKS];
+  asm volatile("" ::"v"(pre_small.x), "v"(pre_small.y), "v"(pre_small.z), "v"(pre_wide.x),
+               "v"(pre_wide.y), "v"(pre_wide.z), "s"(n_split), "s"(n_partials), "s"(kmin),
+               "s"(kmax));
+  MergeParams q = p;
+  q.lse_in = static_cast<const float*>(p.o_in) + int64_t(n_partials) * H * kHeadDim;
+  const int tasks = n_split * H;
+  const int blocks = (tasks + 7) / 8;
   auto small_block = [&](int blk) {
-    int kmax = 0;
+    int most = 0;
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       const int task = 8 * blk + g;
-      if (task < tasks) kmax = max(kmax, merges[4 * (task / H) + 2]);
+      if (task < tasks) most = max(most, merges[4 * (task / H) + 2]);
     }
-    return kmax <= kSmallK;
+    return most <= kSmallK;
   };
   // the plan's fewest and most states per entry tell which passes have work
-  const bool some_small = hdr[PKD_H_MIN_CHUNKS] <= kSmallK;
-  const bool some_large = hdr[PKD_H_MAX_CHUNKS] > kSmallK;
+  const bool some_small = kmin <= kSmallK;
+  const bool some_large = kmax > kSmallK;
   if (some_small) {
-    for (int blk = blockIdx.x; blk < blocks; blk += gridDim.x) {
+    for (int blk = b; blk < blocks; blk += gridDim.x) {
       if (some_large && !small_block(blk)) continue;
       const int task = 8 * blk + grp;
-      if (task < tasks) merge_small(q, task_of(task), task % H, gl);
+      if (task < tasks) {
+        const int4 m = blk == b ? pre_small : merge_entry(merges, task / H);
+        merge_small(q, task_of_entry(m), task % H, gl);
+      }
     }
   }
   if (some_large) {
-    for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+    const int units = tasks * kSlices;
+    for (int u = b; u < units; u += gridDim.x) {
+      const int task = u / kSlices;
       if (some_small && small_block(task / 8)) continue;
-      merge_task<float>(q, task_of(task), task % H, grp_m, grp_s, grp_acc);
+      const int4 m = u == b ? pre_wide : merge_entry(merges, task / H);
+      merge_wide(q, task_of_entry(m), task % H, u % kSlices, wave_state);
     }
   }
 }
@@ -346,27 +475,39 @@ __device__ void merge_segments(const Segment& a, const Segment& b, int H, int h,
 }
 
 __global__ __launch_bounds__(kMergeThreads) void merge_composable_kernel(
-    const int32_t* __restrict__ ws_a, const float* __restrict__ fws_a,
-    const int32_t* __restrict__ ws_b, const float* __restrict__ fws_b, int H,
-    uint16_t* __restrict__ o_out, float* __restrict__ lse_out) {
+    const int32_t* __restrict__ ws_a, const float* __restrict__ fws_a, int slots_a, int cap_a,
+    const int32_t* __restrict__ ws_b, const float* __restrict__ fws_b, int slots_b, int cap_b,
+    int H, uint16_t* __restrict__ o_out, float* __restrict__ lse_out) {
   __shared__ float grp_m[8];
   __shared__ float grp_s[8];
   __shared__ float4 grp_acc[8 * 32];
   const int32_t* ha = ws_a + PKD_HEADER_BASE;
   const int32_t* hb = ws_b + PKD_HEADER_BASE;
+  const int32_t* ma = ws_a + plan_off_merge(slots_a);
+  const int32_t* mb = ws_b + plan_off_merge(slots_b);
+  // this workgroup's first entry of both lists, requested with the headers
+  // (clamped into each workspace; unused when past the lists)
+  const int e0 = int(blockIdx.x) / H;
+  const int4 pre_a = merge_entry(ma, min(e0, max(cap_a - 1, 0)));
+  const int4 pre_b = merge_entry(mb, min(e0, max(cap_b - 1, 0)));
+  const int split_a = ha[PKD_H_SPLIT], split_b = hb[PKD_H_SPLIT];
+  const int parts_a = ha[PKD_H_PARTIALS], parts_b = hb[PKD_H_PARTIALS];
+  asm volatile("" ::"s"(pre_a.x), "s"(pre_a.y), "s"(pre_a.z), "s"(pre_b.y), "s"(pre_b.z),
+               "s"(split_a), "s"(split_b), "s"(parts_a), "s"(parts_b));
   // both lists name every request in order (checked on the host)
-  const int n = min(ha[PKD_H_SPLIT], hb[PKD_H_SPLIT]);
-  const int32_t* ma = ws_a + ha[PKD_H_OFF_MERGE];
-  const int32_t* mb = ws_b + hb[PKD_H_OFF_MERGE];
-  const float* lse_a = fws_a + int64_t(ha[PKD_H_PARTIALS]) * H * kHeadDim;
-  const float* lse_b = fws_b + int64_t(hb[PKD_H_PARTIALS]) * H * kHeadDim;
+  const int n = min(split_a, split_b);
+  const float* lse_a = fws_a + int64_t(parts_a) * H * kHeadDim;
+  const float* lse_b = fws_b + int64_t(parts_b) * H * kHeadDim;
   const int64_t tasks = int64_t(n) * H;
   for (int64_t task = blockIdx.x; task < tasks; task += gridDim.x) {
     const int e = int(task / H);
     const int h = int(task - int64_t(e) * H);
-    const Segment a = {fws_a, lse_a, ma[4 * e + 1], ma[4 * e + 2]};
-    const Segment b = {fws_b, lse_b, mb[4 * e + 1], mb[4 * e + 2]};
-    merge_segments(a, b, H, h, ma[4 * e], o_out, lse_out, grp_m, grp_s, grp_acc);
+    const bool first = task == blockIdx.x;
+    const int4 xa = first ? pre_a : merge_entry(ma, e);
+    const int4 xb = first ? pre_b : merge_entry(mb, e);
+    const Segment a = {fws_a, lse_a, xa.y, xa.z};
+    const Segment b = {fws_b, lse_b, xb.y, xb.z};
+    merge_segments(a, b, H, h, xa.x, o_out, lse_out, grp_m, grp_s, grp_acc);
   }
 }
 
@@ -424,11 +565,12 @@ hipError_t launch_merge_partials(const MergeParams& p, int grid, hipStream_t str
   return hipGetLastError();
 }
 
-hipError_t launch_merge_composable(const int32_t* ws_a, const float* fws_a, const int32_t* ws_b,
-                                   const float* fws_b, int H, uint16_t* o_out, float* lse_out,
-                                   int grid, hipStream_t stream) {
+hipError_t launch_merge_composable(const int32_t* ws_a, const float* fws_a, int slots_a, int cap_a,
+                                   const int32_t* ws_b, const float* fws_b, int slots_b, int cap_b,
+                                   int H, uint16_t* o_out, float* lse_out, int grid,
+                                   hipStream_t stream) {
   hipLaunchKernelGGL(merge_composable_kernel, dim3(grid), dim3(kMergeThreads), 0, stream, ws_a,
-                     fws_a, ws_b, fws_b, H, o_out, lse_out);
+                     fws_a, slots_a, cap_a, ws_b, fws_b, slots_b, cap_b, H, o_out, lse_out);
   return hipGetLastError();
 }
 

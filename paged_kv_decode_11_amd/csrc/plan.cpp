@@ -90,9 +90,8 @@ int64_t max_partials_shared(int64_t max_requests, int64_t num_slots, int64_t num
 
 int64_t plan_image_ints(int64_t num_slots, int64_t num_items, int64_t n_merge,
                         int64_t num_groups) {
-  int64_t off_items = plan_off_items(num_slots);
-  int64_t off_merge = off_items + 8 * num_items;
-  return align_up(off_merge + 4 * n_merge + 4 * num_groups, 32);
+  const int64_t off_items = plan_off_items(num_slots, n_merge);
+  return align_up(off_items + 8 * num_items + 4 * num_groups, 32);
 }
 
 int plan_validate(const PlanInput& in, std::string* err) {
@@ -215,9 +214,9 @@ int plan_measure(const PlanInput& in, PlanScratch& s, PlanLayout* layout, std::s
   layout->rows_per_block = int32_t(tq);
   layout->off_slots = plan_off_slots();
   layout->off_first = plan_off_first(S);
-  layout->off_items = plan_off_items(S);
-  layout->off_merge = layout->off_items + 8 * I;
-  layout->off_groups = layout->off_merge + 4 * n_merge;
+  layout->off_merge = plan_off_merge(S);
+  layout->off_items = plan_off_items(S, n_merge);
+  layout->off_groups = layout->off_items + 8 * I;
   layout->off_indices = align_up(layout->off_groups + 4 * n_groups, 32);
   layout->nnz = in.indptr[in.batch];
   layout->total_tokens = total;

@@ -117,11 +117,11 @@ __device__ __forceinline__ void prefix_body(
 
   const int32_t* hdr = ws + PKD_HEADER_BASE;
   const int32_t* slot_indptr = ws + plan_off_slots();
-  const int32_t* items = ws + plan_off_items(num_slots);
   const int off_indices = hdr[PKD_H_OFF_INDICES];
   const int off_groups = hdr[PKD_H_OFF_GROUPS];
   const int rows_per_block = hdr[PKD_H_ROWS_PER_BLOCK];
   const int partials = hdr[PKD_H_PARTIALS];
+  const int32_t* items = ws + hdr[PKD_H_OFF_ITEMS];
   const int32_t* kv_idx = ws + off_indices;
   const int32_t* groups = ws + off_groups;
   const int Hq = num_qo_heads;

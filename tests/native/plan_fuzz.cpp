@@ -175,7 +175,10 @@ void check_image(const Case& c, const pkd::PlanLayout& L, const int32_t* img) {
   const int32_t* slots = img + pkd::plan_off_slots();
   EXPECT(slots[0] == 0 && slots[S] == I, "slot_indptr ends %d %d (I=%d)", slots[0], slots[S], I);
   for (int32_t s = 0; s < S; ++s) EXPECT(slots[s] <= slots[s + 1], "slot_indptr decreases at %d", s);
-  const int32_t* items = img + pkd::plan_off_items(S);
+  EXPECT(h[PKD_H_OFF_MERGE] == pkd::plan_off_merge(S), "merge list offset %d", h[PKD_H_OFF_MERGE]);
+  EXPECT(h[PKD_H_OFF_ITEMS] == pkd::plan_off_items(S, h[PKD_H_SPLIT]), "items offset %d",
+         h[PKD_H_OFF_ITEMS]);
+  const int32_t* items = img + h[PKD_H_OFF_ITEMS];
   const int32_t* first = img + pkd::plan_off_first(S);
   for (int32_t s = 0; s < S; ++s)
     for (int f = 0; f < 8; ++f)

@@ -66,13 +66,15 @@ def _lengths_ok(p, P):
 
 
 def _first_items_ok(p):
-    """The fixed offsets the kernels compute from the slot count, and the
-    first-item table: slot s's first item again, zeros for an empty slot."""
+    """The fixed offsets the kernels compute from the slot count (slots, the
+    first-item table and the merge list), the items right after the merge
+    list, and the first-item table: slot s's first item again, zeros for an empty slot."""
     h, img = p["header"], p["image"]
     S = h["SLOTS"]
     assert h["OFF_SLOTS"] == 64
     assert h["OFF_FIRST"] == -(-(64 + S + 1) // 8) * 8
-    assert h["OFF_ITEMS"] == h["OFF_FIRST"] + 8 * S
+    assert h["OFF_MERGE"] == h["OFF_FIRST"] + 8 * S
+    assert h["OFF_ITEMS"] == -(-(h["OFF_MERGE"] + 4 * h["SPLIT"]) // 8) * 8
     items8 = img[h["OFF_ITEMS"]: h["OFF_ITEMS"] + 8 * h["ITEMS"]].reshape(-1, 8)
     ind = p["slot_indptr"]
     for s in range(S):
@@ -102,7 +104,7 @@ def test_plan_host_matches_oracle_bit_exact(S, seed):
     _compare(p_lib, p_ref)
     _lengths_ok(p_lib, P)
     h = p_lib["header"]
-    assert h["MAGIC"] == 0x31444B50 and h["VERSION"] == 2 and h["BATCH"] == B
+    assert h["MAGIC"] == 0x31444B50 and h["VERSION"] == 3 and h["BATCH"] == B
     assert h["FLAGS"] == (_lib.PKD_PLAN_ALL_PARTIALS if opts.get("all_partials") else 0)
     if opts.get("all_partials"):
         assert p_lib["n_split"] == B and p_lib["merges"][:, 0].tolist() == list(range(B))

@@ -55,17 +55,19 @@ def test_device_plan_image():
     dev = r.int_workspace.view(torch.int32)[: img.size].cpu().numpy()
     h = host["header"]
     gu.say("plan image", "ints", img.size, "items", h["ITEMS"], "slots", h["SLOTS"])
-    lo, hi = h["OFF_FIRST"], h["OFF_MERGE"]
-    assert hi - lo == 8 * (h["SLOTS"] + h["ITEMS"])
+    # item rows: the first-item table, then the items (after the merge list)
+    row_ints = np.concatenate([
+        np.arange(h["OFF_FIRST"], h["OFF_FIRST"] + 8 * h["SLOTS"]),
+        np.arange(h["OFF_ITEMS"], h["OFF_ITEMS"] + 8 * h["ITEMS"])])
     plan_id = _lib.HEADER_BASE + _lib.H["PLAN_ID"]
     same = np.ones(img.size, dtype=bool)
     same[: _lib.HEADER_BASE] = False  # device-only words
     same[plan_id] = False
-    rows = np.arange(lo, hi).reshape(-1, 8)
+    rows = row_ints.reshape(-1, 8)
     same[rows[:, 6:].ravel()] = False
     assert np.array_equal(dev[same], img[same])
     assert dev[plan_id] == r.plan_id
-    fields = dev[lo:hi].reshape(-1, 8)
+    fields = dev[row_ints].reshape(-1, 8)
     kv = batch.kv_indices.astype(np.int64)
     for row, f in enumerate(fields):
         if f[2] == 0:  # a slot without items
