@@ -190,7 +190,7 @@ __device__ __forceinline__ FRef f_ref(const FCtx& c, const FIds& ids, int s, int
   return r;
 }
 
-__device__ __forceinline__ void f_load(FStep& d, const FCtx& c, const FRef& r) {
+__device__ __forceinline__ void f_load_k(FStep& d, const FCtx& c, const FRef& r) {
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -199,6 +199,9 @@ __device__ __forceinline__ void f_load(FStep& d, const FCtx& c, const FRef& r) {
                                                            kBufferNontemporal);
       d.k[h][i] = make_uint4(w[0], w[1], w[2], w[3]);
     }
+}
+
+__device__ __forceinline__ void f_load_v(FStep& d, const FCtx& c, const FRef& r) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const auto w = __builtin_amdgcn_raw_buffer_load_b128(
@@ -206,6 +209,11 @@ __device__ __forceinline__ void f_load(FStep& d, const FCtx& c, const FRef& r) {
         kBufferNontemporal);
     d.v[i] = make_uint4(w[0], w[1], w[2], w[3]);
   }
+}
+
+__device__ __forceinline__ void f_load(FStep& d, const FCtx& c, const FRef& r) {
+  f_load_k(d, c, r);
+  f_load_v(d, c, r);
 }
 
 template <int G>
@@ -216,8 +224,9 @@ struct FState {
 };
 
 // One 32-token step.  With kPrefetch a later step's loads are issued into
-// `nxt` once this step's V is in LDS and its K has gone through the matrix
-// cores, so `nxt` may be `cur` (the two-step ring); the last step (kLast)
+// `nxt`, its V once this step's V is in LDS and its K once this step's K has
+// gone through the matrix cores, so `nxt` may be `cur` (the two-step ring);
+// the last step (kLast)
 // masks tokens >= valid: their logits to -inf and their V rows to zero (a
 // slot past the sequence may hold any code).
 template <int G, bool kPrefetch, bool kLast>
@@ -242,6 +251,11 @@ __device__ __forceinline__ void f_step(FState<G>& st, const FStep& cur, FStep& n
       *reinterpret_cast<uint4*>(vb + (16 * (i & 1) + 4 * (i >> 1)) * kVRowBytes) = w;
     }
   }
+  if constexpr (kPrefetch) {
+    __builtin_amdgcn_sched_barrier(0);
+    f_load_v(nxt, c, next);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   // S^T for both halves: A = K rows, B = Q^T; MFMA j takes head dims
   // 64 (j >> 1) + 16 kg + 8 (j & 1) .. + 7 at contraction slots 8 kg ..
@@ -259,7 +273,7 @@ __device__ __forceinline__ void f_step(FState<G>& st, const FStep& cur, FStep& n
   }
   if constexpr (kPrefetch) {
     __builtin_amdgcn_sched_barrier(0);
-    f_load(nxt, c, next);
+    f_load_k(nxt, c, next);
     __builtin_amdgcn_sched_barrier(0);
   }
 
