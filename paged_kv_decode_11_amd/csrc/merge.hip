@@ -9,9 +9,10 @@
 //
 // Work units are taken in a grid-stride loop so the grid is fixed.  A
 // (row, query head) task of few states is done by 32 lanes in one round trip
-// (merge_small); a task of many plan partials is cut across head_dim over
-// several workgroups (merge_wide); the uniform bf16 merge gives each task a
-// workgroup whose 8 groups of 32 lanes fold every 8th state (merge_task).
+// (merge_small); a task of more states by a workgroup whose 8 groups of 32
+// lanes fold every 8th state (merge_task, also the uniform bf16 merge); in a
+// plan with a task above 64 states, each task of more than a few is cut
+// across head_dim over several workgroups (merge_wide).
 // Every path folds its states in a fixed order, by the rule above, into a
 // running (max, weight sum, weighted o).  Empty states (lse = -inf) get
 // weight 0; a task with only empty states yields o = 0, lse = -inf.
@@ -298,8 +299,10 @@ __device__ void merge_wide(const MergeParams& p, const Task& t, int h, int slice
 // Tasks (split request e, q head h) = e H + h form blocks of 8.  A block where
 // no task has more than kSmallK states is one work unit: each group of 32
 // lanes does one of its tasks in a single round trip to memory.  The tasks of
-// the other blocks are cut into kSlices work units each (merge_wide), so a
-// few long tasks still spread over many workgroups.
+// the other blocks are work units of their own, done with all 256 lanes
+// (merge_task, one round trip up to 64 states), or, when some task of the
+// plan has more than 64 states, cut into kSlices work units each
+// (merge_wide), so a few long tasks still spread over many workgroups.
 __device__ __forceinline__ Task task_of_entry(const int4 m) {
   Task t;
   t.out_row = m.x;
@@ -314,6 +317,9 @@ __device__ __forceinline__ int4 merge_entry(const int32_t* merges, int e) {
 
 __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(MergeParams p) {
   __shared__ Running wave_state[4 * (kMergeThreads / 64)];
+  __shared__ float grp_m[8];
+  __shared__ float grp_s[8];
+  __shared__ float4 grp_acc[8 * 32];
   const int32_t* hdr = p.ws + PKD_HEADER_BASE;
   const int32_t* merges = p.ws + plan_off_merge(p.num_slots);
   const int H = p.H;
@@ -326,18 +332,22 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(MergePara
   const int b = blockIdx.x;
   const int last_entry = max(p.merge_cap - 1, 0);
   const int4 pre_small = merge_entry(merges, min((8 * b + grp) / H, last_entry));
-  // (a vector load, so that it is issued with the other, not after the
-  // header's scalar loads have been waited for)
+  // The large-task pass takes a task per unit or cuts each task into
+  // kSlices units (which, the header tells); the entry of unit b either way.
+  // (Vector loads, so that they are issued with the others, not after the
+  // header's scalar loads have been waited for.)
+  int e_one = min(b / H, last_entry);
   int e_wide = min(b / kSlices / H, last_entry);
-  asm volatile("" : "+v"(e_wide));
+  asm volatile("" : "+v"(e_one), "+v"(e_wide));
+  const int4 pre_one = merge_entry(merges, e_one);
   const int4 pre_wide = merge_entry(merges, e_wide);
   const int n_split = hdr[PKD_H_SPLIT];
   const int n_partials = hdr[PKD_H_PARTIALS];
   const int kmin = hdr[PKD_H_MIN_CHUNKS];
   const int kmax = hdr[PKD_H_MAX_CHUNKS];
-  asm volatile("" ::"v"(pre_small.x), "v"(pre_small.y), "v"(pre_small.z), "v"(pre_wide.x),
-               "v"(pre_wide.y), "v"(pre_wide.z), "s"(n_split), "s"(n_partials), "s"(kmin),
-               "s"(kmax));
+  asm volatile("" ::"v"(pre_small.x), "v"(pre_small.y), "v"(pre_small.z), "v"(pre_one.x),
+               "v"(pre_one.y), "v"(pre_one.z), "v"(pre_wide.x), "v"(pre_wide.y), "v"(pre_wide.z),
+               "s"(n_split), "s"(n_partials), "s"(kmin), "s"(kmax));
   MergeParams q = p;
   q.lse_in = static_cast<const float*>(p.o_in) + int64_t(n_partials) * H * kHeadDim;
   const int tasks = n_split * H;
@@ -365,12 +375,19 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(MergePara
     }
   }
   if (some_large) {
-    const int units = tasks * kSlices;
+    // up to 8 * kRound states a task is one round trip for one workgroup;
+    // past that (a plan with a request cut into more chunks) every large
+    // task is cut across head_dim
+    const int slices = kmax > 8 * kRound ? kSlices : 1;
+    const int units = tasks * slices;
     for (int u = b; u < units; u += gridDim.x) {
-      const int task = u / kSlices;
+      const int task = u / slices;
       if (some_small && small_block(task / 8)) continue;
-      const int4 m = u == b ? pre_wide : merge_entry(merges, task / H);
-      merge_wide(q, task_of_entry(m), task % H, u % kSlices, wave_state);
+      const int4 m = u != b ? merge_entry(merges, task / H) : slices == 1 ? pre_one : pre_wide;
+      if (slices == 1)
+        merge_task<float>(q, task_of_entry(m), task % H, grp_m, grp_s, grp_acc);
+      else
+        merge_wide(q, task_of_entry(m), task % H, u % kSlices, wave_state);
     }
   }
 }

@@ -130,24 +130,26 @@ def test_merge_long_and_short_entries_across_replays():
         del g
 
 
+@pytest.mark.parametrize("longest", [300, 64, 40])
 @pytest.mark.parametrize("Hq,Hkv", [(32, 8), (4, 1), (8, 8)])
-def test_merge_mixed_entries(Hq, Hkv):
+def test_merge_mixed_entries(Hq, Hkv, longest):
     """One plan whose merge list holds entries of a few states (one round
-    trip by 32 lanes) and of many (cut across head_dim over several
-    workgroups); with 4 or 8 query heads a block of 8 tasks spans several
-    entries, short and long ones together."""
+    trip by 32 lanes) and of more: one workgroup per task while no entry has
+    more than 64 states, else cut across head_dim over several workgroups;
+    with 4 or 8 query heads a block of 8 tasks spans several entries, short
+    and long ones together."""
     import torch
     import paged_kv_decode_11_amd as pkd
 
     P = 16
     pool = 1200
-    rng = np.random.default_rng(57 + Hq)
-    lens = [300 * P, 10 * P, 3 * P + 2, 40 * P - 7, 17 * P, 16 * P, 5, 1]
+    rng = np.random.default_rng(57 + Hq + longest)
+    lens = [longest * P, 10 * P, 3 * P + 2, 40 * P - 7, 17 * P, 16 * P, 5, 1]
     b = workloads.make_batch(lens, P, pool, Hq, Hkv, 128, rng)
     cache = workloads.host_cache(b, rng, poison=True)
     q = workloads.normal_bf16(rng, (len(lens), Hq, 128))
     r = pkd.DecodePlanRun(max_batch=1024, max_nnz=pool, max_qo_heads=Hq)
-    gu.say("merge mixed entries", Hq, Hkv)
+    gu.say("merge mixed entries", Hq, Hkv, longest)
     r.plan(b.kv_indptr, torch.from_numpy(b.kv_indices).cuda(), b.kv_last_page_len, Hq, Hkv, 128,
            P, fixed_chunk_pages=1)
     o, lse = r.run(gu.bits_to_dev(q), gu.bits_to_dev(cache), return_lse=True)
