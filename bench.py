@@ -25,6 +25,7 @@ layer 0's requests.  Inputs are synthetic and seeded.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import math
@@ -793,6 +794,11 @@ def target_summary(line: dict) -> dict:
 
 def main():
     args = parse()
+    # No cyclic garbage collection while timing (as timeit does): a pass over
+    # torch's and numpy's objects in the middle of a timed loop stalls the host
+    # for milliseconds, and with it the GPU of a plan-per-step loop.  Objects
+    # are still freed by reference counting; workloads collect in between.
+    gc.disable()
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
         return
@@ -806,8 +812,6 @@ def main():
     if args.workload == "append":
         bench_append(args)
         return
-    import gc
-
     line = bench_decode(args, args.workload, args.cpu_seconds, placement=args.placement)
     w = args.workload
     if w in TARGET_FRAC:
