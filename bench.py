@@ -38,6 +38,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+# per-chunk weight (in tokens) of the shared-prefix workload's suffix plan
+SUFFIX_ALPHA = 32
 ROTATE_BYTES = 2 << 30  # single-layer workloads rotate caches to >= 2 GiB
 METRIC = "paged GQA decode: achieved KV GB/s (% of HBM peak) and µs/layer-step"
 
@@ -351,8 +353,11 @@ def bench_shared_prefix(args):
     def plan2():
         rp.plan(qo, kv_indptr, idx_pre, prefix.kv_last_page_len[:1], H, main.num_kv_heads, 128, 16,
                 all_partials=True, **pre_opts)
+        # alpha = 32: each chunk weighs 32 tokens on top of its own in the
+        # slot assignment, so that no slot gets three of the short suffix
+        # chunks (the launch's last workgroup) while most get one
         rs.plan(suffix.kv_indptr, idx_suf, suffix.kv_last_page_len, H, main.num_kv_heads, 128, 16,
-                all_partials=True)
+                all_partials=True, alpha=SUFFIX_ALPHA)
 
     def run2():
         for j in range(R):
@@ -372,7 +377,8 @@ def bench_shared_prefix(args):
     def plan5():
         rp5.plan(qo, kv_indptr, idx_pre, prefix.kv_last_page_len[:1], H, main.num_kv_heads, 128,
                  16, **pre_opts)
-        rs5.plan(suffix.kv_indptr, idx_suf, suffix.kv_last_page_len, H, main.num_kv_heads, 128, 16)
+        rs5.plan(suffix.kv_indptr, idx_suf, suffix.kv_last_page_len, H, main.num_kv_heads, 128, 16,
+                 alpha=SUFFIX_ALPHA)
 
     def run5():
         for j in range(R):
