@@ -164,6 +164,9 @@ def test_random_batches_many_splits(variant):
         _check(batch, q, cache, f"random{trial}-{variant}", variant=variant)
         _check(batch, q, cache, f"random{trial}-{variant}-mct16", min_chunk_tokens=16,
                variant=variant)
+        # other cost weights change only which slot takes which chunk
+        _check(batch, q, cache, f"random{trial}-{variant}-a40b3", min_chunk_tokens=16, alpha=40,
+               beta=3, variant=variant)
 
 
 @pytest.mark.parametrize("variant", VARIANTS)

@@ -202,7 +202,7 @@ def _plan_both(rp, rs, gb, sb, qo, P, Hq, Hkv, popts=None, sopts=None):
 
 
 @pytest.mark.parametrize("side_by_side", [False, True])
-@pytest.mark.parametrize("case", range(6))
+@pytest.mark.parametrize("case", range(7))
 def test_run_composable(case, side_by_side):
     """Prefix groups and per-request suffixes in one call against the
     oracle's merge of the two exact states; unsplit and split on either side,
@@ -220,6 +220,8 @@ def test_run_composable(case, side_by_side):
         (64, 8, 8, [9, 3], [700, 64], {}, {"fixed_chunk_pages": 3}),
         (16, 16, 2, [33], [5000], {}, {"min_chunk_tokens": 16}),
         (16, 32, 8, [2, 2, 2, 2], [16, 32, 48, 1], {"fixed_chunk_pages": 1}, {}),
+        # the suffix plan weighing each chunk 32 tokens more (as the benchmark does)
+        (16, 32, 8, [32], [4096], {}, {"alpha": 32}),
     ][case]
     B = int(sum(rows))
     rng = np.random.default_rng(600 + case)
