@@ -97,12 +97,13 @@ enum { PKD_PLAN_ALL_PARTIALS = 1 };
  * in where q.k is evaluated. */
 enum {
   PKD_VARIANT_AUTO = 0,    /* by measurement: PKD_VARIANT_MFMA_PV for group size 8, pages
-                              below 16 tokens or fewer than 768 KV tokens per slot,
-                              PKD_VARIANT_MFMA otherwise */
-  PKD_VARIANT_DOT2 = 1,    /* q.k with packed bf16 dot products on the vector ALUs */
+                              below 16 tokens or fewer than 768 KV tokens per slot, and for
+                              group sizes 3, 5, 6, 7; PKD_VARIANT_MFMA otherwise */
+  PKD_VARIANT_DOT2 = 1,    /* q.k with packed bf16 dot products on the vector ALUs (group
+                              size 1, 2, 4 or 8) */
   PKD_VARIANT_MFMA = 2,    /* q.k as a 16 x 16 tile on the matrix cores (GQA group as rows),
-                              p.v on the vector ALUs */
-  PKD_VARIANT_MFMA_PV = 3  /* both q.k and p.v on the matrix cores */
+                              p.v on the vector ALUs (group size 1, 2, 4 or 8) */
+  PKD_VARIANT_MFMA_PV = 3  /* both q.k and p.v on the matrix cores (group sizes 1 to 8) */
 };
 
 /* ---------------------------------------------------------------------
@@ -241,7 +242,8 @@ size_t pkd_host_workspace_bytes(int32_t max_batch, int32_t num_slots);
  * together with kv_indices.  kv_indptr and kv_last_page_len are host arrays read during the
  * call; kv_indices is a device array the caller may reuse once `stream` has
  * passed this call.  Built: bf16 q, PKD_LAYOUT_NHD, head_dim 128,
- * num_qo_heads / num_kv_heads in {1, 2, 4, 8}, and either a bf16 cache with
+ * num_qo_heads / num_kv_heads from 1 to 8 (PKD_VARIANT_DOT2 and
+ * PKD_VARIANT_MFMA: 1, 2, 4 or 8), and either a bf16 cache with
  * page_size in {1, 2, 4, 8, 16, 32, 64} or an FP8 E4M3 cache
  * (kv_dtype PKD_DTYPE_FP8_E4M3, matrix-core variant only) with page_size in
  * {16, 32, 64}; else PKD_ERR_UNSUPPORTED.  Rejects (PKD_ERR_INVALID_ARG)

@@ -153,12 +153,12 @@ int check_shapes(int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t q_dtype,
   if (kv_dtype == PKD_DTYPE_FP8_E4M3) {
     if (!pkd::fp8_variant_built(Hq / Hkv, P))
       return fail(PKD_ERR_UNSUPPORTED,
-                  "an fp8 e4m3 cache is built for group size 1, 2, 4 or 8 and page_size 16, 32 or 64");
+                  "an fp8 e4m3 cache is built for group sizes 1 to 8 and page_size 16, 32 or 64");
     return PKD_OK;
   }
-  if (!pkd::decode_variant_built(Hq / Hkv, P))
+  if (!pkd::decode_variant_built(Hq / Hkv, P) && !pkd::pv_variant_built(Hq / Hkv, P))
     return fail(PKD_ERR_UNSUPPORTED,
-                "group size must be 1, 2, 4 or 8 and page_size 1, 2, 4, 8, 16, 32 or 64");
+                "group size must be 1 to 8 and page_size 1, 2, 4, 8, 16, 32 or 64");
   return PKD_OK;
 }
 
@@ -404,10 +404,14 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
   if (variant == PKD_VARIANT_MFMA_PV &&
       (kv_dtype != PKD_DTYPE_BF16 || !pkd::pv_variant_built(num_qo_heads / num_kv_heads, page_size)))
     return fail(PKD_ERR_UNSUPPORTED,
-                "the PKD_VARIANT_MFMA_PV kernel is built for a bf16 cache and group size 1, 2, 4 "
-                "or 8");
+                "the PKD_VARIANT_MFMA_PV kernel is built for a bf16 cache and group sizes 1 to 8");
   if (variant == PKD_VARIANT_DOT2 && kv_dtype == PKD_DTYPE_FP8_E4M3)
     return fail(PKD_ERR_UNSUPPORTED, "an fp8 e4m3 cache has only the matrix-core kernel");
+  if ((variant == PKD_VARIANT_DOT2 || variant == PKD_VARIANT_MFMA) &&
+      kv_dtype == PKD_DTYPE_BF16 && !pkd::decode_variant_built(num_qo_heads / num_kv_heads, page_size))
+    return fail(PKD_ERR_UNSUPPORTED,
+                "the PKD_VARIANT_DOT2 and PKD_VARIANT_MFMA kernels are built for group size 1, 2, 4 "
+                "or 8");
 
   DeviceGuard guard(h->device);
   if (!guard.ok) return hip_fail(guard.err, "hipSetDevice");
@@ -524,13 +528,14 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
   // dot-product kernel) and where each slot has little work (skewed batch,
   // about 520 tokens per slot: 87.8 vs 92.1 us); with about 1,000 tokens per
   // slot and smaller groups the q.k-only matrix-core kernel streams faster
-  // (Llama-3-8B-like layer: 156.1 vs 160.8 us).  An FP8 cache has its own
-  // kernel.
+  // (Llama-3-8B-like layer: 156.1 vs 160.8 us).  Group sizes 3, 5, 6 and 7
+  // are built for the P.V kernel only.  An FP8 cache has its own kernel.
   if (variant == PKD_VARIANT_AUTO) {
     const int g = num_qo_heads / num_kv_heads;
     const int64_t tokens_per_slot = layout.total_tokens / h->num_slots;
     const bool pv = kv_dtype == PKD_DTYPE_BF16 && pkd::pv_variant_built(g, page_size) &&
-                    (g == 8 || page_size < 16 || tokens_per_slot < kPvMaxTokensPerSlot);
+                    (g == 8 || page_size < 16 || tokens_per_slot < kPvMaxTokensPerSlot ||
+                     !pkd::decode_variant_built(g, page_size));
     h->variant = pv ? PKD_VARIANT_MFMA_PV : PKD_VARIANT_MFMA;
   } else {
     h->variant = variant;

@@ -554,7 +554,7 @@ hipError_t launch_fg(const DecodeParams& p, int page_size, int num_slots, hipStr
 }  // namespace
 
 bool fp8_variant_built(int g, int page_size) {
-  return (g == 1 || g == 2 || g == 4 || g == 8) &&
+  return g >= 1 && g <= 8 &&
          (page_size == 16 || page_size == 32 || page_size == 64);
 }
 
@@ -563,7 +563,11 @@ hipError_t launch_decode_fp8(const DecodeParams& p, int g, int page_size, int nu
   switch (g) {
     case 1: return launch_fg<1>(p, page_size, num_slots, stream);
     case 2: return launch_fg<2>(p, page_size, num_slots, stream);
+    case 3: return launch_fg<3>(p, page_size, num_slots, stream);
     case 4: return launch_fg<4>(p, page_size, num_slots, stream);
+    case 5: return launch_fg<5>(p, page_size, num_slots, stream);
+    case 6: return launch_fg<6>(p, page_size, num_slots, stream);
+    case 7: return launch_fg<7>(p, page_size, num_slots, stream);
     case 8: return launch_fg<8>(p, page_size, num_slots, stream);
     default: return hipErrorInvalidValue;
   }

@@ -51,7 +51,7 @@ hipError_t launch_vg(const DecodeParams& p, int page_size, int num_slots, hipStr
 }  // namespace
 
 bool pv_variant_built(int g, int page_size) {
-  return (g == 1 || g == 2 || g == 4 || g == 8) &&
+  return g >= 1 && g <= 8 &&
          (page_size == 1 || page_size == 2 || page_size == 4 || page_size == 8 ||
           page_size == 16 || page_size == 32 || page_size == 64);
 }
@@ -61,7 +61,11 @@ hipError_t launch_decode_pv(const DecodeParams& p, int g, int page_size, int num
   switch (g) {
     case 1: return launch_vg<1>(p, page_size, num_slots, stream);
     case 2: return launch_vg<2>(p, page_size, num_slots, stream);
+    case 3: return launch_vg<3>(p, page_size, num_slots, stream);
     case 4: return launch_vg<4>(p, page_size, num_slots, stream);
+    case 5: return launch_vg<5>(p, page_size, num_slots, stream);
+    case 6: return launch_vg<6>(p, page_size, num_slots, stream);
+    case 7: return launch_vg<7>(p, page_size, num_slots, stream);
     case 8: return launch_vg<8>(p, page_size, num_slots, stream);
     default: return hipErrorInvalidValue;
   }

@@ -235,3 +235,36 @@ def test_auto_variant_by_shape():
         assert big.planned_variant == want, (per_slot, Hq, big.planned_variant)
     r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, 8, 8, 128, 16, variant="dot2")
     assert r.planned_variant == "dot2"
+
+
+@pytest.mark.parametrize("P", [1, 4, 16, 32, 64])
+@pytest.mark.parametrize("G,Hkv", [(3, 2), (5, 8), (6, 4), (7, 4)])
+def test_other_group_sizes(P, G, Hkv):
+    """Group sizes 3, 5, 6 and 7 (Hq = 28 over Hkv = 4 is a common model
+    shape), built for the kernel with both products on the matrix cores,
+    which the default picks for them; unsplit and split."""
+    lens = [1, 2, P, P + 1, 37, 333, 1500] if P > 1 else [1, 2, 3, 37, 333, 700]
+    batch, q, cache = _small(900 + 10 * G + P, lens, P, G * Hkv, Hkv)
+    _check(batch, q, cache, f"P{P}-G{G}-Hkv{Hkv}")
+    _check(batch, q, cache, f"P{P}-G{G}-Hkv{Hkv}-split", min_chunk_tokens=16, variant="mfma_pv")
+
+
+def test_other_group_sizes_variant_refusals():
+    """Group sizes the kernels are not built for, or a kernel built only for
+    1, 2, 4 and 8, are refused on the host."""
+    import torch
+    import paged_kv_decode_11_amd as pkd
+    from paged_kv_decode_11_amd import _lib
+
+    batch, _, _ = _small(990, [40, 3], 16, 21, 3)
+    r = gu.runner()
+    idx = torch.from_numpy(batch.kv_indices.astype(np.int32)).cuda()
+    for variant in ("dot2", "mfma"):
+        with pytest.raises(pkd.PkdError) as e:
+            r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, 21, 3, 128, 16, variant=variant)
+        assert e.value.code == _lib.PKD_ERR_UNSUPPORTED
+    r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, 21, 3, 128, 16)
+    assert r.planned_variant == "mfma_pv"
+    with pytest.raises(pkd.PkdError) as e:  # group size 9
+        r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, 27, 3, 128, 16)
+    assert e.value.code == _lib.PKD_ERR_UNSUPPORTED

@@ -315,3 +315,15 @@ def test_fp8_append_then_decode():
     o_ref, lse_ref = att.decode_fp8(q, grown, indptr, indices, last, 8, k_scale=K_SCALE,
                                     v_scale=V_SCALE)
     gu.assert_close(o, lse, o_ref, lse_ref, label="fp8 append-then-decode")
+
+
+@pytest.mark.parametrize("P", [16, 32, 64])
+@pytest.mark.parametrize("g,Hkv", [(3, 2), (5, 8), (6, 4), (7, 4)])
+def test_fp8_decode_other_group_sizes(P, g, Hkv):
+    """Group sizes 3, 5, 6 and 7 over an E4M3 cache, unsplit and split."""
+    rng = np.random.default_rng(1500 + 10 * P + g)
+    batch = workloads.random_batch(rng, 7, 800, P, Hkv * g, Hkv, 128)
+    q = workloads.host_query(batch, rng)
+    codes = workloads.host_cache_e4m3(batch, rng, poison=True)
+    _check(batch, q, codes, f"fp8 P{P} g{g} Hkv{Hkv}")
+    _check(batch, q, codes, f"fp8 P{P} g{g} Hkv{Hkv} split", fixed_chunk_pages=2)
