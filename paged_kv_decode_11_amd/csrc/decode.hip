@@ -404,7 +404,7 @@ void decode_kernel(
           }
         }
       }
-      if (bad && lane == 0) err[0] = PKD_DEVERR_PAGE_ID;
+      report_bad_pages(bad, lane, err, PKD_DEVERR_PAGE_ID);
 
       // totals over the 4 token rows; every lane then holds the full state
 #pragma unroll

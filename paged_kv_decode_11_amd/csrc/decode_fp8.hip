@@ -499,7 +499,7 @@ void decode_fp8_kernel(const uint16_t* __restrict__ q_ptr, const uint8_t* __rest
         if (step2(ta)) break;
         if (step2(tb)) break;
       }
-      if (bad && lane == 0) err[0] = PKD_DEVERR_PAGE_ID;
+      report_bad_pages(bad, lane, err, PKD_DEVERR_PAGE_ID);
       __builtin_amdgcn_s_setprio(0);
       done_steps += nsteps;
 

@@ -447,7 +447,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __re
         if (step(tb, ta)) break;
         if (step(tc, tb)) break;
       }
-      if (bad && lane == 0) err[0] = PKD_DEVERR_PAGE_ID;
+      report_bad_pages(bad, lane, err, PKD_DEVERR_PAGE_ID);
       __builtin_amdgcn_s_setprio(0);
       done_tiles += ntiles;
 

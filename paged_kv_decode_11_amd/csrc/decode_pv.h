@@ -434,7 +434,7 @@ __device__ __forceinline__ void decode_pv_body(
         if (step2(ta)) break;
         if (step2(tb)) break;
       }
-      if (bad && lane == 0) err[0] = PKD_DEVERR_PAGE_ID;
+      report_bad_pages(bad, lane, err, PKD_DEVERR_PAGE_ID);
       __builtin_amdgcn_s_setprio(0);
       done_tiles += ntiles;
 

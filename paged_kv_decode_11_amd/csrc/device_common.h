@@ -150,4 +150,11 @@ __device__ __forceinline__ int64_t safe_page(int32_t id, int64_t num_pages, int&
   return ok ? id : 0;
 }
 
+// Raises the page-id flag (`code`) when any lane of the wave replaced an id.
+// With pages below 16 tokens each lane reads the ids of its own rows, and
+// lane 0's rows need not touch every page of a tile.
+__device__ __forceinline__ void report_bad_pages(int bad, int lane, int32_t* err, int32_t code) {
+  if (__builtin_amdgcn_ballot_w64(bad != 0) != 0 && lane == 0) err[0] = code;
+}
+
 }  // namespace pkd

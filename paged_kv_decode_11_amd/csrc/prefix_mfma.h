@@ -387,7 +387,7 @@ __device__ __forceinline__ void prefix_body(
     // the next item's first tile reuses LDS stage 0
     lds_barrier();
   }
-  if (bad && lane == 0) err[0] = PKD_DEVERR_PAGE_ID;
+  report_bad_pages(bad, lane, err, PKD_DEVERR_PAGE_ID);
 }
 
 }  // namespace

@@ -249,3 +249,37 @@ def test_out_of_range_page_id_in_decode(variant, P, kv, chunk):
     assert r.read_device_error() == _lib.PKD_DEVERR_PAGE_ID
     assert r.read_device_error() == 0  # read clears the flag
     gu.assert_close(o, lse, o_ref, lse_ref, label=f"bad page id {variant} P{P}")
+
+
+@pytest.mark.parametrize("variant", ["dot2", "mfma", "mfma_pv"])
+@pytest.mark.parametrize("P", [1, 2])
+def test_out_of_range_page_id_off_lane_zero(variant, P):
+    """With pages of 1 or 2 tokens each lane reads the page ids of its own
+    rows, and the rows of a wave's lane 0 skip pages 1, 3 and 5 of a tile.
+    Out-of-range ids only there still raise PKD_DEVERR_PAGE_ID (the flag is
+    the wave's, not lane 0's), and page 0 stands in for them."""
+    import torch
+    from oracle import attention as att
+
+    rng = np.random.default_rng(90 + P)
+    lens = [40, 33, 7 * P + 5, 64]
+    need = sum(-(-l // P) for l in lens)
+    batch = workloads.make_batch(lens, P, need + 4, 32, 8, 128, rng)
+    num_pages = batch.num_pages
+    bad_idx = batch.kv_indices.copy()
+    ip = batch.kv_indptr
+    bad_idx[ip[0] + 1] = num_pages
+    bad_idx[ip[1] + 3] = -5
+    bad_idx[ip[3] + 5] = num_pages + 77
+    sub = np.where((bad_idx < 0) | (bad_idx >= num_pages), 0, bad_idx).astype(np.int32)
+    q = workloads.host_query(batch, rng)
+    cache = workloads.host_cache(batch, rng)
+    gu.say("bad page id off lane 0", variant, "P", P)
+    r = gu.runner()
+    r.plan(batch.kv_indptr, torch.from_numpy(bad_idx).cuda(), batch.kv_last_page_len, 32, 8, 128,
+           P, variant=variant)
+    o, lse = r.run(gu.bits_to_dev(q), gu.bits_to_dev(cache), return_lse=True)
+    o_ref, lse_ref = att.decode(q, cache, batch.kv_indptr, sub, batch.kv_last_page_len, 8)
+    torch.cuda.synchronize()
+    assert r.read_device_error() == _lib.PKD_DEVERR_PAGE_ID
+    gu.assert_close(o, lse, o_ref, lse_ref, label=f"bad page id off lane 0 {variant} P{P}")
