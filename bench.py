@@ -568,8 +568,8 @@ def bench_decode(args, workload_name: str, cpu_seconds: float, ceilings: bool = 
                                      batch.num_qo_heads, batch.num_kv_heads, batch.head_dim,
                                      None, scatter=False)
     fp8 = args.kv_dtype == "e4m3"
-    if fp8 and (args.variant == "dot2" or workload_name in ("token_sparse", "tiny")):
-        raise SystemExit("an e4m3 cache runs on the matrix-core kernel with page sizes 16-64")
+    if fp8 and args.variant == "dot2":
+        raise SystemExit("an e4m3 cache runs on its own matrix-core kernel")
     kv_tok = batch.kv_bytes_per_token() // (2 if fp8 else 1)
     kernel = None  # set from the library's plan below
     layer_bytes = batch.total_tokens * kv_tok

@@ -245,8 +245,8 @@ size_t pkd_host_workspace_bytes(int32_t max_batch, int32_t num_slots);
  * num_qo_heads / num_kv_heads from 1 to 8 (PKD_VARIANT_DOT2 and
  * PKD_VARIANT_MFMA: 1, 2, 4 or 8), and either a bf16 cache with
  * page_size in {1, 2, 4, 8, 16, 32, 64} or an FP8 E4M3 cache
- * (kv_dtype PKD_DTYPE_FP8_E4M3, matrix-core variant only) with page_size in
- * {16, 32, 64}; else PKD_ERR_UNSUPPORTED.  Rejects (PKD_ERR_INVALID_ARG)
+ * (kv_dtype PKD_DTYPE_FP8_E4M3, its own matrix-core kernel) with the same
+ * page sizes; else PKD_ERR_UNSUPPORTED.  Rejects (PKD_ERR_INVALID_ARG)
  * kv_indptr[0] != 0, a request with no page, last_page_len outside
  * [1, page_size], batch < 1, num_qo_heads not a multiple of num_kv_heads.
  * The workspaces passed here are the ones later runs use. */

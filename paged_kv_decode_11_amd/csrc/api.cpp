@@ -153,7 +153,8 @@ int check_shapes(int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t q_dtype,
   if (kv_dtype == PKD_DTYPE_FP8_E4M3) {
     if (!pkd::fp8_variant_built(Hq / Hkv, P))
       return fail(PKD_ERR_UNSUPPORTED,
-                  "an fp8 e4m3 cache is built for group sizes 1 to 8 and page_size 16, 32 or 64");
+                  "an fp8 e4m3 cache is built for group sizes 1 to 8 and page_size 1, 2, 4, 8, 16, "
+                  "32 or 64");
     return PKD_OK;
   }
   if (!pkd::decode_variant_built(Hq / Hkv, P) && !pkd::pv_variant_built(Hq / Hkv, P))

@@ -41,9 +41,11 @@
 // is computed (two steps in a ring, each refilled with the step two ahead
 // once its V is in LDS and its K consumed), one wave per KV head as in the bf16
 // matrix-core kernel; Q waits in LDS.  The two waves that share a SIMD keep
-// pace through issue priority (see the steady-state loop).  Page sizes 16, 32 and 64: each 16-token half of a
-// step lies in one page, addressed through a buffer descriptor over that
-// page.
+// pace through issue priority (see the steady-state loop).  Page sizes 16,
+// 32 and 64 keep each 16-token half of a step in one page, addressed through
+// a buffer descriptor over that page; smaller pages (1, 2, 4, 8 tokens) give
+// each lane the address of each of its rows (two K rows and four V rows per
+// step).
 
 #include <hip/hip_runtime.h>
 
@@ -132,15 +134,43 @@ struct FStep {
   uint4 v[4];     // load i: V[token 8 i + (l >> 3)] bytes 16 (l & 7) .. + 16
 };
 
-// Buffers over the pages of the two halves of a step and the byte offset of
-// each half's first token row within its page.
-struct FRef {
+// Where this lane's rows of one step are.  Pages of 16 or more tokens:
+// buffers over the pages of the two halves and the byte offset of each
+// half's first token row within its page.  Smaller pages: the range-checked
+// page id of each of this lane's rows (K rows of both halves, V rows of the
+// four V loads), the step and the item length; each address is formed at
+// its load (six 64-bit addresses held across the step would spill).
+template <int P, bool kWhole = (P % 16 == 0)>
+struct FRef;
+
+template <int P>
+struct FRef<P, true> {
   __amdgpu_buffer_rsrc_t page[2];
   uint32_t off[2];
 };
 
-struct FIds {
+template <int P>
+struct FRef<P, false> {
+  int32_t k[2];
+  int32_t v[4];
+  int32_t step;
+  int32_t len;
+};
+
+// Page ids of one step, read a step ahead of their use: one wave-uniform id
+// per half for whole-half pages, else the id of each of this lane's rows.
+template <int P, bool kWhole = (P % 16 == 0)>
+struct FIds;
+
+template <int P>
+struct FIds<P, true> {
   int32_t id[2];
+};
+
+template <int P>
+struct FIds<P, false> {
+  int32_t k[2];
+  int32_t v[4];
 };
 
 struct FCtx {
@@ -151,69 +181,124 @@ struct FCtx {
   uint32_t page_bytes;
   uint32_t k_lane;      // this lane's K offset in a half: (l & 15) rows + head + 16 (l >> 4)
   uint32_t v_lane;      // this lane's V offset in a load: (l >> 3) rows + head + 16 (l & 7)
+  uint32_t k_col;       // this lane's K offset in a row: head + 16 (l >> 4)
+  uint32_t v_col;       // this lane's V offset in a row: head + 16 (l & 7)
 };
 
-// Page ids of step s's halves; a half past the item's last page (possible
-// when P = 16) reads that last page and is masked.
+// Step tokens of this lane's rows, clamped into the item (rows past its end
+// re-read its last token; their logits are masked and their V zeroed): K
+// row of half h is token 16 h + (l & 15), V load i holds token 8 i + (l >> 3).
+__device__ __forceinline__ int f_k_token(int s, int h, int lane, int len) {
+  return min(kStep * s + 16 * h + (lane & 15), len - 1);
+}
+__device__ __forceinline__ int f_v_token(int s, int i, int lane, int len) {
+  return min(kStep * s + 8 * i + (lane >> 3), len - 1);
+}
+
+// Page ids of step s.  Whole-half pages: the id of each half; a half past
+// the item's last page (possible when P = 16) reads that last page and is
+// masked.  Smaller pages: the id of each of this lane's rows.
 template <int P>
-__device__ __forceinline__ FIds f_read_ids(const int32_t* idx, int len, int s) {
-  FIds ids;
-  const int last = (len - 1) / P;
-  ids.id[0] = idx[min((kStep * s) / P, last)];
-  if constexpr (P == 16) {
-    ids.id[1] = idx[min((kStep * s + 16) / P, last)];
+__device__ __forceinline__ FIds<P> f_read_ids(const int32_t* idx, int len, int s, int lane) {
+  FIds<P> ids;
+  if constexpr (P % 16 == 0) {
+    const int last = (len - 1) / P;
+    ids.id[0] = idx[min((kStep * s) / P, last)];
+    if constexpr (P == 16) {
+      ids.id[1] = idx[min((kStep * s + 16) / P, last)];
+    } else {
+      ids.id[1] = ids.id[0];
+    }
   } else {
-    ids.id[1] = ids.id[0];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) ids.k[h] = idx[f_k_token(s, h, lane, len) / P];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ids.v[i] = idx[f_v_token(s, i, lane, len) / P];
   }
   return ids;
 }
 
 template <int P>
-__device__ __forceinline__ FRef f_ref(const FCtx& c, const FIds& ids, int s, int& bad) {
-  FRef r;
+__device__ __forceinline__ FRef<P> f_ref(const FCtx& c, FIds<P> ids, int s, int lane, int len,
+                                         int& bad) {
+  FRef<P> r;
+  if constexpr (P % 16 != 0) {
+    // (the ids were requested a step earlier; the empty asm keeps each range
+    // check here instead of next to its load)
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    // The id was requested a step earlier.  Passing it through an empty asm
-    // here keeps its range check from being hoisted next to the load, where
-    // it would make the step wait for the scalar load before its prefetch.
-    // (wave-uniform by construction; readfirstlane keeps it in a scalar
-    // register whatever the loop structure)
-    int32_t id = __builtin_amdgcn_readfirstlane(ids.id[h]);
-    asm volatile("" : "+s"(id));
-    const int64_t pg = safe_page(id, c.num_pages, bad);
-    // raw buffer over one page (32-bit data format word as raw loads need);
-    // offsets past the page read zeros
-    r.page[h] = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(c.kv + pg * c.page_bytes), 0,
-                                                  int(c.page_bytes), 0x00020000);
-    r.off[h] = uint32_t((kStep * s + 16 * h) % P) * c.row_bytes;
+    for (int h = 0; h < 2; ++h) {
+      asm volatile("" : "+v"(ids.k[h]));
+      r.k[h] = int32_t(safe_page(ids.k[h], c.num_pages, bad));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      asm volatile("" : "+v"(ids.v[i]));
+      r.v[i] = int32_t(safe_page(ids.v[i], c.num_pages, bad));
+    }
+    r.step = s;
+    r.len = len;
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // The id was requested a step earlier.  Passing it through an empty asm
+      // here keeps its range check from being hoisted next to the load, where
+      // it would make the step wait for the scalar load before its prefetch.
+      // (wave-uniform by construction; readfirstlane keeps it in a scalar
+      // register whatever the loop structure)
+      int32_t id = __builtin_amdgcn_readfirstlane(ids.id[h]);
+      asm volatile("" : "+s"(id));
+      const int64_t pg = safe_page(id, c.num_pages, bad);
+      // raw buffer over one page (32-bit data format word as raw loads need);
+      // offsets past the page read zeros
+      r.page[h] = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(c.kv + pg * c.page_bytes),
+                                                    0, int(c.page_bytes), 0x00020000);
+      r.off[h] = uint32_t((kStep * s + 16 * h) % P) * c.row_bytes;
+    }
   }
   return r;
 }
 
-__device__ __forceinline__ void f_load_k(FStep& d, const FCtx& c, const FRef& r) {
+template <int P>
+__device__ __forceinline__ void f_load_k(FStep& d, const FCtx& c, const FRef<P>& r) {
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const auto w = __builtin_amdgcn_raw_buffer_load_b128(r.page[h], c.k_lane, r.off[h] + 64 * i,
-                                                           kBufferNontemporal);
-      d.k[h][i] = make_uint4(w[0], w[1], w[2], w[3]);
+      if constexpr (P % 16 == 0) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b128(r.page[h], c.k_lane,
+                                                             r.off[h] + 64 * i, kBufferNontemporal);
+        d.k[h][i] = make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
+        const int lane = threadIdx.x & 63;
+        const uint32_t slot = uint32_t(f_k_token(r.step, h, lane, r.len) % P);
+        d.k[h][i] = load_stream16(c.kv + int64_t(r.k[h]) * c.page_bytes + slot * c.row_bytes +
+                                  c.k_col + 64 * i);
+      }
     }
 }
 
-__device__ __forceinline__ void f_load_v(FStep& d, const FCtx& c, const FRef& r) {
+template <int P>
+__device__ __forceinline__ void f_load_v(FStep& d, const FCtx& c, const FRef<P>& r) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const auto w = __builtin_amdgcn_raw_buffer_load_b128(
-        r.page[i >> 1], c.v_lane, r.off[i >> 1] + c.v_bytes + 8 * (i & 1) * c.row_bytes,
-        kBufferNontemporal);
-    d.v[i] = make_uint4(w[0], w[1], w[2], w[3]);
+    if constexpr (P % 16 == 0) {
+      const auto w = __builtin_amdgcn_raw_buffer_load_b128(
+          r.page[i >> 1], c.v_lane, r.off[i >> 1] + c.v_bytes + 8 * (i & 1) * c.row_bytes,
+          kBufferNontemporal);
+      d.v[i] = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      const int lane = threadIdx.x & 63;
+      const uint32_t slot = uint32_t(f_v_token(r.step, i, lane, r.len) % P);
+      d.v[i] = load_stream16(c.kv + int64_t(r.v[i]) * c.page_bytes + c.v_bytes +
+                             slot * c.row_bytes + c.v_col);
+    }
   }
 }
 
-__device__ __forceinline__ void f_load(FStep& d, const FCtx& c, const FRef& r) {
-  f_load_k(d, c, r);
-  f_load_v(d, c, r);
+template <int P>
+__device__ __forceinline__ void f_load(FStep& d, const FCtx& c, const FRef<P>& r) {
+  f_load_k<P>(d, c, r);
+  f_load_v<P>(d, c, r);
 }
 
 template <int G>
@@ -229,9 +314,9 @@ struct FState {
 // the last step (kLast)
 // masks tokens >= valid: their logits to -inf and their V rows to zero (a
 // slot past the sequence may hold any code).
-template <int G, bool kPrefetch, bool kLast>
+template <int G, int P, bool kPrefetch, bool kLast>
 __device__ __forceinline__ void f_step(FState<G>& st, const FStep& cur, FStep& nxt,
-                                       const FCtx& c, const FRef& next,
+                                       const FCtx& c, const FRef<P>& next,
                                        int valid, int lane, float scale_log2, FShared& sh,
                                        uint32_t v_wr, uint32_t v_rd) {
   const int kg = lane >> 4;
@@ -253,7 +338,7 @@ __device__ __forceinline__ void f_step(FState<G>& st, const FStep& cur, FStep& n
   }
   if constexpr (kPrefetch) {
     __builtin_amdgcn_sched_barrier(0);
-    f_load_v(nxt, c, next);
+    f_load_v<P>(nxt, c, next);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -273,7 +358,7 @@ __device__ __forceinline__ void f_step(FState<G>& st, const FStep& cur, FStep& n
   }
   if constexpr (kPrefetch) {
     __builtin_amdgcn_sched_barrier(0);
-    f_load_k(nxt, c, next);
+    f_load_k<P>(nxt, c, next);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -339,7 +424,8 @@ void decode_fp8_kernel(const uint16_t* __restrict__ q_ptr, const uint8_t* __rest
                        int32_t* __restrict__ err, int64_t num_pages, float scale_log2,
                        float out_scale, int num_qo_heads, int num_kv_heads) {
   static_assert(G >= 1 && G <= 8, "group size");
-  static_assert(P == 16 || P == 32 || P == 64, "page size");
+  static_assert(P == 1 || P == 2 || P == 4 || P == 8 || P == 16 || P == 32 || P == 64,
+                "page size");
   __shared__ FShared shared[kMaxWavesPerBlock];
   // steps each wave has completed; see the steady-state loop
   __shared__ int progress[kMaxWavesPerBlock];
@@ -347,7 +433,8 @@ void decode_fp8_kernel(const uint16_t* __restrict__ q_ptr, const uint8_t* __rest
   // The slot's bounds, its first item (with the ids of that item's first two
   // pages) and the header fields sit at offsets fixed by the slot count (the
   // grid size): requested together, waited for at once (the empty asm), one
-  // round trip to memory before the first loads of K and V.
+  // round trip to memory before the first loads of K and V (two for pages
+  // below 16 tokens, whose ids come from the page table).
   const int32_t* hdr = ws + PKD_HEADER_BASE;
   const int num_slots = gridDim.x;
   const int32_t* slot_indptr = ws + plan_off_slots();
@@ -413,6 +500,8 @@ void decode_fp8_kernel(const uint16_t* __restrict__ q_ptr, const uint8_t* __rest
       const uint32_t head = uint32_t(kh) * kHeadDim;
       c.k_lane = uint32_t(row16) * c.row_bytes + head + 16 * uint32_t(kg);
       c.v_lane = uint32_t(lane >> 3) * c.row_bytes + head + 16 * uint32_t(lane & 7);
+      c.k_col = head + 16 * uint32_t(kg);
+      c.v_col = head + 16 * uint32_t(lane & 7);
 
       // Q^T operand: lane (row l & 15, kg) holds head dims
       // 64 (j >> 1) + 16 kg + 8 (j & 1) .. + 7 for MFMA j; rows >= g are zero.
@@ -440,25 +529,31 @@ void decode_fp8_kernel(const uint16_t* __restrict__ q_ptr, const uint8_t* __rest
       // Step 0 lies in the item's first two pages (one, for P >= 32), whose
       // ids the item row holds; so does step 1 for P >= 32 (page 1 for
       // P = 32: the first page again when the item has one page, as then it
-      // has one step).  For P = 16 step 1 needs the page table.
-      FIds ids0, ids1;
-      ids0.id[0] = id0;
-      ids0.id[1] = P == 16 ? id1 : id0;
-      f_load(ta, c, f_ref<P>(c, ids0, 0, bad));
+      // has one step).  For P = 16 step 1 needs the page table.  Smaller
+      // pages read the ids of both steps from the page table, together.
+      FIds<P> ids0, ids1;
+      if constexpr (P % 16 == 0) {
+        ids0.id[0] = id0;
+        ids0.id[1] = P == 16 ? id1 : id0;
+      } else {
+        ids0 = f_read_ids<P>(idx, len, 0, lane);
+        ids1 = f_read_ids<P>(idx, len, min(1, nsteps - 1), lane);
+      }
+      f_load<P>(ta, c, f_ref<P>(c, ids0, 0, lane, len, bad));
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (P == 16) {
-        ids1 = f_read_ids<P>(idx, len, min(1, nsteps - 1));
-      } else {
+        ids1 = f_read_ids<P>(idx, len, min(1, nsteps - 1), lane);
+      } else if constexpr (P % 16 == 0) {
         ids1.id[0] = ids1.id[1] = P == 32 ? id1 : id0;
       }
-      f_load(tb, c, f_ref<P>(c, ids1, min(1, nsteps - 1), bad));
-      FIds ids_next = f_read_ids<P>(idx, len, min(2, nsteps - 1));
+      f_load<P>(tb, c, f_ref<P>(c, ids1, min(1, nsteps - 1), lane, len, bad));
+      FIds<P> ids_next = f_read_ids<P>(idx, len, min(2, nsteps - 1), lane);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) sh.q[j][lane] = qop[j];
       __builtin_amdgcn_wave_barrier();
       const int last_valid = len - kStep * (nsteps - 1);
-      const FRef none = {};
+      const FRef<P> none = {};
       int n = 0;
       // Two steps form the ring; each is refilled with the step two ahead as
       // soon as its V is in LDS and its K consumed, so while a step is
@@ -466,18 +561,18 @@ void decode_fp8_kernel(const uint16_t* __restrict__ q_ptr, const uint8_t* __rest
       // trip.
       auto step2 = [&](FStep& cur) -> bool {
         if (n == nsteps - 1) {
-          f_step<G, false, true>(st, cur, cur, c, none, last_valid, lane, scale_log2, sh,
-                                 v_wr, v_rd);
+          f_step<G, P, false, true>(st, cur, cur, c, none, last_valid, lane, scale_log2, sh,
+                                    v_wr, v_rd);
           return true;
         }
         if (n + 2 < nsteps) {
-          const FRef ref = f_ref<P>(c, ids_next, n + 2, bad);
-          ids_next = f_read_ids<P>(idx, len, min(n + 3, nsteps - 1));
-          f_step<G, true, false>(st, cur, cur, c, ref, kStep, lane, scale_log2, sh, v_wr,
-                                 v_rd);
+          const FRef<P> ref = f_ref<P>(c, ids_next, n + 2, lane, len, bad);
+          ids_next = f_read_ids<P>(idx, len, min(n + 3, nsteps - 1), lane);
+          f_step<G, P, true, false>(st, cur, cur, c, ref, kStep, lane, scale_log2, sh, v_wr,
+                                    v_rd);
         } else {
-          f_step<G, false, false>(st, cur, cur, c, none, kStep, lane, scale_log2, sh, v_wr,
-                                  v_rd);
+          f_step<G, P, false, false>(st, cur, cur, c, none, kStep, lane, scale_log2, sh, v_wr,
+                                     v_rd);
         }
         ++n;
         return false;
@@ -489,9 +584,10 @@ void decode_fp8_kernel(const uint16_t* __restrict__ q_ptr, const uint8_t* __rest
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           FStep& cur = k == 0 ? ta : tb;
-          const FRef ref = f_ref<P>(c, ids_next, n + 2, bad);
-          ids_next = f_read_ids<P>(idx, len, min(n + 3, nsteps - 1));
-          f_step<G, true, false>(st, cur, cur, c, ref, kStep, lane, scale_log2, sh, v_wr, v_rd);
+          const FRef<P> ref = f_ref<P>(c, ids_next, n + 2, lane, len, bad);
+          ids_next = f_read_ids<P>(idx, len, min(n + 3, nsteps - 1), lane);
+          f_step<G, P, true, false>(st, cur, cur, c, ref, kStep, lane, scale_log2, sh, v_wr,
+                                    v_rd);
           ++n;
         }
       }
@@ -544,6 +640,10 @@ hipError_t launch_f(const DecodeParams& p, int num_slots, hipStream_t stream) {
 template <int G>
 hipError_t launch_fg(const DecodeParams& p, int page_size, int num_slots, hipStream_t stream) {
   switch (page_size) {
+    case 1: return launch_f<G, 1>(p, num_slots, stream);
+    case 2: return launch_f<G, 2>(p, num_slots, stream);
+    case 4: return launch_f<G, 4>(p, num_slots, stream);
+    case 8: return launch_f<G, 8>(p, num_slots, stream);
     case 16: return launch_f<G, 16>(p, num_slots, stream);
     case 32: return launch_f<G, 32>(p, num_slots, stream);
     case 64: return launch_f<G, 64>(p, num_slots, stream);
@@ -555,7 +655,8 @@ hipError_t launch_fg(const DecodeParams& p, int page_size, int num_slots, hipStr
 
 bool fp8_variant_built(int g, int page_size) {
   return g >= 1 && g <= 8 &&
-         (page_size == 16 || page_size == 32 || page_size == 64);
+         (page_size == 1 || page_size == 2 || page_size == 4 || page_size == 8 ||
+          page_size == 16 || page_size == 32 || page_size == 64);
 }
 
 hipError_t launch_decode_fp8(const DecodeParams& p, int g, int page_size, int num_slots,

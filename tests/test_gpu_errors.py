@@ -72,8 +72,9 @@ def test_dtype_and_layout_errors():
 
 
 def test_fp8_cache_errors():
-    """An E4M3 cache: page sizes and kernels it is not built for, scales on a
-    bf16 cache, invalid scales, and a run whose cache dtype is not the plan's."""
+    """An E4M3 cache: a page size and a kernel it is not built for, scales on
+    a bf16 cache, invalid scales, and a run whose cache dtype is not the
+    plan's."""
     import torch
     import paged_kv_decode_11_amd as pkd
 
@@ -83,7 +84,7 @@ def test_fp8_cache_errors():
     idx = torch.from_numpy(batch.kv_indices).cuda()
     args = (batch.kv_indptr, idx, batch.kv_last_page_len, 32, 8, 128)
     with pytest.raises(pkd.PkdError) as e:
-        r.plan(*args, 8, kv_data_type=fp8)
+        r.plan(*args, 128, kv_data_type=fp8)
     assert e.value.code == _lib.PKD_ERR_UNSUPPORTED
     with pytest.raises(pkd.PkdError) as e:
         r.plan(*args, 16, kv_data_type=fp8, variant="dot2")
@@ -251,7 +252,7 @@ def test_out_of_range_page_id_in_decode(variant, P, kv, chunk):
     gu.assert_close(o, lse, o_ref, lse_ref, label=f"bad page id {variant} P{P}")
 
 
-@pytest.mark.parametrize("variant", ["dot2", "mfma", "mfma_pv"])
+@pytest.mark.parametrize("variant", ["dot2", "mfma", "mfma_pv", "e4m3"])
 @pytest.mark.parametrize("P", [1, 2])
 def test_out_of_range_page_id_off_lane_zero(variant, P):
     """With pages of 1 or 2 tokens each lane reads the page ids of its own
@@ -273,13 +274,22 @@ def test_out_of_range_page_id_off_lane_zero(variant, P):
     bad_idx[ip[3] + 5] = num_pages + 77
     sub = np.where((bad_idx < 0) | (bad_idx >= num_pages), 0, bad_idx).astype(np.int32)
     q = workloads.host_query(batch, rng)
-    cache = workloads.host_cache(batch, rng)
     gu.say("bad page id off lane 0", variant, "P", P)
     r = gu.runner()
-    r.plan(batch.kv_indptr, torch.from_numpy(bad_idx).cuda(), batch.kv_last_page_len, 32, 8, 128,
-           P, variant=variant)
-    o, lse = r.run(gu.bits_to_dev(q), gu.bits_to_dev(cache), return_lse=True)
-    o_ref, lse_ref = att.decode(q, cache, batch.kv_indptr, sub, batch.kv_last_page_len, 8)
+    idx = torch.from_numpy(bad_idx).cuda()
+    if variant == "e4m3":  # the FP8 kernel (per-lane rows of 2 K and 4 V loads)
+        codes = workloads.host_cache_e4m3(batch, rng)
+        r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, 32, 8, 128, P,
+               kv_data_type=torch.float8_e4m3fn)
+        o, lse = r.run(gu.bits_to_dev(q), gu.codes_to_dev(codes), return_lse=True,
+                       k_scale=1.0 / 64, v_scale=1.0 / 32)
+        o_ref, lse_ref = att.decode_fp8(q, codes, batch.kv_indptr, sub, batch.kv_last_page_len, 8,
+                                        k_scale=1.0 / 64, v_scale=1.0 / 32)
+    else:
+        cache = workloads.host_cache(batch, rng)
+        r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, 32, 8, 128, P, variant=variant)
+        o, lse = r.run(gu.bits_to_dev(q), gu.bits_to_dev(cache), return_lse=True)
+        o_ref, lse_ref = att.decode(q, cache, batch.kv_indptr, sub, batch.kv_last_page_len, 8)
     torch.cuda.synchronize()
     assert r.read_device_error() == _lib.PKD_DEVERR_PAGE_ID
     gu.assert_close(o, lse, o_ref, lse_ref, label=f"bad page id off lane 0 {variant} P{P}")

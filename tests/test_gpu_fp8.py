@@ -47,7 +47,7 @@ def _check(batch, q, codes, label, k_scale=K_SCALE, v_scale=V_SCALE, sm_scale=No
     return gu.assert_close(o, lse, o_ref, lse_ref, label=label)
 
 
-@pytest.mark.parametrize("P", [16, 32, 64])
+@pytest.mark.parametrize("P", [1, 2, 4, 8, 16, 32, 64])
 @pytest.mark.parametrize("g", [1, 2, 4, 8])
 def test_fp8_decode_random_batch(P, g):
     """Random lengths over scattered pages; unused slots and pages hold NaN
@@ -74,10 +74,11 @@ def test_fp8_decode_kv_head_counts(Hkv, g):
     _check(batch, q, codes, f"fp8 Hkv{Hkv} g{g} split", fixed_chunk_pages=3)
 
 
-@pytest.mark.parametrize("P", [16, 32, 64])
+@pytest.mark.parametrize("P", [1, 2, 4, 8, 16, 32, 64])
 def test_fp8_decode_edge_lengths(P):
     """Lengths at page and 32-token step boundaries (a step's second half
-    past the last page when P = 16)."""
+    past the last page when P = 16; rows past the end within a step when
+    pages are smaller)."""
     lens = sorted(set(workloads.edge_lengths(P)) | {15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64,
                                                     65, 95, 96, 97, 129})
     rng = np.random.default_rng(77 + P)
@@ -88,7 +89,8 @@ def test_fp8_decode_edge_lengths(P):
     _check(batch, q, codes, f"fp8 edges P{P}")
 
 
-@pytest.mark.parametrize("P,chunk", [(16, 1), (16, 3), (32, 1), (64, 1), (64, 2)])
+@pytest.mark.parametrize("P,chunk", [(1, 20), (1, 48), (2, 24), (4, 5), (8, 6), (16, 1), (16, 3),
+                                     (32, 1), (64, 1), (64, 2)])
 def test_fp8_decode_forced_splits(P, chunk):
     """Every request cut into chunks of `chunk` pages: partial states and the
     merge, chunks shorter than a 32-token step included."""
@@ -232,7 +234,7 @@ def _dev_i32(a):
 
 @pytest.mark.parametrize("P,Hkv,k_scale,v_scale", [(16, 8, 1.0, 1.0), (16, 1, 0.37, 3.0),
                                                     (64, 2, 1.0 / 64, 1.0 / 32),
-                                                    (32, 8, 0.1, 0.01)])
+                                                    (32, 8, 0.1, 0.01), (1, 8, 0.5, 2.0)])
 def test_fp8_append_bit_exact(P, Hkv, k_scale, v_scale):
     import paged_kv_decode_11_amd as pkd
     import torch
@@ -317,7 +319,7 @@ def test_fp8_append_then_decode():
     gu.assert_close(o, lse, o_ref, lse_ref, label="fp8 append-then-decode")
 
 
-@pytest.mark.parametrize("P", [16, 32, 64])
+@pytest.mark.parametrize("P", [1, 4, 16, 32, 64])
 @pytest.mark.parametrize("g,Hkv", [(3, 2), (5, 8), (6, 4), (7, 4)])
 def test_fp8_decode_other_group_sizes(P, g, Hkv):
     """Group sizes 3, 5, 6 and 7 over an E4M3 cache, unsplit and split."""
@@ -326,4 +328,5 @@ def test_fp8_decode_other_group_sizes(P, g, Hkv):
     q = workloads.host_query(batch, rng)
     codes = workloads.host_cache_e4m3(batch, rng, poison=True)
     _check(batch, q, codes, f"fp8 P{P} g{g} Hkv{Hkv}")
-    _check(batch, q, codes, f"fp8 P{P} g{g} Hkv{Hkv} split", fixed_chunk_pages=2)
+    _check(batch, q, codes, f"fp8 P{P} g{g} Hkv{Hkv} split",
+           fixed_chunk_pages=2 if P >= 16 else 48 // P)
