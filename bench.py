@@ -293,7 +293,8 @@ def bench_shared_prefix(args):
     the suffix states from a decode plan, merged row by row.  Single format:
     one decode plan over each request's prefix + suffix pages.  `value` is
     the KV bytes the composable step streams (prefix once, suffixes) over its
-    time."""
+    time.  With --kv-dtype e4m3 every format runs over E4M3 codes with
+    per-tensor scales."""
     import numpy as np
     import torch
 
@@ -304,7 +305,10 @@ def bench_shared_prefix(args):
     torch.cuda.set_device(dev)
     spec, rng, b = workloads.workload("shared_prefix")
     main, prefix, suffix = b["main"], b["prefix"], b["suffix"]
-    kv_tok = main.kv_bytes_per_token()
+    fp8 = args.kv_dtype == "e4m3"
+    kv_tok = main.kv_bytes_per_token() // (2 if fp8 else 1)
+    kv = dict(kv_data_type=torch.float8_e4m3fn) if fp8 else {}
+    scales = dict(k_scale=1.0 / 64, v_scale=1.0 / 64) if fp8 else {}
     n_prefix_pages = int(prefix.kv_indptr[1])
     prefix_tokens = int(prefix.kv_lens[0])
     unique_bytes = (prefix_tokens + suffix.total_tokens) * kv_tok
@@ -312,7 +316,8 @@ def bench_shared_prefix(args):
     R = 8  # cache copies: R x unique bytes well above the last-level cache
     log(f"shared_prefix: B={main.batch} prefix={prefix_tokens} suffix tokens={suffix.total_tokens} "
         f"unique {unique_bytes / 1e6:.1f} MB, single-format {single_bytes / 1e6:.1f} MB, R={R}")
-    base = workloads.device_cache(main, spec.seed * 1000, dev, used_only=True)
+    base = (workloads.device_cache_e4m3(main, spec.seed * 1000, dev) if fp8 else
+            workloads.device_cache(main, spec.seed * 1000, dev, used_only=True))
     caches = [base] + [base.clone() for _ in range(R - 1)]
     qs = [workloads.device_query(main, spec.seed * 7919 + j, dev) for j in range(R)]
     H = main.num_qo_heads
@@ -324,17 +329,21 @@ def bench_shared_prefix(args):
     lses1 = [torch.empty((main.batch, H), dtype=torch.float32, device=dev) for _ in range(R)]
 
     def plan1():
-        r1.plan(main.kv_indptr, idx_main, main.kv_last_page_len, H, main.num_kv_heads, 128, 16)
+        r1.plan(main.kv_indptr, idx_main, main.kv_last_page_len, H, main.num_kv_heads, 128, 16,
+                **kv)
 
     def run1():
         for j in range(R):
-            r1.run(qs[j], caches[j], out=outs1[j], lse=lses1[j])
+            r1.run(qs[j], caches[j], out=outs1[j], lse=lses1[j], **scales)
 
     # composable: one shared-prefix plan (all 32 requests over the prefix
     # pages) and one decode plan (each request's own suffix), both writing
     # every chunk's state as a partial; pkd_run_composable runs the prefix
     # kernel, the suffix decode and one merge
-    half = torch.cuda.get_device_properties(dev).multi_processor_count // 2
+    # half of the compute units each, so that the bf16 form runs both
+    # attention kernels in one launch side by side; over an E4M3 cache the
+    # two kernels run one after the other and each takes the whole chip
+    half = 0 if fp8 else torch.cuda.get_device_properties(dev).multi_processor_count // 2
     rp = pkd.SharedPlanRun(4, main.batch, n_prefix_pages, H, main.num_kv_heads,
                            num_slots=half if args.prefix_slots < 0 else args.prefix_slots,
                            device=0)
@@ -352,16 +361,16 @@ def bench_shared_prefix(args):
 
     def plan2():
         rp.plan(qo, kv_indptr, idx_pre, prefix.kv_last_page_len[:1], H, main.num_kv_heads, 128, 16,
-                all_partials=True, **pre_opts)
+                all_partials=True, **pre_opts, **kv)
         # alpha = 32: each chunk weighs 32 tokens on top of its own in the
         # slot assignment, so that no slot gets three of the short suffix
         # chunks (the launch's last workgroup) while most get one
         rs.plan(suffix.kv_indptr, idx_suf, suffix.kv_last_page_len, H, main.num_kv_heads, 128, 16,
-                all_partials=True, alpha=SUFFIX_ALPHA)
+                all_partials=True, alpha=SUFFIX_ALPHA, **kv)
 
     def run2():
         for j in range(R):
-            pkd.run_composable(rp, rs, qs[j], caches[j], out=outs2[j], lse=lses2[j])
+            pkd.run_composable(rp, rs, qs[j], caches[j], out=outs2[j], lse=lses2[j], **scales)
 
     # the same states through separate calls (prefix run with its merge,
     # suffix run with its merge, merge_state): five launches per layer
@@ -376,14 +385,14 @@ def bench_shared_prefix(args):
 
     def plan5():
         rp5.plan(qo, kv_indptr, idx_pre, prefix.kv_last_page_len[:1], H, main.num_kv_heads, 128,
-                 16, **pre_opts)
+                 16, **pre_opts, **kv)
         rs5.plan(suffix.kv_indptr, idx_suf, suffix.kv_last_page_len, H, main.num_kv_heads, 128, 16,
-                 alpha=SUFFIX_ALPHA)
+                 alpha=SUFFIX_ALPHA, **kv)
 
     def run5():
         for j in range(R):
-            rp5.run(qs[j], caches[j], out=op[j], lse=lp[j])
-            rs5.run(qs[j], caches[j], out=os_[j], lse=ls[j])
+            rp5.run(qs[j], caches[j], out=op[j], lse=lp[j], **scales)
+            rs5.run(qs[j], caches[j], out=os_[j], lse=ls[j], **scales)
             pkd.merge_state(op[j], lp[j], os_[j], ls[j], out=outs5[j], lse_out=lses5[j])
 
     plan1()
@@ -439,12 +448,16 @@ def bench_shared_prefix(args):
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms2, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 q/K/V, seeded lengths and page placement)",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "e4m3 kv (bf16/f16 mfma, f32 accumulate)" if fp8 else "bf16",
+        "data": ("synthetic (seeded N(0,1) bf16 q, uniformly drawn E4M3 K/V codes with scales "
+                 "1/64, seeded lengths and page placement)" if fp8 else
+                 "synthetic (seeded N(0,1) bf16 q/K/V, seeded lengths and page placement)"),
         "config": {"workload": "shared_prefix", "batch": main.batch, "layers": R,
                    "prefix_tokens": prefix_tokens, "suffix_tokens": suffix.total_tokens,
                    "num_qo_heads": H, "num_kv_heads": main.num_kv_heads, "head_dim": 128,
-                   "page_size": 16, "slots": rp.num_slots, "parallelism": "single GPU"},
+                   "page_size": 16, "slots": rp.num_slots, "kv_dtype": args.kv_dtype,
+                   "parallelism": "single GPU"},
         "us_per_layer_step": round(us2, 2),
         "frac_of_hbm_peak": round(value / PEAK_HBM_GBS, 4),
         "composable_us_per_layer": round(us2, 2),
@@ -457,7 +470,7 @@ def bench_shared_prefix(args):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": (measured_traffic("shared_prefix", "composable_kernel", "bf16")
-                                 if one_launch else None),
+                                 if one_launch and not fp8 else None),
                      "kernel": roof_kernel, "avg_launch_us": round(attn_us, 2),
                      "algorithmic_bytes_per_launch": unique_bytes,
                      "merge_avg_launch_us": round(prefix_merge_us, 2)},

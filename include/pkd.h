@@ -293,9 +293,10 @@ int pkd_plan_host(const int32_t* kv_indptr, const int32_t* kv_last_page_len, int
  * cp = max(ceil(min_chunk_tokens / P), ceil(ceil(T_eff num_kv_heads / S) /
  * P)) pages; an item is one KV head of one (group, row block, chunk) and
  * costs alpha x (requests in its block) + beta x (chunk tokens).  Built for
- * gqa 1, 2, 4, 8 and page_size 16, 32, 64 (else PKD_ERR_UNSUPPORTED); the
- * variant option is ignored.  Workspaces: size them with
- * pkd_shared_workspace_bytes. */
+ * gqa 1, 2, 4, 8 and page_size 16, 32, 64 (else PKD_ERR_UNSUPPORTED), over a
+ * bf16 or an FP8 E4M3 cache (runs of an E4M3 plan take per-tensor scales
+ * through pkd_run_scaled, as for a decode plan); the variant option is
+ * ignored.  Workspaces: size them with pkd_shared_workspace_bytes. */
 int pkd_plan_shared(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_indptr,
                     const int32_t* kv_indices, const int32_t* kv_last_page_len,
                     int32_t num_groups, int32_t num_qo_heads, int32_t num_kv_heads,
@@ -417,10 +418,23 @@ int pkd_run_scaled(pkd_handle* h, const void* q, int32_t batch, const void* kv_c
  * captured in a graph replays correctly after re-plans of either handle on
  * the same workspaces (the choice between the two forms is made at the call
  * from the handles' slot counts and the suffix plan's kernel).  Device
- * errors are raised on each handle's own flag. */
+ * errors are raised on each handle's own flag.  Over a bf16 cache; an FP8
+ * E4M3 cache goes through pkd_run_composable_scaled. */
 int pkd_run_composable(pkd_handle* prefix, pkd_handle* suffix, const void* q, int32_t batch,
                        const void* kv_cache, int64_t num_pages, int32_t q_dtype, int32_t kv_dtype,
                        void* o, float* lse, float sm_scale, pkd_stream_t stream);
+
+/* pkd_run_composable over a cache of FP8 E4M3 codes with one scale per
+ * tensor (the meaning of the codes and scales as in pkd_run_scaled): both
+ * plans made with kv_dtype PKD_DTYPE_FP8_E4M3.  The shared-prefix kernel and
+ * the FP8 decode kernel then run one after the other (the one-launch form
+ * is built for a bf16 cache), followed by the same merge.  k_scale and
+ * v_scale must be finite and > 0, and 1 for a bf16 cache (else
+ * PKD_ERR_INVALID_ARG); pkd_run_composable is this call with both 1. */
+int pkd_run_composable_scaled(pkd_handle* prefix, pkd_handle* suffix, const void* q,
+                              int32_t batch, const void* kv_cache, int64_t num_pages,
+                              int32_t q_dtype, int32_t kv_dtype, void* o, float* lse,
+                              float sm_scale, float k_scale, float v_scale, pkd_stream_t stream);
 
 /* Waits for `stream`, returns the device error flags raised by runs since
  * the last read (PKD_DEVERR_*, 0 if none) and clears them. */

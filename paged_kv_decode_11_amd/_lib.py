@@ -101,6 +101,9 @@ SIGNATURES = {
                                       ctypes.c_float, ctypes.c_float, ctypes.c_float, _vp]),
     "pkd_run_composable": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _vp, _vp,
                                           ctypes.c_float, _vp]),
+    "pkd_run_composable_scaled": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _vp,
+                                                 _vp, ctypes.c_float, ctypes.c_float,
+                                                 ctypes.c_float, _vp]),
     "pkd_read_device_error": (ctypes.c_int, [_vp, _pi32, _vp]),
     "pkd_merge_state": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "pkd_merge_states": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),

@@ -414,11 +414,13 @@ class StaticPlanRun(DecodePlanRun):
 
 
 def run_composable(prefix, suffix, q, kv_cache, out=None, lse=None, return_lse: bool = False,
-                   sm_scale=None, stream=None):
+                   sm_scale=None, stream=None, k_scale=None, v_scale=None):
     """The composable format in one call (pkd_run_composable): ``prefix`` a
     SharedPlanRun and ``suffix`` a DecodePlanRun, both planned with
     ``all_partials=True`` for the same requests; returns o (and lse) of every
-    request over its group's prefix and its own pages."""
+    request over its group's prefix and its own pages.  A float8_e4m3fn
+    cache takes per-tensor k_scale / v_scale (pkd_run_composable_scaled
+    when a scale is given)."""
     import torch
 
     shapes = []
@@ -435,11 +437,16 @@ def run_composable(prefix, suffix, q, kv_cache, out=None, lse=None, return_lse: 
         out = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=q.device)
     if return_lse and lse is None:
         lse = torch.empty(tuple(q.shape[:2]), dtype=torch.float32, device=q.device)
-    check(_lib.load().pkd_run_composable(
-        prefix._h, suffix._h, q.data_ptr(), q.shape[0], kv_cache.data_ptr(), kv_cache.shape[0],
-        _dtype_code(q.dtype), _dtype_code(kv_cache.dtype), out.data_ptr(),
-        lse.data_ptr() if lse is not None else None,
-        float(sm_scale) if sm_scale is not None else 0.0, _stream_ptr(stream)))
+    args = (prefix._h, suffix._h, q.data_ptr(), q.shape[0], kv_cache.data_ptr(), kv_cache.shape[0],
+            _dtype_code(q.dtype), _dtype_code(kv_cache.dtype), out.data_ptr(),
+            lse.data_ptr() if lse is not None else None,
+            float(sm_scale) if sm_scale is not None else 0.0)
+    if k_scale is None and v_scale is None:
+        check(_lib.load().pkd_run_composable(*args, _stream_ptr(stream)))
+    else:
+        check(_lib.load().pkd_run_composable_scaled(
+            *args, float(1.0 if k_scale is None else k_scale),
+            float(1.0 if v_scale is None else v_scale), _stream_ptr(stream)))
     return (out, lse) if (return_lse or lse is not None) else out
 
 

@@ -389,8 +389,6 @@ static int plan_impl(pkd_handle* h, const int32_t* qo_indptr, const int32_t* kv_
   if (rc != PKD_OK) return rc;
   if (qo_indptr && (rc = check_shared_shapes(num_qo_heads, num_kv_heads, page_size)) != PKD_OK)
     return rc;
-  if (qo_indptr && kv_dtype != PKD_DTYPE_BF16)
-    return fail(PKD_ERR_UNSUPPORTED, "shared-prefix plans are built for a bf16 cache only");
   if (!kv_indices || !int_workspace || !float_workspace || !host_workspace)
     return fail(PKD_ERR_INVALID_ARG, "kv_indices and the three workspaces must be non-null");
   if ((reinterpret_cast<uintptr_t>(int_workspace) & 255) ||
@@ -661,7 +659,8 @@ int pkd_run_scaled(pkd_handle* h, const void* q, int32_t batch, const void* kv_c
   hipError_t e;
   if (prof && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if (h->layout.kind == PKD_PLAN_SHARED)
-    e = pkd::launch_prefix_mfma(dp, h->Hq / h->Hkv, h->P, h->num_slots, s);
+    e = pkd::launch_prefix_mfma(dp, h->Hq / h->Hkv, h->P, h->num_slots,
+                                h->kv_dtype == PKD_DTYPE_FP8_E4M3, s);
   else if (h->kv_dtype == PKD_DTYPE_FP8_E4M3)
     e = pkd::launch_decode_fp8(dp, h->Hq / h->Hkv, h->P, h->num_slots, s);
   else if (h->variant == PKD_VARIANT_MFMA_PV)
@@ -681,6 +680,14 @@ int pkd_run_scaled(pkd_handle* h, const void* q, int32_t batch, const void* kv_c
 int pkd_run_composable(pkd_handle* prefix, pkd_handle* suffix, const void* q, int32_t batch,
                        const void* kv_cache, int64_t num_pages, int32_t q_dtype, int32_t kv_dtype,
                        void* o, float* lse, float sm_scale, pkd_stream_t stream) {
+  return pkd_run_composable_scaled(prefix, suffix, q, batch, kv_cache, num_pages, q_dtype,
+                                   kv_dtype, o, lse, sm_scale, 1.f, 1.f, stream);
+}
+
+int pkd_run_composable_scaled(pkd_handle* prefix, pkd_handle* suffix, const void* q,
+                              int32_t batch, const void* kv_cache, int64_t num_pages,
+                              int32_t q_dtype, int32_t kv_dtype, void* o, float* lse,
+                              float sm_scale, float k_scale, float v_scale, pkd_stream_t stream) {
   if (!prefix || !suffix || prefix == suffix)
     return fail(PKD_ERR_INVALID_ARG, "two distinct handles are needed (prefix plan, suffix plan)");
   if (!prefix->planned || !suffix->planned)
@@ -712,6 +719,11 @@ int pkd_run_composable(pkd_handle* prefix, pkd_handle* suffix, const void* q, in
       (reinterpret_cast<uintptr_t>(o) & 15))
     return fail(PKD_ERR_INVALID_ARG, "q, kv_cache and o must be 16-byte aligned");
   if (!(std::isfinite(sm_scale))) return fail(PKD_ERR_INVALID_ARG, "sm_scale must be finite");
+  if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return fail(PKD_ERR_INVALID_ARG, "k_scale and v_scale must be finite and > 0");
+  if (prefix->kv_dtype != PKD_DTYPE_FP8_E4M3 && (k_scale != 1.f || v_scale != 1.f))
+    return fail(PKD_ERR_INVALID_ARG, "k_scale and v_scale apply to an fp8 e4m3 cache only");
+  const bool fp8 = prefix->kv_dtype == PKD_DTYPE_FP8_E4M3;
 
   DeviceGuard guard(prefix->device);
   if (!guard.ok) return hip_fail(guard.err, "hipSetDevice");
@@ -727,8 +739,8 @@ int pkd_run_composable(pkd_handle* prefix, pkd_handle* suffix, const void* q, in
     dp.fws = static_cast<float*>(h->float_ws);
     dp.err = static_cast<int32_t*>(h->int_ws);
     dp.num_pages = num_pages;
-    dp.scale_log2 = scale * 1.44269504088896341f;
-    dp.out_scale = 1.f;
+    dp.scale_log2 = scale * k_scale * 1.44269504088896341f;
+    dp.out_scale = v_scale;
     dp.num_qo_heads = h->Hq;
     dp.num_kv_heads = h->Hkv;
     return dp;
@@ -755,7 +767,8 @@ int pkd_run_composable(pkd_handle* prefix, pkd_handle* suffix, const void* q, in
     e = pkd::launch_composable(dpre, ds, g, prefix->P, prefix->num_slots, suffix->num_slots, s);
     if (e != hipSuccess) return hip_fail(e, "composable kernel launch");
   } else {
-    e = pkd::launch_prefix_mfma(dpre, prefix->Hq / prefix->Hkv, prefix->P, prefix->num_slots, s);
+    e = pkd::launch_prefix_mfma(dpre, prefix->Hq / prefix->Hkv, prefix->P, prefix->num_slots, fp8,
+                                s);
     if (e != hipSuccess) return hip_fail(e, "shared-prefix kernel launch");
     if (suffix->kv_dtype == PKD_DTYPE_FP8_E4M3)
       e = pkd::launch_decode_fp8(ds, g, suffix->P, suffix->num_slots, s);

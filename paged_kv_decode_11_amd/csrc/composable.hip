@@ -48,9 +48,9 @@ void composable_kernel(const uint16_t* __restrict__ q_ptr, const uint16_t* __res
   __shared__ ComposableShared sh;
   const int b = blockIdx.x;
   if (b < prefix_slots) {
-    prefix::prefix_body<G, P>(q_ptr, kv_ptr, o_ptr, lse_ptr, ws_pre, fws_pre, err_pre, num_pages,
-                              scale_log2, num_qo_heads, num_kv_heads, b, prefix_slots,
-                              sh.prefix);
+    prefix::prefix_body<G, P, false>(q_ptr, kv_ptr, o_ptr, lse_ptr, ws_pre, fws_pre, err_pre,
+                                     num_pages, scale_log2, 1.f, num_qo_heads, num_kv_heads, b,
+                                     prefix_slots, sh.prefix);
   } else {
     pv::decode_pv_body<G, P>(q_ptr, kv_ptr, o_ptr, lse_ptr, ws_suf, fws_suf, err_suf, num_pages,
                              scale_log2, num_qo_heads, num_kv_heads, b - prefix_slots,

@@ -70,15 +70,6 @@ constexpr int kStep = 32;
 // probabilities enter fp16 as p * 2^kPShift
 constexpr float kPShift = 15.f;
 
-// 8 E4M3 codes (two dwords) to 8 bf16 (exact).
-__device__ __forceinline__ uint4 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
-  return make_uint4(
-      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false)),
-      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true)),
-      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false)),
-      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true)));
-}
-
 // 8 E4M3 codes to 8 fp16 (exact).
 __device__ __forceinline__ uint4 fp8x8_to_f16(uint32_t w0, uint32_t w1) {
   return make_uint4(

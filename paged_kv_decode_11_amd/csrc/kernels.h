@@ -64,9 +64,10 @@ hipError_t launch_decode_fp8(const DecodeParams& p, int g, int page_size, int nu
                              hipStream_t stream);
 bool fp8_variant_built(int g, int page_size);
 // Shared-prefix kernel (prefix_mfma.hip): one KV head of one (group, row
-// block, chunk) item per workgroup, 128 query rows sharing each K/V tile.
+// block, chunk) item per workgroup, 128 query rows sharing each K/V tile;
+// fp8: the cache holds E4M3 codes (p.out_scale = v_scale).
 hipError_t launch_prefix_mfma(const DecodeParams& p, int g, int page_size, int num_slots,
-                              hipStream_t stream);
+                              bool fp8, hipStream_t stream);
 bool prefix_variant_built(int g, int page_size);
 // The shared-prefix kernel on a prefix plan (workgroups [0, prefix_slots))
 // and the matrix-core P.V decode kernel on a suffix plan (the next

@@ -36,6 +36,15 @@
 //     query row l & 15 (head dims 16 b + 4 (l >> 4) + v), the row the
 //     softmax keeps in that lane, so rescale factors and the final max and
 //     sum never move between lanes.
+//
+// Over an FP8 E4M3 cache (kFp8) a head row is 128 bytes of codes: every lane
+// loads one 16-byte piece of one K row and of one V row per tile and
+// stages it as two bf16 pieces (every E4M3 value is exact in bf16), so the
+// LDS tiles and the products are those of the bf16 cache.  P enters P V as
+// a bf16 high part and the bf16 rounding of its remainder (two products),
+// about 16 bits of each probability, so the output error does not grow
+// with the values' magnitude (up to 448 v_scale).  k_scale is folded into
+// the logit scale and v_scale into the final normalisation.
 
 #pragma once
 
@@ -60,7 +69,6 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 64;   // tokens per tile (four quarters of 16)
 constexpr int kDepth = 4;   // tiles in flight per workgroup
-constexpr int kLdRows = kTile / 32;  // tile rows each lane loads (32 rows per pass)
 
 // A wave's 16 fp32 output rows, staged in LDS at the end of an item so that
 // each store instruction writes two whole 512-byte rows: rows 528 bytes apart
@@ -94,26 +102,37 @@ __device__ __forceinline__ uint2 lds_read_tr(const void* p) {
 }
 
 // One workgroup's work: the items of slot `slot` of `num_slots`, with `sh`
-// its LDS.  Needs kThreads lanes.
-template <int G, int P>
+// its LDS.  Needs kThreads lanes.  kFp8: the cache holds E4M3 codes;
+// out_scale multiplies every output (v_scale; 1 for a bf16 cache).
+template <int G, int P, bool kFp8>
 __device__ __forceinline__ void prefix_body(
     const uint16_t* __restrict__ q_ptr, const uint16_t* __restrict__ kv_ptr,
     uint16_t* __restrict__ o_ptr, float* __restrict__ lse_ptr, const int32_t* __restrict__ ws,
     float* __restrict__ fws, int32_t* __restrict__ err, int64_t num_pages, float scale_log2,
-    int num_qo_heads, int num_kv_heads, int slot, int num_slots, PShared& sh) {
+    float out_scale, int num_qo_heads, int num_kv_heads, int slot, int num_slots, PShared& sh) {
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
   static_assert(P % 16 == 0, "a 16-token half tile must lie in one page");
   constexpr int kReqPerWave = 16 / G;
+  // bytes per cached element; 16-byte pieces per head row; tile rows one
+  // pass of the workgroup's lanes loads; passes per tile
+  constexpr int kElem = kFp8 ? 1 : 2;
+  constexpr int kPieces = kHeadDim * kElem / 16;
+  constexpr int kRowsPerPass = kThreads / kPieces;
+  constexpr int kLdRows = kTile / kRowsPerPass;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row16 = lane & 15;
   const int kg = lane >> 4;
-  // load role: tile rows (tid >> 4) + 32 i, 16-byte piece tid & 15
-  const int ld_row = tid >> 4;
-  const int ld_piece = tid & 15;
+  // load role: tile rows ld_row + kRowsPerPass i, 16-byte piece ld_piece
+  // (its LDS slot in a row, rotated by the row; an E4M3 piece fills the two
+  // bf16 slots 2 ld_piece and 2 ld_piece + 1)
+  const int ld_row = tid / kPieces;
+  const int ld_piece = tid % kPieces;
   const int ld_slot = ld_piece ^ (ld_row & 15);
+  const int ld_slot2 = (2 * ld_piece) ^ (ld_row & 15);
+  const int ld_slot2b = (2 * ld_piece + 1) ^ (ld_row & 15);
 
   const int32_t* hdr = ws + PKD_HEADER_BASE;
   const int32_t* slot_indptr = ws + plan_off_slots();
@@ -126,7 +145,7 @@ __device__ __forceinline__ void prefix_body(
   const int32_t* groups = ws + off_groups;
   const int Hq = num_qo_heads;
 
-  const uint32_t row_bytes = uint32_t(num_kv_heads) * kHeadDim * 2;
+  const uint32_t row_bytes = uint32_t(num_kv_heads) * kHeadDim * kElem;
   const uint64_t v_bytes = uint64_t(P) * row_bytes;
   const uint64_t page_bytes = 2 * v_bytes;
   const char* kv = reinterpret_cast<const char*>(kv_ptr);
@@ -167,7 +186,9 @@ __device__ __forceinline__ void prefix_body(
     // This lane's token of row ld_row + 32 i of tile t (clamped to the
     // chunk: rows past its end repeat the last token; they are masked, and V
     // of those rows is zeroed when staged) and the page id of that token.
-    auto token_of = [&](int t, int i) { return min(kTile * t + 32 * i + ld_row, last_token); };
+    auto token_of = [&](int t, int i) {
+      return min(kTile * t + kRowsPerPass * i + ld_row, last_token);
+    };
     // (threadIdx.y is 0 in this one-dimensional launch; adding it makes the
     // page-id load a per-lane one, so its wait sits where the id is used)
     auto page_of = [&](int t, int i) -> int32_t {
@@ -176,7 +197,7 @@ __device__ __forceinline__ void prefix_body(
     auto piece_addr = [&](int t, int i, int32_t id) -> const uint4* {
       const int64_t pg = safe_page(id, num_pages, bad);
       const uint64_t off = uint64_t(pg) * page_bytes + uint64_t(token_of(t, i) % P) * row_bytes +
-                           uint64_t(kh) * kHeadDim * 2 + uint64_t(ld_piece) * 16;
+                           uint64_t(kh) * kHeadDim * kElem + uint64_t(ld_piece) * 16;
       return reinterpret_cast<const uint4*>(kv + off);
     };
 
@@ -241,9 +262,18 @@ __device__ __forceinline__ void prefix_body(
       // must not meet a repeated or NaN value)
 #pragma unroll
       for (int i = 0; i < kLdRows; ++i) {
-        const int r = 32 * i + ld_row;
-        sh.t.k[stage][r][ld_slot] = sk[i];
-        sh.t.v[stage][r][ld_slot] = r < valid ? sv[i] : make_uint4(0u, 0u, 0u, 0u);
+        const int r = kRowsPerPass * i + ld_row;
+        if constexpr (kFp8) {
+          const uint4 kc = sk[i];
+          const uint4 vc = r < valid ? sv[i] : make_uint4(0u, 0u, 0u, 0u);
+          sh.t.k[stage][r][ld_slot2] = fp8x8_to_bf16(kc.x, kc.y);
+          sh.t.k[stage][r][ld_slot2b] = fp8x8_to_bf16(kc.z, kc.w);
+          sh.t.v[stage][r][ld_slot2] = fp8x8_to_bf16(vc.x, vc.y);
+          sh.t.v[stage][r][ld_slot2b] = fp8x8_to_bf16(vc.z, vc.w);
+        } else {
+          sh.t.k[stage][r][ld_slot] = sk[i];
+          sh.t.v[stage][r][ld_slot] = r < valid ? sv[i] : make_uint4(0u, 0u, 0u, 0u);
+        }
       }
       lds_barrier();
       if (reload) {
@@ -293,12 +323,21 @@ __device__ __forceinline__ void prefix_body(
       // k = 8 kg + j <-> token 4 kg + j (j < 4) of the first quarter and
       // 16 + 4 kg + j - 4 of the second
       uint4 pb[2];
+      [[maybe_unused]] uint4 pr[2];
 #pragma unroll
-      for (int e = 0; e < 2; ++e)
-        pb[e] = make_uint4(pack_bf16x2(p[8 * e + 0], p[8 * e + 1]),
-                           pack_bf16x2(p[8 * e + 2], p[8 * e + 3]),
-                           pack_bf16x2(p[8 * e + 4], p[8 * e + 5]),
-                           pack_bf16x2(p[8 * e + 6], p[8 * e + 7]));
+      for (int e = 0; e < 2; ++e) {
+        const float* pe = p + 8 * e;
+        const uint4 h = make_uint4(pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3]),
+                                   pack_bf16x2(pe[4], pe[5]), pack_bf16x2(pe[6], pe[7]));
+        pb[e] = h;
+        if constexpr (kFp8) {
+          // what the bf16 high parts leave over (exact in fp32), in bf16
+          pr[e] = make_uint4(pack_bf16x2(pe[0] - bf16_lo(h.x), pe[1] - bf16_hi(h.x)),
+                             pack_bf16x2(pe[2] - bf16_lo(h.y), pe[3] - bf16_hi(h.y)),
+                             pack_bf16x2(pe[4] - bf16_lo(h.z), pe[5] - bf16_hi(h.z)),
+                             pack_bf16x2(pe[6] - bf16_lo(h.w), pe[7] - bf16_hi(h.w)));
+        }
+      }
       // V^T as the A operand of head-dim block cb: lane (kg, i = 4 r + q)
       // points the transposing read at row 4 kg + r of each quarter,
       // elements cb 16 + 4 q .. + 3
@@ -314,8 +353,14 @@ __device__ __forceinline__ void prefix_body(
               reinterpret_cast<const char*>(&sh.t.v[stage][16 * h + tr_row][piece ^ tr_row]) +
               8 * (tr_q & 1));
         acc[cb] *= alpha;
-        acc[cb] = mfma32(make_uint4(b[0].x, b[0].y, b[1].x, b[1].y), pb[0], acc[cb]);
-        acc[cb] = mfma32(make_uint4(b[2].x, b[2].y, b[3].x, b[3].y), pb[1], acc[cb]);
+        const uint4 va = make_uint4(b[0].x, b[0].y, b[1].x, b[1].y);
+        const uint4 vb = make_uint4(b[2].x, b[2].y, b[3].x, b[3].y);
+        acc[cb] = mfma32(va, pb[0], acc[cb]);
+        acc[cb] = mfma32(vb, pb[1], acc[cb]);
+        if constexpr (kFp8) {
+          acc[cb] = mfma32(va, pr[0], acc[cb]);
+          acc[cb] = mfma32(vb, pr[1], acc[cb]);
+        }
       }
     };
 
@@ -339,7 +384,7 @@ __device__ __forceinline__ void prefix_body(
       // lane l: query row l & 15, head dims 16 cb + 4 kg + v
       const float lt = rows_sum(lsum);
       const int i = row16 / G;
-      const float inv = 1.f / lt;
+      const float inv = out_scale / lt;
       if (out >= 0) {
         char* epi = sh.epi + wave * kEpiWaveBytes;
 #pragma unroll

@@ -106,9 +106,9 @@ def test_fp8_cache_errors():
         r.run(q, cache)
     assert e.value.code == _lib.PKD_ERR_DTYPE_MISMATCH
     sr = pkd.SharedPlanRun(2, 4, 64, 32, 8)
-    with pytest.raises(pkd.PkdError) as e:
+    with pytest.raises(pkd.PkdError) as e:  # shared-prefix plans need pages of 16-64 tokens
         sr.plan(np.array([0, 2]), batch.kv_indptr[:2], idx[:3].contiguous(),
-                batch.kv_last_page_len[:1], 32, 8, 128, 16, kv_data_type=fp8)
+                batch.kv_last_page_len[:1], 32, 8, 128, 8, kv_data_type=fp8)
     assert e.value.code == _lib.PKD_ERR_UNSUPPORTED
     k = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
     i32 = torch.zeros(1, dtype=torch.int32, device="cuda")

@@ -161,9 +161,9 @@ def test_shared_prefix_workload_composable_full():
 # the composable format in one call: pkd_run_composable
 # ---------------------------------------------------------------------------
 
-def _composable_inputs(seed, rows, prefix_lens, suffix_lens, P, Hq, Hkv):
+def _composable_inputs(seed, rows, prefix_lens, suffix_lens, P, Hq, Hkv, fp8=False):
     """Groups over prefixes and every request's own suffix, in one pool: the
-    group table, the suffix table and the cache."""
+    group table, the suffix table and the cache (E4M3 codes when fp8)."""
     rng = np.random.default_rng(seed)
     lens = list(prefix_lens) + list(suffix_lens)
     need = int(sum(-(-l // P) for l in lens))
@@ -178,7 +178,8 @@ def _composable_inputs(seed, rows, prefix_lens, suffix_lens, P, Hq, Hkv):
                               allb.kv_indices[gi[G]:].copy(), allb.kv_last_page_len[G:].copy())
     qo = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
     q = workloads.normal_bf16(rng, (int(qo[-1]), Hq, 128))
-    cache = workloads.host_cache(allb, rng, poison=True)
+    cache = (workloads.host_cache_e4m3(allb, rng, poison=True) if fp8
+             else workloads.host_cache(allb, rng, poison=True))
     return gb, sb, qo, q, cache
 
 
@@ -192,13 +193,14 @@ def _composable_ref(gb, sb, qo, q, cache, Hkv, sm_scale=None):
     return om.merge_rows(o_p, l_p, o_s, l_s)
 
 
-def _plan_both(rp, rs, gb, sb, qo, P, Hq, Hkv, popts=None, sopts=None):
+def _plan_both(rp, rs, gb, sb, qo, P, Hq, Hkv, popts=None, sopts=None, fp8=False):
     import torch
 
+    kv = dict(kv_data_type=torch.float8_e4m3fn) if fp8 else {}
     rp.plan(qo, gb.kv_indptr, torch.from_numpy(gb.kv_indices.astype(np.int32)).cuda(),
-            gb.kv_last_page_len, Hq, Hkv, 128, P, all_partials=True, **(popts or {}))
+            gb.kv_last_page_len, Hq, Hkv, 128, P, all_partials=True, **kv, **(popts or {}))
     rs.plan(sb.kv_indptr, torch.from_numpy(sb.kv_indices.astype(np.int32)).cuda(),
-            sb.kv_last_page_len, Hq, Hkv, 128, P, all_partials=True, **(sopts or {}))
+            sb.kv_last_page_len, Hq, Hkv, 128, P, all_partials=True, **kv, **(sopts or {}))
 
 
 @pytest.mark.parametrize("side_by_side", [False, True])
@@ -268,6 +270,16 @@ def test_run_composable_refusals():
     with pytest.raises(pkd.PkdError) as e:
         pkd.run_composable(rp, rs, qd, cd)
     assert e.value.code == _lib.PKD_ERR_STALE_PLAN
+    # scales on a bf16 cache; a plan pair whose cache dtypes differ
+    _plan_both(rp, rs, gb, sb, qo, 16, 32, 8)
+    with pytest.raises(pkd.PkdError) as e:
+        pkd.run_composable(rp, rs, qd, cd, k_scale=0.5)
+    assert e.value.code == _lib.PKD_ERR_INVALID_ARG
+    rs.plan(sb.kv_indptr, idx_s, sb.kv_last_page_len, 32, 8, 128, 16, all_partials=True,
+            kv_data_type=torch.float8_e4m3fn)
+    with pytest.raises(pkd.PkdError) as e:
+        pkd.run_composable(rp, rs, qd, cd)
+    assert e.value.code == _lib.PKD_ERR_DTYPE_MISMATCH
 
 
 def _half_cus():
@@ -354,3 +366,102 @@ def test_shared_prefix_workload_run_composable_full():
     o_ref, lse_ref = att.decode(q, cache, main.kv_indptr, main.kv_indices, main.kv_last_page_len,
                                 main.num_kv_heads, requests=req)
     gu.assert_close(o, lse, o_ref, lse_ref, requests=req, label="run_composable full")
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 cache: shared-prefix plans and the composable call with scales
+
+K_SCALE, V_SCALE = 1.0 / 64, 1.0 / 32
+
+
+@pytest.mark.parametrize("P", [16, 32, 64])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_fp8_shared_groups(P, G):
+    """A shared-prefix plan over E4M3 codes (NaN codes past every group's
+    last token): every request's state over its group's tokens against the
+    oracle on the table expanded to one page list per request; unsplit and
+    split."""
+    import torch
+
+    Hkv = 8 if G <= 4 else 4
+    Hq = Hkv * G
+    rows, lens = [128 // G + 3, 5], [40 * P + 7, 3 * P]
+    rng = np.random.default_rng(2000 + 10 * P + G)
+    gb = workloads.make_batch(lens, P, int(sum(-(-l // P) for l in lens)) + 7, Hq, Hkv, 128, rng)
+    qo = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    q = workloads.normal_bf16(rng, (int(qo[-1]), Hq, 128))
+    codes = workloads.host_cache_e4m3(gb, rng, poison=True)
+    indptr, indices, last = _expanded(gb, qo)
+    o_ref, lse_ref = att.decode_fp8(q, codes, indptr, indices, last, Hkv, k_scale=K_SCALE,
+                                    v_scale=V_SCALE)
+    r = shared_runner(Hq=Hq, Hkv=Hkv)
+    idx = torch.from_numpy(gb.kv_indices.astype(np.int32)).cuda()
+    for opts in ({}, {"fixed_chunk_pages": 3}):
+        gu.say("fp8 shared", "P", P, "G", G, "rows", rows, "lens", lens, opts)
+        r.plan(qo, gb.kv_indptr, idx, gb.kv_last_page_len, Hq, Hkv, 128, P,
+               kv_data_type=torch.float8_e4m3fn, **opts)
+        o, lse = r.run(gu.bits_to_dev(q), gu.codes_to_dev(codes), return_lse=True,
+                       k_scale=K_SCALE, v_scale=V_SCALE)
+        torch.cuda.synchronize()
+        assert r.read_device_error() == 0
+        gu.assert_close(o, lse, o_ref, lse_ref, label=f"fp8 shared P{P} G{G} {opts}")
+
+
+def test_fp8_shared_unit_scales():
+    """Unit scales (values up to 448): P enters the product as a bf16 high
+    part plus remainder, so the plain bar holds at any magnitude."""
+    import torch
+
+    rows, lens, P = [32], [700], 16
+    rng = np.random.default_rng(2100)
+    gb = workloads.make_batch(lens, P, 60, 32, 8, 128, rng)
+    qo = np.array([0, 32], np.int32)
+    q = workloads.normal_bf16(rng, (32, 32, 128))
+    codes = workloads.host_cache_e4m3(gb, rng, poison=True)
+    indptr, indices, last = _expanded(gb, qo)
+    o_ref, lse_ref = att.decode_fp8(q, codes, indptr, indices, last, 8, k_scale=1.0, v_scale=1.0,
+                                    sm_scale=1.0 / 4096)
+    r = shared_runner()
+    idx = torch.from_numpy(gb.kv_indices.astype(np.int32)).cuda()
+    r.plan(qo, gb.kv_indptr, idx, gb.kv_last_page_len, 32, 8, 128, P,
+           kv_data_type=torch.float8_e4m3fn)
+    o, lse = r.run(gu.bits_to_dev(q), gu.codes_to_dev(codes), return_lse=True, k_scale=1.0,
+                   v_scale=1.0, sm_scale=1.0 / 4096)
+    torch.cuda.synchronize()
+    gu.assert_close(o, lse, o_ref, lse_ref, label="fp8 shared unit scales")
+
+
+@pytest.mark.parametrize("case", range(3))
+def test_fp8_run_composable(case):
+    """Prefix groups and per-request suffixes over one E4M3 cache, with
+    scales, against the oracle's merge of the two exact states (the
+    shared-prefix kernel and the FP8 decode kernel one after the other)."""
+    import torch
+    import paged_kv_decode_11_amd as pkd
+    from oracle import merge as om
+
+    P, Hq, Hkv, rows, plens, popts, sopts = [
+        (16, 32, 8, [32], [8 * 16 + 5], {}, {}),
+        (16, 32, 8, [5, 40, 1], [300, 2000, 17], {"fixed_chunk_pages": 2}, {"fixed_chunk_pages": 1}),
+        (64, 8, 8, [9, 3], [700, 64], {}, {"fixed_chunk_pages": 3}),
+    ][case]
+    B = int(sum(rows))
+    rng = np.random.default_rng(700 + case)
+    slens = rng.integers(1, 900, size=B).tolist()
+    slens[0] = 1
+    gb, sb, qo, q, codes = _composable_inputs(710 + case, rows, plens, slens, P, Hq, Hkv, fp8=True)
+    gu.say("fp8 composable", case, "rows", rows, "prefix", plens, "P", P, "Hq", Hq, "Hkv", Hkv)
+    rp = pkd.SharedPlanRun(64, 256, 1 << 14, Hq, Hkv)
+    rs = pkd.DecodePlanRun(max_batch=1024, max_nnz=1 << 14, max_qo_heads=Hq)
+    _plan_both(rp, rs, gb, sb, qo, P, Hq, Hkv, popts, sopts, fp8=True)
+    o, lse = pkd.run_composable(rp, rs, gu.bits_to_dev(q), gu.codes_to_dev(codes), return_lse=True,
+                                k_scale=K_SCALE, v_scale=V_SCALE)
+    torch.cuda.synchronize()
+    assert rp.read_device_error() == 0 and rs.read_device_error() == 0
+    indptr, indices, last = _expanded(gb, qo)
+    o_p, l_p = att.decode_fp8(q, codes, indptr, indices, last, Hkv, k_scale=K_SCALE,
+                              v_scale=V_SCALE)
+    o_s, l_s = att.decode_fp8(q, codes, sb.kv_indptr, sb.kv_indices, sb.kv_last_page_len, Hkv,
+                              k_scale=K_SCALE, v_scale=V_SCALE)
+    o_ref, lse_ref = om.merge_rows(o_p, l_p, o_s, l_s)
+    gu.assert_close(o, lse, o_ref, lse_ref, label=f"fp8 composable-{case}")
