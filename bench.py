@@ -90,12 +90,14 @@ def parse():
 KERNEL_FILES = {
     "decode_mfma_kernel": ("decode_mfma.hip", "device_common.h", "plan_layout.h"),
     "decode_kernel": ("decode.hip", "device_common.h", "plan_layout.h"),
-    "decode_fp8_kernel": ("decode_fp8.hip", "device_common.h", "plan_layout.h"),
+    "decode_fp8_kernel": ("decode_fp8.hip", "decode_fp8.h", "device_common.h", "plan_layout.h"),
     "decode_pv_kernel": ("decode_pv.hip", "decode_pv.h", "device_common.h", "plan_layout.h"),
     "prefix_mfma_kernel": ("prefix_mfma.hip", "prefix_mfma.h", "device_common.h",
                            "plan_layout.h"),
     "composable_kernel": ("composable.hip", "prefix_mfma.h", "decode_pv.h", "device_common.h",
                           "plan_layout.h"),
+    "composable_fp8_kernel": ("composable.hip", "prefix_mfma.h", "decode_fp8.h",
+                              "device_common.h", "plan_layout.h"),
 }
 
 
@@ -340,10 +342,9 @@ def bench_shared_prefix(args):
     # pages) and one decode plan (each request's own suffix), both writing
     # every chunk's state as a partial; pkd_run_composable runs the prefix
     # kernel, the suffix decode and one merge
-    # half of the compute units each, so that the bf16 form runs both
-    # attention kernels in one launch side by side; over an E4M3 cache the
-    # two kernels run one after the other and each takes the whole chip
-    half = 0 if fp8 else torch.cuda.get_device_properties(dev).multi_processor_count // 2
+    # half of the compute units each, so that both attention kernels run in
+    # one launch side by side
+    half = torch.cuda.get_device_properties(dev).multi_processor_count // 2
     rp = pkd.SharedPlanRun(4, main.batch, n_prefix_pages, H, main.num_kv_heads,
                            num_slots=half if args.prefix_slots < 0 else args.prefix_slots,
                            device=0)
@@ -426,7 +427,7 @@ def bench_shared_prefix(args):
     # two handles' slots fit the compute units side by side and the suffix
     # plan runs the matrix-core P.V kernel
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    one_launch = rp.num_slots + rs.num_slots <= cus and rs.planned_variant == "mfma_pv"
+    one_launch = rp.num_slots + rs.num_slots <= cus and (fp8 or rs.planned_variant == "mfma_pv")
     attn_us = attn_ms * 1e3 / runs
     prefix_merge_us = merge_ms * 1e3 / runs
     breakdown = {"attention_kernels": round(attn_us, 2), "merge": round(prefix_merge_us, 2),
@@ -442,7 +443,8 @@ def bench_shared_prefix(args):
     # the attention launch(es) read the prefix once per KV head and every
     # suffix once: the unique K/V bytes
     achieved = unique_bytes / (attn_us / 1e6) / 1e9
-    roof_kernel = "composable_kernel" if one_launch else "prefix_mfma_kernel + decode kernel"
+    roof_kernel = (("composable_fp8_kernel" if fp8 else "composable_kernel") if one_launch
+                   else "prefix_mfma_kernel + decode kernel")
     log(f"single format {us1:.1f} us/layer, composable {us2:.1f} us/layer (five launches "
         f"{us5:.1f}; attention {attn_us:.1f} us, merge {prefix_merge_us:.1f} us)")
     line = {
@@ -469,8 +471,8 @@ def bench_shared_prefix(args):
         "single_format_kv_gbs": round(single_bytes * R / (ms1 / 1e3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": (measured_traffic("shared_prefix", "composable_kernel", "bf16")
-                                 if one_launch and not fp8 else None),
+                     "traffic": (measured_traffic("shared_prefix", roof_kernel, args.kv_dtype)
+                                 if one_launch else None),
                      "kernel": roof_kernel, "avg_launch_us": round(attn_us, 2),
                      "algorithmic_bytes_per_launch": unique_bytes,
                      "merge_avg_launch_us": round(prefix_merge_us, 2)},

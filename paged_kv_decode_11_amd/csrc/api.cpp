@@ -751,9 +751,10 @@ int pkd_run_composable_scaled(pkd_handle* prefix, pkd_handle* suffix, const void
   // disjoint compute units at the same time.  Otherwise the two kernels run
   // one after the other.  (Two streams forked and joined inside the call were
   // measured first: the waits between them cost more than the overlap gave.)
+  // (over an E4M3 cache the suffix plan always runs the FP8 decode kernel,
+  // whose code has a one-launch form too)
   const bool one_launch = prefix->num_slots + suffix->num_slots <= prefix->cu_count &&
-                          suffix->variant == PKD_VARIANT_MFMA_PV &&
-                          suffix->kv_dtype == PKD_DTYPE_BF16;
+                          (fp8 || suffix->variant == PKD_VARIANT_MFMA_PV);
   // profiling, both handles: start, after the attention kernel(s), after the merge
   hipEvent_t *ep = nullptr, *es = nullptr;
   hipError_t e = profile_events(prefix, s, &ep);
@@ -764,7 +765,8 @@ int pkd_run_composable_scaled(pkd_handle* prefix, pkd_handle* suffix, const void
   const pkd::DecodeParams dpre = params(prefix), ds = params(suffix);
   const int g = suffix->Hq / suffix->Hkv;
   if (one_launch) {
-    e = pkd::launch_composable(dpre, ds, g, prefix->P, prefix->num_slots, suffix->num_slots, s);
+    e = pkd::launch_composable(dpre, ds, g, prefix->P, prefix->num_slots, suffix->num_slots, fp8,
+                               s);
     if (e != hipSuccess) return hip_fail(e, "composable kernel launch");
   } else {
     e = pkd::launch_prefix_mfma(dpre, prefix->Hq / prefix->Hkv, prefix->P, prefix->num_slots, fp8,

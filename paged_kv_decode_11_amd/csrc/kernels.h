@@ -72,9 +72,10 @@ bool prefix_variant_built(int g, int page_size);
 // The shared-prefix kernel on a prefix plan (workgroups [0, prefix_slots))
 // and the matrix-core P.V decode kernel on a suffix plan (the next
 // suffix_slots workgroups) in one launch (composable.hip); page sizes 16,
-// 32, 64.
+// 32, 64.  fp8: an E4M3 cache, the suffix on the FP8 decode kernel's code
+// (pre.out_scale = v_scale).
 hipError_t launch_composable(const DecodeParams& pre, const DecodeParams& suf, int g,
-                             int page_size, int prefix_slots, int suffix_slots,
+                             int page_size, int prefix_slots, int suffix_slots, bool fp8,
                              hipStream_t stream);
 // Occupancy (workgroups per CU) of the matrix-core decode kernel at g=4,
 // P=16 (the default kernel), and of the dot-product kernel.

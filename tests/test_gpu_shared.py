@@ -431,11 +431,14 @@ def test_fp8_shared_unit_scales():
     gu.assert_close(o, lse, o_ref, lse_ref, label="fp8 shared unit scales")
 
 
+@pytest.mark.parametrize("side_by_side", [False, True])
 @pytest.mark.parametrize("case", range(3))
-def test_fp8_run_composable(case):
+def test_fp8_run_composable(case, side_by_side):
     """Prefix groups and per-request suffixes over one E4M3 cache, with
-    scales, against the oracle's merge of the two exact states (the
-    shared-prefix kernel and the FP8 decode kernel one after the other)."""
+    scales, against the oracle's merge of the two exact states: the
+    shared-prefix kernel and the FP8 decode kernel one after the other
+    (default slot counts), and in one launch (half of the compute units per
+    handle)."""
     import torch
     import paged_kv_decode_11_amd as pkd
     from oracle import merge as om
@@ -450,9 +453,11 @@ def test_fp8_run_composable(case):
     slens = rng.integers(1, 900, size=B).tolist()
     slens[0] = 1
     gb, sb, qo, q, codes = _composable_inputs(710 + case, rows, plens, slens, P, Hq, Hkv, fp8=True)
-    gu.say("fp8 composable", case, "rows", rows, "prefix", plens, "P", P, "Hq", Hq, "Hkv", Hkv)
-    rp = pkd.SharedPlanRun(64, 256, 1 << 14, Hq, Hkv)
-    rs = pkd.DecodePlanRun(max_batch=1024, max_nnz=1 << 14, max_qo_heads=Hq)
+    gu.say("fp8 composable", case, "side by side", side_by_side, "rows", rows, "prefix", plens,
+           "P", P, "Hq", Hq, "Hkv", Hkv)
+    slots = _half_cus() if side_by_side else 0
+    rp = pkd.SharedPlanRun(64, 256, 1 << 14, Hq, Hkv, num_slots=slots)
+    rs = pkd.DecodePlanRun(max_batch=1024, max_nnz=1 << 14, max_qo_heads=Hq, num_slots=slots)
     _plan_both(rp, rs, gb, sb, qo, P, Hq, Hkv, popts, sopts, fp8=True)
     o, lse = pkd.run_composable(rp, rs, gu.bits_to_dev(q), gu.codes_to_dev(codes), return_lse=True,
                                 k_scale=K_SCALE, v_scale=V_SCALE)
