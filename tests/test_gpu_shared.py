@@ -432,7 +432,7 @@ def test_fp8_shared_unit_scales():
 
 
 @pytest.mark.parametrize("side_by_side", [False, True])
-@pytest.mark.parametrize("case", range(3))
+@pytest.mark.parametrize("case", range(5))
 def test_fp8_run_composable(case, side_by_side):
     """Prefix groups and per-request suffixes over one E4M3 cache, with
     scales, against the oracle's merge of the two exact states: the
@@ -447,6 +447,9 @@ def test_fp8_run_composable(case, side_by_side):
         (16, 32, 8, [32], [8 * 16 + 5], {}, {}),
         (16, 32, 8, [5, 40, 1], [300, 2000, 17], {"fixed_chunk_pages": 2}, {"fixed_chunk_pages": 1}),
         (64, 8, 8, [9, 3], [700, 64], {}, {"fixed_chunk_pages": 3}),
+        # KV head counts the 8 waves of a workgroup do not divide evenly
+        (16, 16, 2, [33], [5000], {}, {"min_chunk_tokens": 16}),
+        (32, 32, 16, [7, 2], [900, 40], {"fixed_chunk_pages": 4}, {}),
     ][case]
     B = int(sum(rows))
     rng = np.random.default_rng(700 + case)
