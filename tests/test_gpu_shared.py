@@ -473,3 +473,62 @@ def test_fp8_run_composable(case, side_by_side):
                               k_scale=K_SCALE, v_scale=V_SCALE)
     o_ref, lse_ref = om.merge_rows(o_p, l_p, o_s, l_s)
     gu.assert_close(o, lse, o_ref, lse_ref, label=f"fp8 composable-{case}")
+
+
+@pytest.mark.parametrize("side_by_side", [False, True])
+def test_fp8_run_composable_graph_replay(side_by_side):
+    """The composable call over an E4M3 cache, captured once, replays
+    correctly after both handles are planned again for other lengths, in
+    both forms (one launch, and the two kernels one after the other)."""
+    import torch
+    import paged_kv_decode_11_amd as pkd
+    from oracle import merge as om
+
+    P, Hq, Hkv, rows = 16, 32, 8, [6, 10]
+    B = sum(rows)
+    slots = _half_cus() if side_by_side else 0
+    rp = pkd.SharedPlanRun(4, 64, 1 << 12, Hq, Hkv, num_slots=slots)
+    rs = pkd.DecodePlanRun(max_batch=512, max_nnz=1 << 12, max_qo_heads=Hq, num_slots=slots)
+    steps = []
+    for seed in range(3):
+        rng = np.random.default_rng(730 + seed)
+        plens = rng.integers(1, 1500, size=2).tolist()
+        slens = rng.integers(1, 600, size=B).tolist()
+        steps.append(_composable_inputs(740 + seed, rows, plens, slens, P, Hq, Hkv, fp8=True))
+    pool = max(s[0].num_pages for s in steps)
+    cd = torch.zeros((pool, 2, P, Hkv, 128), dtype=torch.uint8, device="cuda")
+    cd8 = cd.view(torch.float8_e4m3fn)
+    q_buf = torch.zeros((B, Hq, 128), dtype=torch.bfloat16, device="cuda")
+    o_buf = torch.zeros((B, Hq, 128), dtype=torch.bfloat16, device="cuda")
+    lse_buf = torch.zeros((B, Hq), dtype=torch.float32, device="cuda")
+    gb, sb, qo, q, codes = steps[0]
+    _plan_both(rp, rs, gb, sb, qo, P, Hq, Hkv, fp8=True)
+    run = lambda: pkd.run_composable(rp, rs, q_buf, cd8, out=o_buf, lse=lse_buf,
+                                     k_scale=K_SCALE, v_scale=V_SCALE)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        pkd.run_composable(rp, rs, q_buf, cd8, out=o_buf, lse=lse_buf, k_scale=K_SCALE,
+                           v_scale=V_SCALE, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for n, (gb, sb, qo, q, codes) in enumerate(steps[1:] + steps[:1]):
+        gu.say("fp8 composable graph step", n, "side by side", side_by_side)
+        _plan_both(rp, rs, gb, sb, qo, P, Hq, Hkv, sopts={"fixed_chunk_pages": n + 1}, fp8=True)
+        cd[:codes.shape[0]].copy_(torch.from_numpy(codes).cuda())
+        q_buf.copy_(gu.bits_to_dev(q))
+        indptr, indices, last = _expanded(gb, qo)
+        o_p, l_p = att.decode_fp8(q, codes, indptr, indices, last, Hkv, k_scale=K_SCALE,
+                                  v_scale=V_SCALE)
+        o_s, l_s = att.decode_fp8(q, codes, sb.kv_indptr, sb.kv_indices, sb.kv_last_page_len, Hkv,
+                                  k_scale=K_SCALE, v_scale=V_SCALE)
+        o_ref, lse_ref = om.merge_rows(o_p, l_p, o_s, l_s)
+        for _ in range(2):
+            o_buf.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            gu.assert_close(o_buf, lse_buf, o_ref, lse_ref, label=f"fp8 composable replay {n}")
