@@ -60,18 +60,20 @@ def test_fp8_decode_random_batch(P, g):
     _check(batch, q, codes, f"fp8 random P{P} g{g}")
 
 
+@pytest.mark.parametrize("P", [16, 1, 4])
 @pytest.mark.parametrize("Hkv,g", [(1, 4), (3, 2), (12, 1), (16, 2)])
-def test_fp8_decode_kv_head_counts(Hkv, g):
+def test_fp8_decode_kv_head_counts(Hkv, g, P):
     """KV head counts below, above and not dividing the 8 waves of a
     workgroup: one wave per head, two heads per wave, and 12 heads (waves
     0-3 take two, waves 4-7 one, so the kernel runs without its per-step
     workgroup barrier)."""
-    rng = np.random.default_rng(500 + 10 * Hkv + g)
-    batch = workloads.random_batch(rng, 5, 900, 16, Hkv * g, Hkv, 128)
+    rng = np.random.default_rng(500 + 10 * Hkv + g + 1000 * P)
+    batch = workloads.random_batch(rng, 5, 900, P, Hkv * g, Hkv, 128)
     q = workloads.host_query(batch, rng)
     codes = workloads.host_cache_e4m3(batch, rng, poison=True)
-    _check(batch, q, codes, f"fp8 Hkv{Hkv} g{g}")
-    _check(batch, q, codes, f"fp8 Hkv{Hkv} g{g} split", fixed_chunk_pages=3)
+    _check(batch, q, codes, f"fp8 Hkv{Hkv} g{g} P{P}")
+    _check(batch, q, codes, f"fp8 Hkv{Hkv} g{g} P{P} split",
+           fixed_chunk_pages=3 if P >= 16 else 48 // P)
 
 
 @pytest.mark.parametrize("P", [1, 2, 4, 8, 16, 32, 64])
