@@ -418,19 +418,21 @@ int pkd_run_scaled(pkd_handle* h, const void* q, int32_t batch, const void* kv_c
  * captured in a graph replays correctly after re-plans of either handle on
  * the same workspaces (the choice between the two forms is made at the call
  * from the handles' slot counts and the suffix plan's kernel).  Device
- * errors are raised on each handle's own flag.  Over a bf16 cache; an FP8
- * E4M3 cache goes through pkd_run_composable_scaled. */
+ * errors are raised on each handle's own flag.  This is
+ * pkd_run_composable_scaled with both scales 1 (which an FP8 E4M3 cache
+ * then has). */
 int pkd_run_composable(pkd_handle* prefix, pkd_handle* suffix, const void* q, int32_t batch,
                        const void* kv_cache, int64_t num_pages, int32_t q_dtype, int32_t kv_dtype,
                        void* o, float* lse, float sm_scale, pkd_stream_t stream);
 
 /* pkd_run_composable over a cache of FP8 E4M3 codes with one scale per
  * tensor (the meaning of the codes and scales as in pkd_run_scaled): both
- * plans made with kv_dtype PKD_DTYPE_FP8_E4M3.  The shared-prefix kernel and
- * the FP8 decode kernel then run one after the other (the one-launch form
- * is built for a bf16 cache), followed by the same merge.  k_scale and
- * v_scale must be finite and > 0, and 1 for a bf16 cache (else
- * PKD_ERR_INVALID_ARG); pkd_run_composable is this call with both 1. */
+ * plans made with kv_dtype PKD_DTYPE_FP8_E4M3.  The same two forms: when
+ * the handles' slot counts together fit the compute units, one launch runs
+ * the shared-prefix kernel's code on the prefix plan and the FP8 decode
+ * kernel's code on the suffix plan side by side; otherwise the two kernels
+ * run one after the other; then the same merge.  k_scale and v_scale must
+ * be finite and > 0, and 1 for a bf16 cache (else PKD_ERR_INVALID_ARG). */
 int pkd_run_composable_scaled(pkd_handle* prefix, pkd_handle* suffix, const void* q,
                               int32_t batch, const void* kv_cache, int64_t num_pages,
                               int32_t q_dtype, int32_t kv_dtype, void* o, float* lse,
