@@ -332,3 +332,41 @@ def test_fp8_decode_other_group_sizes(P, g, Hkv):
     _check(batch, q, codes, f"fp8 P{P} g{g} Hkv{Hkv}")
     _check(batch, q, codes, f"fp8 P{P} g{g} Hkv{Hkv} split",
            fixed_chunk_pages=2 if P >= 16 else 48 // P)
+
+
+def _fp8_sampled(name, requests, seed_offset=0):
+    """A workload at full size over an E4M3 cache filled on the device, in
+    the benchmark's launch configuration (default plan and slot count);
+    the sampled requests' pages are copied back for the oracle."""
+    import torch
+
+    spec, rng, b = workloads.workload(name)
+    batch = b["main"]
+    q = workloads.host_query(batch, rng)
+    cache = workloads.device_cache_e4m3(batch, spec.seed + 400 + seed_offset, "cuda")
+    gu.say("fp8", name, "B", batch.batch, "T", batch.total_tokens, "P", batch.page_size,
+           "requests", requests)
+    r = gu.runner()
+    idx = torch.from_numpy(batch.kv_indices.astype(np.int32)).cuda()
+    r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, batch.num_qo_heads, batch.num_kv_heads,
+           batch.head_dim, batch.page_size, kv_data_type=torch.float8_e4m3fn)
+    o, lse = r.run(gu.bits_to_dev(q), cache, return_lse=True, k_scale=K_SCALE, v_scale=V_SCALE)
+    torch.cuda.synchronize()
+    assert r.read_device_error() == 0
+    host, indptr, indices, last = gu.compact_pages(batch, cache, requests)
+    del cache
+    torch.cuda.empty_cache()
+    o_ref, lse_ref = att.decode_fp8(q[requests], host, indptr, indices, last, batch.num_kv_heads,
+                                    k_scale=K_SCALE, v_scale=V_SCALE)
+    gu.assert_close(o[requests], lse[requests], o_ref, lse_ref, label=f"fp8 {name}")
+
+
+def test_fp8_skewed_full_size():
+    """The 100k-token request (split across most slots) and three of the
+    512-token ones."""
+    _fp8_sampled("skewed", [63, 0, 31, 62])
+
+
+def test_fp8_token_sparse_full_size():
+    """Page size 1 (every lane addresses its own rows), all 32 requests."""
+    _fp8_sampled("token_sparse", list(range(32)))
