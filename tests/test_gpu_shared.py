@@ -432,7 +432,7 @@ def test_fp8_shared_unit_scales():
 
 
 @pytest.mark.parametrize("side_by_side", [False, True])
-@pytest.mark.parametrize("case", range(5))
+@pytest.mark.parametrize("case", range(6))
 def test_fp8_run_composable(case, side_by_side):
     """Prefix groups and per-request suffixes over one E4M3 cache, with
     scales, against the oracle's merge of the two exact states: the
@@ -450,6 +450,8 @@ def test_fp8_run_composable(case, side_by_side):
         # KV head counts the 8 waves of a workgroup do not divide evenly
         (16, 16, 2, [33], [5000], {}, {"min_chunk_tokens": 16}),
         (32, 32, 16, [7, 2], [900, 40], {"fixed_chunk_pages": 4}, {}),
+        # one-token and page-aligned prefixes, one page per chunk
+        (16, 32, 8, [2, 2, 2, 2], [16, 32, 48, 1], {"fixed_chunk_pages": 1}, {}),
     ][case]
     B = int(sum(rows))
     rng = np.random.default_rng(700 + case)
