@@ -142,3 +142,39 @@ def test_static_plan_graph_replay():
             o_ref, lse_ref = att.decode(q, cache, b.kv_indptr, b.kv_indices, b.kv_last_page_len,
                                         HKV)
             gu.assert_close(o_buf[:B], lse_buf[:B], o_ref, lse_ref, label=f"static replay {seed}")
+
+
+@pytest.mark.parametrize("page", [16, 1])
+def test_static_plan_fp8_cache(page):
+    """An FP8 E4M3 cache through pkd_plan_static: the same bits as after a
+    plan on caller-owned workspaces, and the oracle's bar; two calls, the
+    second smaller, unsplit and forced-split."""
+    import torch
+    import paged_kv_decode_11_amd as pkd
+
+    fp8 = torch.float8_e4m3fn
+    static = pkd.StaticPlanRun()
+    ws = pkd.DecodePlanRun(max_batch=1024, max_nnz=1 << 14, max_qo_heads=HQ)
+    for call, (B, max_len, seed) in enumerate([(24, 1500, 21), (5, 400, 22)]):
+        rng = np.random.default_rng(seed + page)
+        batch = workloads.random_batch(rng, B, max_len, page, HQ, HKV, 128)
+        q = workloads.host_query(batch, rng)
+        codes = workloads.host_cache_e4m3(batch, rng, poison=True)
+        q_dev, c_dev = gu.bits_to_dev(q), gu.codes_to_dev(codes)
+        o_ref, lse_ref = att.decode_fp8(q, codes, batch.kv_indptr, batch.kv_indices,
+                                        batch.kv_last_page_len, HKV, k_scale=1 / 64, v_scale=1 / 32)
+        idx = torch.from_numpy(batch.kv_indices).cuda()
+        for opts in ({}, {"fixed_chunk_pages": 2 if page >= 16 else 48}):
+            gu.say("no-alloc fp8 call", call, "P", page, "B", B, "opts", opts)
+            outs = []
+            for r in (static, ws):
+                r.plan(batch.kv_indptr, idx, batch.kv_last_page_len, HQ, HKV, 128, page,
+                       kv_data_type=fp8, **opts)
+                o, lse = r.run(q_dev, c_dev, return_lse=True, k_scale=1 / 64, v_scale=1 / 32)
+                torch.cuda.synchronize()
+                assert r.read_device_error() == 0
+                outs.append((o, lse))
+            (o_s, lse_s), (o_w, lse_w) = outs
+            assert torch.equal(o_s.view(torch.int16), o_w.view(torch.int16)), "o differs"
+            assert torch.equal(lse_s.view(torch.int32), lse_w.view(torch.int32)), "lse differs"
+            gu.assert_close(o_s, lse_s, o_ref, lse_ref, label=f"static fp8 P{page} call {call}")
