@@ -55,7 +55,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_step",
                     choices=["llama8b_step", "skewed", "wide_gqa", "token_sparse", "tiny",
-                             "shared_prefix", "append"])
+                             "shared_prefix", "shared_prefix_b16", "shared_prefix_b64",
+                             "append"])
     ap.add_argument("--slots", type=int, default=0, help="persistent workgroups (0 = default)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="oracle time budget for cpu_baseline (0 disables)")
@@ -305,7 +306,7 @@ def bench_shared_prefix(args):
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    spec, rng, b = workloads.workload("shared_prefix")
+    spec, rng, b = workloads.workload(args.workload)
     main, prefix, suffix = b["main"], b["prefix"], b["suffix"]
     fp8 = args.kv_dtype == "e4m3"
     kv_tok = main.kv_bytes_per_token() // (2 if fp8 else 1)
@@ -455,7 +456,7 @@ def bench_shared_prefix(args):
         "data": ("synthetic (seeded N(0,1) bf16 q, uniformly drawn E4M3 K/V codes with scales "
                  "1/64, seeded lengths and page placement)" if fp8 else
                  "synthetic (seeded N(0,1) bf16 q/K/V, seeded lengths and page placement)"),
-        "config": {"workload": "shared_prefix", "batch": main.batch, "layers": R,
+        "config": {"workload": args.workload, "batch": main.batch, "layers": R,
                    "prefix_tokens": prefix_tokens, "suffix_tokens": suffix.total_tokens,
                    "num_qo_heads": H, "num_kv_heads": main.num_kv_heads, "head_dim": 128,
                    "page_size": 16, "slots": rp.num_slots, "kv_dtype": args.kv_dtype,
@@ -471,7 +472,7 @@ def bench_shared_prefix(args):
         "single_format_kv_gbs": round(single_bytes * R / (ms1 / 1e3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": (measured_traffic("shared_prefix", roof_kernel, args.kv_dtype)
+                     "traffic": (measured_traffic(args.workload, roof_kernel, args.kv_dtype)
                                  if one_launch else None),
                      "kernel": roof_kernel, "avg_launch_us": round(attn_us, 2),
                      "algorithmic_bytes_per_launch": unique_bytes,
@@ -827,7 +828,7 @@ def main():
         print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU sharding is a design "
                                    "note only (see the design document)", "n_gpus": args.gpus}))
         sys.exit(2)
-    if args.workload == "shared_prefix":
+    if args.workload.startswith("shared_prefix"):
         bench_shared_prefix(args)
         return
     if args.workload == "append":

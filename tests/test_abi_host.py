@@ -113,7 +113,8 @@ def test_plan_host_matches_oracle_bit_exact(S, seed):
 
 
 @pytest.mark.parametrize("name", ["tiny", "llama8b_step", "skewed", "shared_prefix",
-                                  "token_sparse", "wide_gqa"])
+                                  "token_sparse", "wide_gqa", "shared_prefix_b16",
+                                  "shared_prefix_b64"])
 def test_plan_host_matches_oracle_on_workloads(name):
     spec, _, batches = workloads.workload(name)
     for key, bt in batches.items():

@@ -340,13 +340,14 @@ def test_run_composable_graph_replay(side_by_side):
             gu.assert_close(o_buf, lse_buf, o_ref, lse_ref, label=f"composable replay {n}")
 
 
-def test_shared_prefix_workload_run_composable_full():
-    """The shared-prefix workload at full size through pkd_run_composable,
-    against the single-format oracle on 8 requests."""
+@pytest.mark.parametrize("name", ["shared_prefix", "shared_prefix_b16", "shared_prefix_b64"])
+def test_shared_prefix_workload_run_composable_full(name):
+    """A shared-prefix workload at full size through pkd_run_composable,
+    against the single-format oracle on 8 requests (the last among them)."""
     import torch
     import paged_kv_decode_11_amd as pkd
 
-    spec, rng, b = workloads.workload("shared_prefix")
+    spec, rng, b = workloads.workload(name)
     main, prefix, suffix = b["main"], b["prefix"], b["suffix"]
     q = workloads.host_query(main, rng)
     cache = workloads.host_cache(main, rng)
@@ -362,10 +363,11 @@ def test_shared_prefix_workload_run_composable_full():
             suffix.kv_last_page_len, 32, 8, 128, 16, all_partials=True)
     o, lse = pkd.run_composable(rp, rs, qd, cd, return_lse=True)
     torch.cuda.synchronize()
-    req = [0, 3, 7, 12, 18, 24, 29, 31]
+    B = main.batch
+    req = sorted({0, 3, 7, B // 3, B // 2, (2 * B) // 3, B - 2, B - 1})
     o_ref, lse_ref = att.decode(q, cache, main.kv_indptr, main.kv_indices, main.kv_last_page_len,
                                 main.num_kv_heads, requests=req)
-    gu.assert_close(o, lse, o_ref, lse_ref, requests=req, label="run_composable full")
+    gu.assert_close(o, lse, o_ref, lse_ref, requests=req, label=f"run_composable full {name}")
 
 
 # ---------------------------------------------------------------------------

@@ -270,9 +270,27 @@ def _build_shared_prefix(spec, rng):
     own suffix of U{64..1024} tokens.  Three page tables over one pool:
     ``main`` (each row = prefix pages + own suffix pages), ``prefix`` (every
     row = the 512 prefix pages) and ``suffix`` (own suffix pages only)."""
+    return _shared_prefix(spec, rng, 32, 8192, 64, 1024)
+
+
+def _build_shared_prefix_b16(spec, rng):
+    """16 requests over one 8192-token prefix, each with its own 128-token
+    suffix (the batch-16, prefix-8192 row of the pinghaoyang page's
+    composable-format table; the page states no head shapes)."""
+    return _shared_prefix(spec, rng, 16, 8192, 128, 128)
+
+
+def _build_shared_prefix_b64(spec, rng):
+    """The same with 64 requests (that table's batch-64 row)."""
+    return _shared_prefix(spec, rng, 64, 8192, 128, 128)
+
+
+def _shared_prefix(spec, rng, n_req, prefix_len, suffix_lo, suffix_hi):
+    """n_req requests over one prefix_len-token prefix plus their own suffix
+    of U{suffix_lo..suffix_hi} tokens, in the three page tables described
+    above."""
     P = spec.page_size
-    n_req, prefix_len = 32, 8192
-    suffix = rng.integers(64, 1025, size=n_req)
+    suffix = rng.integers(suffix_lo, suffix_hi + 1, size=n_req)
     perm = rng.permutation(spec.pool_pages)
     n_prefix_pages = prefix_len // P
     prefix_pages = perm[:n_prefix_pages]
@@ -329,6 +347,10 @@ WORKLOADS: Dict[str, WorkloadSpec] = {
                      1, 32, 8, 128, 1, 1 << 16, _build_token_sparse),
         WorkloadSpec("wide_gqa", "batch 256, log-normal KV (median 2048), Hq 64 / Hkv 8", 5,
                      16, 64, 8, 128, 1, 1 << 20, _build_wide_gqa),
+        WorkloadSpec("shared_prefix_b16", "16 requests: 8192-token shared prefix + 128 suffix", 6,
+                     16, 32, 8, 128, 1, 1 << 15, _build_shared_prefix_b16),
+        WorkloadSpec("shared_prefix_b64", "64 requests: 8192-token shared prefix + 128 suffix", 7,
+                     16, 32, 8, 128, 1, 1 << 15, _build_shared_prefix_b64),
     ]
 }
 
