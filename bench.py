@@ -70,11 +70,12 @@ def parse():
                          "library's default)")
     ap.add_argument("--prefix-slots", type=int, default=-1,
                     help="shared_prefix: workgroups of the shared-prefix kernel (0 = the "
-                         "library's default, -1 = half the compute units)")
+                         "library's default, -1 = one per 512-token prefix item, between half "
+                         "and three quarters of the compute units)")
     ap.add_argument("--suffix-slots", type=int, default=-1,
                     help="shared_prefix: workgroups of the suffix decode kernel (0 = the "
-                         "library's default, -1 = half the compute units, so the two kernels "
-                         "run side by side)")
+                         "library's default, -1 = the compute units the prefix plan leaves, so "
+                         "the two kernels run side by side)")
     ap.add_argument("--targets", default="skewed",
                     help="comma-separated decode workloads also timed after the main one (graph "
                          "mode, no oracle), reported under `targets` ('none' skips)")
@@ -343,14 +344,23 @@ def bench_shared_prefix(args):
     # pages) and one decode plan (each request's own suffix), both writing
     # every chunk's state as a partial; pkd_run_composable runs the prefix
     # kernel, the suffix decode and one merge
-    # half of the compute units each, so that both attention kernels run in
-    # one launch side by side
-    half = torch.cuda.get_device_properties(dev).multi_processor_count // 2
+    # The compute units split between the two plans so that both attention
+    # kernels run in one launch side by side: the prefix plan gets one slot
+    # per item of 512 prefix tokens (row blocks of 128 query rows x KV heads
+    # x chunks), at least half of the units and at most three quarters; the
+    # suffix plan the rest.  (Measured: 128 + 128 best for 16 and 32
+    # requests, 192 + 64 for 64 requests, over a 256-CU part.)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    g = H // main.num_kv_heads
+    row_blocks = -(-main.batch * g // 128)
+    pre_items = row_blocks * main.num_kv_heads * -(-prefix_tokens // 512)
+    pre_slots = min(max(pre_items, cus // 2), cus - cus // 4)
     rp = pkd.SharedPlanRun(4, main.batch, n_prefix_pages, H, main.num_kv_heads,
-                           num_slots=half if args.prefix_slots < 0 else args.prefix_slots,
+                           num_slots=pre_slots if args.prefix_slots < 0 else args.prefix_slots,
                            device=0)
     rs = pkd.DecodePlanRun(max_batch=suffix.batch, max_nnz=suffix.nnz, max_qo_heads=H,
-                           num_slots=half if args.suffix_slots < 0 else args.suffix_slots,
+                           num_slots=(cus - pre_slots if args.suffix_slots < 0
+                                      else args.suffix_slots),
                            device=0)
     qo = np.array([0, main.batch], np.int32)
     kv_indptr = np.array([0, n_prefix_pages], np.int32)
