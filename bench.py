@@ -569,7 +569,7 @@ def bench_append(args):
     print(json.dumps(line), flush=True)
 
 
-# spec fractions of the HBM peak per workload
+# the fraction of the HBM peak each of these workloads is held to
 TARGET_FRAC = {"llama8b_step": 0.70, "skewed": 0.60}
 
 
